@@ -1,0 +1,226 @@
+"""CPU oracle of the LatentMoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow float64 reference of what the layer computes.  Only the test
+suite, the package's smoke check and the benchmark's CPU-baseline leg may
+import it; the HIP library never does, and this file shares no code,
+constants or helpers with it.  numpy's matmul and stable argsort are used as
+library steps; everything else is written out from the definitions below.
+
+The layer (sources: the Nemotron 3 overview article, section 2.2 "LatentMoE",
+steps 1-3 and the paragraph after its table; the Nemotron 3 Super blog,
+section "Latent MoE"; the Nemotron 3 Ultra release news, architecture
+paragraph):
+  1. z_t = W_down x_t, the token's hidden vector (width d) projected down to
+     the latent width l = d/4                                (overview s2.2 step 1)
+  2. s_t = W_r x_t + b, router logits over E experts; the router reads x in d
+     (the routing gate stays in d per the paragraph after the s2.2 table;
+     the pages also place routing in l -- see the note on readings)
+  3. I_t = the k largest logits, ordered by (logit desc, expert id asc);
+     Ultra uses E = 512, k = 22                           (release news, architecture)
+  4. g_t = softmax over the k selected logits (the gate form is this layer's
+     specification; the pages do not give one)
+  5. y_{t,j} = W2_e (max(0, W1_e z_t))^2 for e = I_t[j]: each routed expert is
+     a ReLU^2 FFN l -> f -> l run in the latent space       (overview s2.2 step 2)
+  6. c_t = sum_j g_{t,j} y_{t,j}, then out_t = W_up c_t, back to width d
+                                                            (overview s2.2 step 3)
+  7. optional shared expert in d: out_t += W_s2 (max(0, W_s1 x_t))^2
+                                   (overview s2.2, paragraph after the table)
+  Integer side: counts[e] = #{(t, j): I_t[j] = e}, offsets = exclusive prefix
+  sum of counts, perm = stable counting sort of the row-major (t, j) pairs by
+  expert, inv = perm^-1.
+
+Precision: all arithmetic in float64 on the exact values of the stored
+inputs.  The one place floating point decides an integer (the top-k) takes
+the decision on float32 logits, the precision the layer stores its logits in;
+ties in float32 are broken by the lower expert id.
+
+Data format: bf16 tensors are numpy uint16 arrays of bf16 bit patterns;
+fp32 tensors are float32 arrays.  NVFP4 expert weights are byte arrays of
+E2M1 codes (two per byte, even element in the low nibble), E4M3 block scales
+(one per 16 consecutive fan-in elements) and one fp32 tensor scale per
+expert matrix (overview s3.1.1, NVFP4 format: E2M1 elements, 16-element
+micro-blocks, E4M3 block scale).
+"""
+from __future__ import annotations
+
+from collections import OrderedDict
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64.  A bf16 number is the upper half of an
+    IEEE-754 binary32 with the lower 16 mantissa bits zero."""
+    u32 = bits.astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def as_f64(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported array dtype {a.dtype}")
+
+
+def e2m1_value(code) -> np.ndarray:
+    """Value of a 4-bit E2M1 code: bit 3 sign, bits 2-1 exponent (bias 1),
+    bit 0 mantissa.  Exponent field 0 is subnormal: 0.5 * mantissa."""
+    code = np.asarray(code).astype(np.int64)
+    sign = (code >> 3) & 1
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = np.where(e == 0, 0.5 * m, np.exp2(e - 1.0) * (1.0 + 0.5 * m))
+    return np.where(sign == 1, -mag, mag)
+
+
+def e4m3_value(byte) -> np.ndarray:
+    """Value of an 8-bit E4M3 (FN variant) pattern: bit 7 sign, bits 6-3
+    exponent (bias 7), bits 2-0 mantissa; exponent field 0 is subnormal
+    2^-6 * m/8; no infinities; exponent 15 with mantissa 7 is NaN."""
+    byte = np.asarray(byte).astype(np.int64)
+    sign = (byte >> 7) & 1
+    e = (byte >> 3) & 15
+    m = byte & 7
+    mag = np.where(e == 0, np.exp2(-6.0) * (m / 8.0), np.exp2(e - 7.0) * (1.0 + m / 8.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, tensor_scale: float) -> np.ndarray:
+    """w[r][c] = E2M1(code[r][c]) * E4M3(scale[r][c // 16]) * tensor_scale."""
+    codes = np.asarray(codes)
+    q = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.float64)
+    q[..., 0::2] = e2m1_value(codes & 0x0F)
+    q[..., 1::2] = e2m1_value(codes >> 4)
+    s = np.repeat(e4m3_value(scales), 16, axis=-1)
+    return q * s * float(tensor_scale)
+
+
+# --------------------------------------------------------------------------
+# Expert weights
+# --------------------------------------------------------------------------
+
+class ExpertWeights:
+    """float64 W1_e [f][l] and W2_e [l][f], decoded on demand from the input
+    dict (dense stacks 'W1'/'W2', or NVFP4 '<W>_codes', '<W>_scales', '<W>_ts').
+    Decoded experts are memoised (a cache of decoded values, not a change of
+    arithmetic)."""
+
+    def __init__(self, inp: dict, cache_size: int = 64):
+        self.inp = inp
+        self.nvfp4 = inp.get("W1_codes") is not None
+        self.cache: "OrderedDict[int, tuple]" = OrderedDict()
+        self.cache_size = cache_size
+
+    def _decode(self, which: str, e: int) -> np.ndarray:
+        if self.nvfp4:
+            return nvfp4_dequant(self.inp[which + "_codes"][e], self.inp[which + "_scales"][e],
+                                 float(np.asarray(self.inp[which + "_ts"])[e]))
+        return as_f64(self.inp[which][e])
+
+    def __call__(self, e: int):
+        e = int(e)
+        if e in self.cache:
+            self.cache.move_to_end(e)
+            return self.cache[e]
+        w = (self._decode("W1", e), self._decode("W2", e))
+        self.cache[e] = w
+        if len(self.cache) > self.cache_size:
+            self.cache.popitem(last=False)
+        return w
+
+
+# --------------------------------------------------------------------------
+# The steps
+# --------------------------------------------------------------------------
+
+def down_project(x: np.ndarray, W_down: np.ndarray) -> np.ndarray:
+    """Step 1: z_t = W_down x_t for every row t of x.  [n][d] -> [n][l]."""
+    return as_f64(x) @ as_f64(W_down).T
+
+
+def router_logits(x: np.ndarray, W_r: np.ndarray, b_r=None) -> np.ndarray:
+    """Step 2: s_t = W_r x_t (+ b) in float64, returned as float32 (the
+    precision in which the top-k decision is taken)."""
+    s = as_f64(x) @ as_f64(W_r).T
+    if b_r is not None:
+        s = s + as_f64(b_r)[None, :]
+    return s.astype(np.float32)
+
+
+def select_topk(s: np.ndarray, k: int) -> np.ndarray:
+    """Step 3: per row, the k expert ids with the largest logits, in the order
+    (logit desc, id asc).  A stable sort of -s keeps equal logits in id order."""
+    order = np.argsort(-np.asarray(s, dtype=np.float32), axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def gate_weights(s: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Step 4: g_{t,j} = exp(s_{t,I_j}) / sum_j' exp(s_{t,I_j'}) over the k
+    selected logits (shifted by the row's top logit for range)."""
+    sel = np.take_along_axis(np.asarray(s, dtype=np.float64), idx.astype(np.int64), axis=1)
+    w = np.exp(sel - sel[:, :1])
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def expert_ffn(z_t: np.ndarray, W1_e: np.ndarray, W2_e: np.ndarray) -> np.ndarray:
+    """Step 5: y = W2_e (max(0, W1_e z_t))^2, a ReLU^2 FFN in the latent space."""
+    h = np.maximum(W1_e @ z_t, 0.0) ** 2
+    return W2_e @ h
+
+
+def permutation(idx: np.ndarray, E: int):
+    """Integer side: counts [E], offsets [E+1] (exclusive prefix sum with the
+    total at the end), perm [n*k] (stable sort of the flat pair index
+    t*k + j by expert) and inv [n*k] = perm^-1, all int32."""
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(flat, kind="stable")
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    return (counts.astype(np.int32), offsets.astype(np.int32), perm.astype(np.int32),
+            inv.astype(np.int32))
+
+
+def route(inp: dict, k: int):
+    """Steps 2-4 for every token: logits (float32), idx, gates (float64)."""
+    s = router_logits(inp["x"], inp["W_r"], inp.get("b_r"))
+    idx = select_topk(s, k)
+    return s, idx, gate_weights(s, idx)
+
+
+def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> dict:
+    """The layer forward for the given token rows (all rows by default).
+
+    Returns float64 z [n][l], c [n][l], out [n][d], and the routing of those
+    rows: logits (float32) [n][E], idx [n][k], gate [n][k].  Tokens are
+    independent (no capacity limit, every routed pair is computed), so any
+    subset of rows gives the same values as the full call for those rows.
+    """
+    x = np.asarray(inp["x"])
+    if tokens is not None:
+        x = x[np.asarray(tokens)]
+    experts = experts or ExpertWeights(inp)
+    z = down_project(x, inp["W_down"])
+    s = router_logits(x, inp["W_r"], inp.get("b_r"))
+    idx = select_topk(s, k)
+    g = gate_weights(s, idx)
+    n, l = z.shape
+    c = np.zeros((n, l), dtype=np.float64)
+    for t in range(n):
+        for j in range(k):
+            W1_e, W2_e = experts(idx[t, j])
+            c[t] += g[t, j] * expert_ffn(z[t], W1_e, W2_e)
+    out = c @ as_f64(inp["W_up"]).T
+    if inp.get("W_s1") is not None:
+        hs = np.maximum(as_f64(x) @ as_f64(inp["W_s1"]).T, 0.0) ** 2
+        out = out + hs @ as_f64(inp["W_s2"]).T
+    return dict(z=z, logits=s, idx=idx, gate=g, c=c, out=out)

@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test computes the expected value by a different route than the oracle:
+brute force on tiny inputs, closed forms, invariants, special cases that
+reduce to plain matrix products, or library routines (torch dtype casts).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import latentmoe_oracle as O
+from sparse_moe_layer_06_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def host_inputs(cfg, seed=0):
+    inp = synth.make_inputs(cfg, seed, "cpu")
+    return {k: synth.host_view(v) for k, v in inp.items()}
+
+
+TINY = synth.CONFIGS["tiny_f32"]
+SMALL_BF16 = TINY.with_(name="small_bf16", T=48, d=128, l=32, E=12, k=3, f=64, f_s=96,
+                        act="bf16", experts="bf16")
+SMALL_NVFP4 = TINY.with_(name="small_nvfp4", T=40, d=128, l=32, E=8, k=2, f=64, f_s=0,
+                         act="bf16", experts="nvfp4")
+SMALL_ZIPF = SMALL_BF16.with_(name="small_zipf", zipf_bias=True, f_s=0)
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def _read_golden_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def test_e2m1_all_codes_match_golden_grid():
+    # The E2M1 grid: 2 exponent bits (bias 1), 1 mantissa bit, sign bit.
+    rows = _read_golden_table("e2m1_codes.txt")
+    assert len(rows) == 16
+    for code_s, val_s in rows:
+        assert O.e2m1_value(int(code_s, 16)) == float(val_s), code_s
+
+
+def test_e4m3_all_patterns_match_torch_float8():
+    # Library routine: torch's float8_e4m3fn decoding of every byte.
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_value(b)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2  # 0x7f and 0xff
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e4m3_landmarks():
+    # Facts of the format: max finite 448, min normal 2^-6, min subnormal 2^-9, one = 0x38.
+    assert O.e4m3_value(0x7E) == 448.0
+    assert O.e4m3_value(0x08) == 2.0 ** -6
+    assert O.e4m3_value(0x01) == 2.0 ** -9
+    assert O.e4m3_value(0x38) == 1.0
+    assert O.e4m3_value(0xB8) == -1.0
+    pos = O.e4m3_value(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)  # monotone in the byte for positive patterns
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, size=1 << 20, dtype=np.uint32).astype(np.uint16)
+    # drop NaN patterns (exponent all ones, nonzero mantissa)
+    keep = ~(((bits & 0x7F80) == 0x7F80) & ((bits & 0x007F) != 0))
+    bits = bits[keep]
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_to_f64(bits)
+    assert np.array_equal(got, ref)
+
+
+def test_nvfp4_generator_roundtrip_is_nearest_grid_point():
+    # The generator's encoder and the oracle's decoder are independent: decoding
+    # what was encoded must give the nearest E2M1 point (ties to even mantissa)
+    # to W / (s * ts) clamped to [-6, 6].
+    g = torch.Generator().manual_seed(7)
+    R, K = 64, 256
+    W = torch.randn((R, K), generator=g) / math.sqrt(K)
+    # plant exact midpoints and clamp cases
+    ts = np.float32(1.0 / math.sqrt(K))
+    su = torch.rand((R, K // 16), generator=g) * 1.5 + 0.5
+    codes, scales, ts_val = synth._nvfp4_quantize(W, su, K)
+    s = O.e4m3_value(scales.numpy())
+    assert np.all((s >= 0.5) & (s <= 2.0))
+    w = O.nvfp4_dequant(codes.numpy(), scales.numpy(), ts_val)
+    assert ts_val == float(ts)
+    v = np.clip(W.numpy().astype(np.float64) / (np.repeat(s, 16, axis=1) * float(np.float32(ts))), -6, 6)
+    q = w / (np.repeat(s, 16, axis=1) * ts_val)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    dist = np.abs(np.abs(v)[..., None] - grid)
+    best = np.min(dist, axis=-1)
+    assert np.allclose(np.abs(np.abs(q) - np.abs(v)), best, rtol=0, atol=1e-6)
+
+
+def test_nvfp4_ties_go_to_even_mantissa():
+    # Exact midpoints between E2M1 neighbours, with s = 1 and ts chosen as 1.
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75, 7.0, -9.0])
+    expect = np.array([0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, -1.0, 6.0, -6.0])
+    codes = synth._e2m1_codes(mids.clamp(-6, 6))
+    assert np.array_equal(O.e2m1_value(codes.numpy()), expect)
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+
+def brute_force_topk_set(s_row, k):
+    """Expert e is selected iff fewer than k experts precede it in the order
+    (logit desc, id asc).  O(E^2) counting, no sort."""
+    E = s_row.size
+    rank = np.array([np.sum(s_row > s_row[e]) + np.sum(s_row[:e] == s_row[e]) for e in range(E)])
+    return rank
+
+
+def test_topk_matches_brute_force_rank_with_ties():
+    rng = np.random.default_rng(3)
+    for E, k in [(16, 4), (33, 7), (64, 1), (20, 20)]:
+        s = (rng.integers(-6, 6, size=(50, E)) / 4.0).astype(np.float32)  # many exact ties
+        idx = O.select_topk(s, k)
+        for t in range(s.shape[0]):
+            rank = brute_force_topk_set(s[t], k)
+            expect = np.argsort(rank)[:k]  # ranks are a permutation of 0..E-1
+            assert np.array_equal(idx[t], expect)
+
+
+def test_gates_sum_to_one_and_equal_renormalised_full_softmax():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((100, 64)).astype(np.float32) * 3
+    idx = O.select_topk(s, 9)
+    g = O.gate_weights(s, idx)
+    assert np.max(np.abs(g.sum(1) - 1.0)) <= 1e-12
+    full = np.exp(s.astype(np.float64))
+    full /= full.sum(1, keepdims=True)
+    sel = np.take_along_axis(full, idx.astype(np.int64), 1)
+    assert rel_err(g, sel / sel.sum(1, keepdims=True)) <= 1e-12
+    assert np.all(np.diff(g, axis=1) <= 0)  # ordered like the logits
+
+
+def test_logits_are_float32_of_float64_product():
+    inp = host_inputs(TINY)
+    s = O.router_logits(inp["x"], inp["W_r"])
+    assert s.dtype == np.float32
+    ref = inp["x"].astype(np.float64) @ inp["W_r"].astype(np.float64).T
+    assert np.array_equal(s, ref.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Permutation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,n,k", [(16, 64, 4), (7, 1, 7), (5, 33, 1), (128, 200, 8)])
+def test_permutation_matches_brute_force(E, n, k):
+    rng = np.random.default_rng(E * 1000 + n)
+    # skewed draws so that some experts are empty
+    idx = np.minimum(rng.geometric(0.3, size=(n, k)) - 1, E - 1).astype(np.int32)
+    counts, offsets, perm, inv = O.permutation(idx, E)
+    flat = idx.reshape(-1)
+    bf_counts = np.array([sum(1 for v in flat if v == e) for e in range(E)])
+    assert np.array_equal(counts, bf_counts)
+    assert offsets[0] == 0 and offsets[-1] == n * k
+    assert np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(np.sort(perm), np.arange(n * k))  # bijection
+    assert np.array_equal(inv[perm], np.arange(n * k))
+    # expected perm built by walking experts in order and pairs in order
+    expect = [p for e in range(E) for p in range(n * k) if flat[p] == e]
+    assert np.array_equal(perm, np.array(expect, dtype=np.int32))
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+
+def dense_bruteforce(inp, k):
+    """Every expert on every token, weighted by the full-E softmax masked to
+    the top-k set and renormalised; one up-projection per expert."""
+    x = O.as_f64(inp["x"])
+    z = x @ O.as_f64(inp["W_down"]).T
+    s = O.router_logits(inp["x"], inp["W_r"], inp.get("b_r")).astype(np.float64)
+    E = s.shape[1]
+    W_up = O.as_f64(inp["W_up"])
+    ew = O.ExpertWeights(inp)
+    out = np.zeros((x.shape[0], W_up.shape[0]))
+    for t in range(x.shape[0]):
+        rank = brute_force_topk_set(s[t].astype(np.float32), k)
+        mask = (rank < k).astype(np.float64)
+        p = np.exp(s[t] - s[t].max()) * mask
+        p /= p.sum()
+        for e in range(E):
+            if p[e] == 0.0:
+                continue
+            W1, W2 = ew(e)
+            h = np.maximum(W1 @ z[t], 0) ** 2
+            out[t] += p[e] * (W_up @ (W2 @ h))
+    if inp.get("W_s1") is not None:
+        hs = np.maximum(x @ O.as_f64(inp["W_s1"]).T, 0) ** 2
+        out += hs @ O.as_f64(inp["W_s2"]).T
+    return out
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_ZIPF,
+                                 TINY.with_(k=1), TINY.with_(E=5, k=5)], ids=lambda c: f"{c.name}-E{c.E}k{c.k}")
+def test_sparse_equals_dense_bruteforce(cfg):
+    inp = host_inputs(cfg)
+    got = O.forward(inp, cfg.k)["out"]
+    ref = dense_bruteforce(inp, cfg.k)
+    assert rel_err(got, ref) <= 1e-12
+
+
+def test_single_expert_reduces_to_low_rank_ffn():
+    cfg = SMALL_BF16.with_(E=1, k=1)
+    inp = host_inputs(cfg)
+    r = O.forward(inp, 1)
+    assert np.all(r["gate"] == 1.0) and np.all(r["idx"] == 0)
+    x = torch.from_numpy(O.as_f64(inp["x"]))
+    W = {n: torch.from_numpy(O.as_f64(inp[n])) for n in ["W_down", "W_up", "W_s1", "W_s2"]}
+    W1 = torch.from_numpy(O.as_f64(inp["W1"][0]))
+    W2 = torch.from_numpy(O.as_f64(inp["W2"][0]))
+    ref = torch.relu(x @ W["W_down"].T @ W1.T).square() @ W2.T @ W["W_up"].T
+    ref += torch.relu(x @ W["W_s1"].T).square() @ W["W_s2"].T
+    assert rel_err(r["out"], ref.numpy()) <= 1e-12
+
+
+def test_doubling_down_projection_scales_routed_output_by_four():
+    cfg = SMALL_BF16.with_(f_s=0)
+    inp = host_inputs(cfg)
+    a = O.forward(inp, cfg.k)
+    inp2 = dict(inp)
+    inp2["W_down"] = (O.as_f64(inp["W_down"]) * 2.0)
+    b = O.forward(inp2, cfg.k)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert rel_err(b["out"], 4.0 * a["out"]) <= 1e-14
+
+
+def test_combine_then_up_equals_up_then_combine():
+    cfg = SMALL_BF16.with_(f_s=0)
+    inp = host_inputs(cfg)
+    r = O.forward(inp, cfg.k)
+    W_up = O.as_f64(inp["W_up"])
+    ew = O.ExpertWeights(inp)
+    out = np.zeros_like(r["out"])
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            W1, W2 = ew(r["idx"][t, j])
+            out[t] += W_up @ (r["gate"][t, j] * O.expert_ffn(r["z"][t], W1, W2))
+    assert rel_err(r["out"], out) <= 1e-12
+
+
+def test_relabelling_experts_leaves_output_unchanged():
+    cfg = SMALL_BF16
+    inp = host_inputs(cfg)
+    rng = np.random.default_rng(5)
+    p = rng.permutation(cfg.E)  # new expert i is old expert p[i]
+    inp2 = dict(inp)
+    inp2["W_r"] = inp["W_r"][p]
+    inp2["W1"] = inp["W1"][p]
+    inp2["W2"] = inp["W2"][p]
+    a = O.forward(inp, cfg.k)
+    b = O.forward(inp2, cfg.k)
+    assert rel_err(b["out"], a["out"]) <= 1e-12
+    ca = O.permutation(a["idx"], cfg.E)[0]
+    cb = O.permutation(b["idx"], cfg.E)[0]
+    assert np.array_equal(cb, ca[p])
+
+
+def test_k_equals_E_is_dense_moe_with_full_softmax():
+    cfg = TINY.with_(E=6, k=6)
+    inp = host_inputs(cfg)
+    r = O.forward(inp, cfg.k)
+    x = O.as_f64(inp["x"])
+    s = x @ O.as_f64(inp["W_r"]).T
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    z = x @ O.as_f64(inp["W_down"]).T
+    c = np.zeros_like(z)
+    for e in range(cfg.E):
+        W1, W2 = O.as_f64(inp["W1"][e]), O.as_f64(inp["W2"][e])
+        c += p[:, e:e + 1] * (np.maximum(z @ W1.T, 0) ** 2 @ W2.T)
+    assert rel_err(r["out"], c @ O.as_f64(inp["W_up"]).T) <= 1e-6  # float32 logits in the gate
+
+
+def test_shared_expert_alone():
+    cfg = SMALL_BF16
+    inp = host_inputs(cfg)
+    inp["W_up"] = np.zeros_like(inp["W_up"])
+    r = O.forward(inp, cfg.k)
+    x = torch.from_numpy(O.as_f64(inp["x"]))
+    ref = torch.relu(x @ torch.from_numpy(O.as_f64(inp["W_s1"])).T).square() @ torch.from_numpy(O.as_f64(inp["W_s2"])).T
+    assert rel_err(r["out"], ref.numpy()) <= 1e-12
+
+
+def test_nvfp4_forward_equals_dense_forward_on_dequantised_weights():
+    cfg = SMALL_NVFP4
+    inp = host_inputs(cfg)
+    dense = dict(inp)
+    dense["W1"] = np.stack([O.nvfp4_dequant(inp["W1_codes"][e], inp["W1_scales"][e], inp["W1_ts"][e]) for e in range(cfg.E)])
+    dense["W2"] = np.stack([O.nvfp4_dequant(inp["W2_codes"][e], inp["W2_scales"][e], inp["W2_ts"][e]) for e in range(cfg.E)])
+    for n in ("W1_codes", "W1_scales", "W1_ts", "W2_codes", "W2_scales", "W2_ts"):
+        dense[n] = None
+    a = O.forward(inp, cfg.k)["out"]
+    b = O.forward(dense, cfg.k)["out"]
+    assert np.array_equal(a, b)
+
+
+def test_token_subset_equals_full_call_rows():
+    inp = host_inputs(SMALL_BF16)
+    full = O.forward(inp, SMALL_BF16.k)
+    sub = O.forward(inp, SMALL_BF16.k, tokens=[5, 0, 17])
+    # same values up to the summation order of the library matmul
+    assert rel_err(sub["out"], full["out"][[5, 0, 17]]) <= 1e-13
+    assert np.array_equal(sub["idx"], full["idx"][[5, 0, 17]])
+
+
+def test_latent_width_is_quarter_of_hidden_in_every_workload():
+    for cfg in synth.CONFIGS.values():
+        assert cfg.l * 4 == cfg.d, cfg.name
+        assert 1 <= cfg.k <= cfg.E
+
+
+def test_workload_shapes():
+    c = synth.CONFIGS
+    assert (c["prefill_bf16"].d, c["prefill_bf16"].E, c["prefill_bf16"].k) == (8192, 512, 22)
+    assert c["decode_bf16_zipf"].zipf_bias and c["decode_bf16_zipf"].T == 64
+    assert c["prefill_nvfp4"].experts == "nvfp4"
+
+
+def test_zipf_bias_values():
+    inp = synth.make_inputs(SMALL_ZIPF, 0, "cpu")
+    b = inp["b_r"].numpy()
+    assert b[0] == 0.0
+    assert np.allclose(b, -2.0 * np.log(np.arange(1, SMALL_ZIPF.E + 1)), rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# The pins catch planted mistakes (mistakes planted in the oracle, on the CPU)
+# ---------------------------------------------------------------------------
+
+def _plant(monkeypatch, which):
+    if which == "gate_full_softmax":
+        def bad(s, idx):
+            full = np.exp(np.asarray(s, np.float64))
+            full /= full.sum(1, keepdims=True)
+            return np.take_along_axis(full, idx.astype(np.int64), 1)
+        monkeypatch.setattr(O, "gate_weights", bad)
+    elif which == "relu_not_squared":
+        monkeypatch.setattr(O, "expert_ffn", lambda z, W1, W2: W2 @ np.maximum(W1 @ z, 0.0))
+    elif which == "off_by_one_expert":
+        orig = O.ExpertWeights.__call__
+        monkeypatch.setattr(O.ExpertWeights, "__call__", lambda self, e: orig(self, (int(e) + 1) % len(self.inp["W1"])))
+    elif which == "tie_high_index":
+        monkeypatch.setattr(O, "select_topk", lambda s, k: (s.shape[1] - 1 - np.argsort(-s[:, ::-1], axis=1, kind="stable")[:, :k]).astype(np.int32))
+    elif which == "dropped_last_expert":
+        monkeypatch.setattr(O, "gate_weights", lambda s, idx: np.concatenate([np.ones((idx.shape[0], 1)), np.zeros((idx.shape[0], idx.shape[1] - 1))], 1))
+
+
+@pytest.mark.parametrize("which", ["gate_full_softmax", "relu_not_squared", "off_by_one_expert", "dropped_last_expert"])
+def test_planted_mistake_is_caught_by_dense_pin(monkeypatch, which):
+    cfg = TINY
+    inp = host_inputs(cfg)
+    ref = dense_bruteforce(inp, cfg.k)  # computed before planting
+    _plant(monkeypatch, which)
+    got = O.forward(inp, cfg.k)["out"]
+    assert rel_err(got, ref) > 1e-6
+
+
+def test_planted_tie_mistake_is_caught_by_rank_pin(monkeypatch):
+    s = np.array([[1.0, 2.0, 2.0, 0.5, 2.0]], dtype=np.float32)
+    _plant(monkeypatch, "tie_high_index")
+    idx = O.select_topk(s, 2)
+    rank = brute_force_topk_set(s[0], 2)
+    assert not np.array_equal(idx[0], np.argsort(rank)[:2])
