@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""LatentMoE layer forward benchmark on one MI355X (gfx950).
+
+One step = one whole forward of the layer (projection + router, top-k,
+permutation, both expert GEMMs, combine, up-projection + shared expert) over
+one batch of seeded synthetic inputs already resident in HBM.  The default
+workload is the Ultra-shape prefill layer: T=8192 tokens, d=8192, l=2048,
+E=512, top-22, f=2048, shared expert 8192, bf16 with fp32 accumulation.
+
+Prints one JSON line:
+  value         whole-layer tokens/s over the K timed steps
+  roofline      the dominant kernel (the grouped expert GEMM): algorithmic
+                FLOPs per launch / its average launch time from hipEvents on
+                the launch stream, against the bf16 dense MFMA peak
+  decode        the weight-streaming decode layer (T=64, skewed routing):
+                tokens/s and algorithmic HBM bytes / time against 8 TB/s
+  cpu_baseline  the CPU oracle on a bounded token sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LatentMoE fwd tokens/s + % MFMA peak (prefill) / % HBM BW (decode), d=8192"
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_prefill_bf16_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_mfma.hip", "device_common.hpp", "lmoe_internal.hpp"):
+        with open(os.path.join(ROOT, "sparse_moe_layer_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per grouped-GEMM launch from the committed rocprofv3 counter
+    runs, only if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_steps(call, steps, torch):
+    """Average ms per call over `steps` back-to-back calls (hipEvents on the stream)."""
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(s)
+    for _ in range(steps):
+        call()
+    b.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / steps, wall
+
+
+def prefill(cfg, steps, warmup, torch, B, synth):
+    log(f"bench: generating inputs {cfg.name}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    ws = B.alloc_workspace(cfg)
+    call = B.Call(cfg, inp, out, ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    log(f"bench: timing {steps} steps")
+    ms, wall = time_steps(call, steps, torch)
+    log(f"bench: {ms:.3f} ms/step")
+
+    # Per-kernel durations over the same number of steps (separate pass, so the
+    # headline timing has no extra events between launches).
+    with B.KernelTimer(capacity=64 * steps) as kt:
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+    per = kt.by_kernel()
+    kernels = {n: dict(avg_ms=sum(v) / len(v), launches_per_step=len(v) / steps,
+                       ms_per_step=sum(v) / steps) for n, v in per.items()}
+    return inp, out, ms, wall, kernels
+
+
+def decode(cfg, steps, torch, B, synth):
+    log(f"bench: generating inputs {cfg.name}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    ws = B.alloc_workspace(cfg)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    call = B.Call(cfg, inp, out, ws, debug=dict(counts=counts))
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")  # evicts the 256 MB Infinity Cache
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        call()
+        b.record(s)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+    touched = int((counts > 0).sum().item())
+    l, f, d, E, T = cfg.l, cfg.f, cfg.d, cfg.E, cfg.T
+    bytes_alg = touched * 2 * l * f * 2 + (2 * d * l + d * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    return dict(workload=f"{cfg.name} T={T} d={d} l={l} E={E} k={cfg.k} f={f}", tokens_per_s=T / (ms * 1e-3),
+                ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
+                hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
+                "512 MB buffer written between steps" % steps)
+
+
+def cpu_baseline(cfg, inp, n_tokens, synth):
+    import numpy as np
+    from oracle import latentmoe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    h = {}
+    for k, v in inp.items():
+        if v is None:
+            h[k] = None
+        elif k in ("W1", "W2"):
+            h[k] = synth.LazyExperts(v)
+        else:
+            h[k] = synth.host_view(v)
+    tokens = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int64)
+    # copy the experts these tokens use to the host first: device->host copies are not oracle work
+    _, idx, _ = O.route({"x": h["x"][tokens], "W_r": h["W_r"], "b_r": h.get("b_r")}, cfg.k)
+    for e in np.unique(idx):
+        h["W1"][e], h["W2"][e]
+    t0 = time.perf_counter()
+    O.forward(h, cfg.k, tokens=tokens, experts=O.ExpertWeights(h, cache_size=cfg.E))
+    dt = time.perf_counter() - t0
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n_tokens} evenly spaced tokens of {cfg.name} (routing, experts, up-projection "
+                       f"and shared expert of those tokens), {dt:.1f} s, float64 numpy")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer is benchmarked on a single MI355X "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_moe_layer_06_amd import binding as B
+    from sparse_moe_layer_06_amd import synth
+
+    B.lib()
+    cfg = synth.CONFIGS[args.workload]
+    inp, out, ms, wall, kernels = prefill(cfg, args.steps, args.warmup, torch, B, synth)
+    tokens_per_s = cfg.T / (ms * 1e-3)
+    layer_tflops = cfg.flops / (ms * 1e-3) / 1e12
+
+    # Dominant kernel: the grouped expert GEMM (two launches per step, equal FLOPs).
+    gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
+    g = kernels.get(gname)
+    flops_per_launch = 2.0 * cfg.T * cfg.k * cfg.l * cfg.f
+    roofline = None
+    if g:
+        achieved = flops_per_launch / (g["avg_ms"] * 1e-3) / 1e12
+        roofline = dict(kernel=gname, bound="mfma", achieved=achieved, peak=PEAK_BF16_FLOPS / 1e12,
+                        unit="TFLOP/s", frac=achieved * 1e12 / PEAK_BF16_FLOPS, traffic=measured_traffic(),
+                        avg_launch_ms=g["avg_ms"], alg_flops_per_launch=flops_per_launch)
+    for v in kernels.values():
+        v["avg_ms"] = round(v["avg_ms"], 4)
+        v["ms_per_step"] = round(v["ms_per_step"], 4)
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: LatentMoE layer T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} "
+                               f"k={cfg.k} f={cfg.f} f_s={cfg.f_s}, {cfg.experts} experts, seed 0",
+                   "global_batch": cfg.T, "parallelism": "single GPU"},
+        "layer_tflops": layer_tflops,
+        "layer_mfma_frac": layer_tflops * 1e12 / PEAK_BF16_FLOPS,
+        "wall_s_timed": wall,
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_decode:
+        result["decode"] = decode(synth.CONFIGS["decode_bf16_zipf"], args.decode_steps, torch, B, synth)
+    if not args.no_cpu:
+        log("bench: cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens, synth)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * latentmoe.h -- C ABI of the LatentMoE layer forward for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (Nemotron 3 overview article, section 2.2 "LatentMoE", steps 1-3
+ * and the paragraph after its comparison table; Nemotron 3 Super blog,
+ * section "Latent MoE"; Nemotron 3 Ultra release news, architecture
+ * paragraph):
+ *
+ *   z_t   = W_down x_t                      hidden d -> latent l = d/4
+ *   s_t   = W_r x_t + b                     router logits over E experts (reads x in d)
+ *   I_t   = top-k of s_t, ordered (logit desc, expert id asc)
+ *   g_t   = softmax over the k selected logits
+ *   y_tj  = W2_e (max(0, W1_e z_t))^2       routed expert e = I_t[j], ReLU^2 FFN in l
+ *   c_t   = sum_j g_tj y_tj                 combine in the latent space
+ *   out_t = W_up c_t  [+ W_s2 (max(0, W_s1 x_t))^2]   back to d, optional shared expert in d
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *     never frees, keeps or reallocates it after the call returns, and it
+ *     never allocates device memory itself: scratch comes from the caller's
+ *     workspace (see lmoe_workspace_bytes).
+ *   - Weights are stored out x in, row-major (fan-in contiguous):
+ *       W_down [l][d], W_r [E][d], W1 [E][f][l], W2 [E][l][f], W_up [d][l],
+ *       W_s1 [f_s][d], W_s2 [d][f_s].  x and out are [T][d] row-major.
+ *   - Activation dtype (dims.act_dtype) is the storage type of x, W_down,
+ *     W_r, W_up, W_s1, W_s2, out and of the latent intermediates.  Every
+ *     product accumulates in fp32.  Router logits and gates are fp32.
+ *   - Calls are asynchronous: kernels are enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and the call returns without a
+ *     host synchronisation.  Device faults surface at the caller's next
+ *     synchronisation.
+ *   - Errors are returned as negative codes, and are detected on the host
+ *     before anything is enqueued: on error no output is touched.  A launch
+ *     failure returns LMOE_ERR_HIP (detail: lmoe_last_hip_error()).
+ *   - Pointers must be 16-byte aligned.  NaN/Inf inputs give undefined
+ *     outputs.  Calls that share a workspace must not run concurrently.
+ */
+#ifndef LATENTMOE_H
+#define LATENTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define LMOE_OK             0
+#define LMOE_ERR_NULL      -1  /* a required pointer is NULL */
+#define LMOE_ERR_SHAPE     -2  /* a size is out of range (see lmoe_dims) */
+#define LMOE_ERR_DTYPE     -3  /* unknown dtype or unsupported combination */
+#define LMOE_ERR_ALIGN     -4  /* a pointer is not 16-byte aligned */
+#define LMOE_ERR_WORKSPACE -5  /* workspace missing or smaller than lmoe_workspace_bytes */
+#define LMOE_ERR_HIP       -6  /* a HIP launch failed */
+
+/* ---- dtypes ---------------------------------------------------------- */
+#define LMOE_F32   0  /* IEEE binary32 */
+#define LMOE_BF16  1  /* bfloat16 */
+#define LMOE_NVFP4 2  /* routed-expert weights only, see lmoe_experts */
+
+/*
+ * Layer sizes.  Constraints (LMOE_ERR_SHAPE otherwise):
+ *   T >= 1 tokens; d >= 256 and d % 256 == 0; l == d / 4 (latent width,
+ *   overview section 2.2 step 1); 1 <= E <= 1024 experts; 1 <= k <= E;
+ *   f >= 64 and f % 64 == 0; f_s == 0 (no shared expert) or f_s % 64 == 0.
+ * Dtypes (LMOE_ERR_DTYPE otherwise):
+ *   act_dtype LMOE_F32 with expert_dtype LMOE_F32, or
+ *   act_dtype LMOE_BF16 with expert_dtype LMOE_BF16 or LMOE_NVFP4.
+ */
+typedef struct lmoe_dims {
+    int64_t T, d, l, E, k, f, f_s;
+    int32_t act_dtype;
+    int32_t expert_dtype;
+} lmoe_dims;
+
+/*
+ * Routed-expert weights.  Dense formats (F32/BF16) use W1 [E][f][l] and
+ * W2 [E][l][f] in the activation dtype.  NVFP4 (overview section 3.1.1,
+ * NVFP4 format: E2M1 elements in 16-element micro-blocks with an E4M3 block
+ * scale; the Ultra release news, quantisation paragraph: 4-bit weights run
+ * against 16-bit activations) uses, per matrix M in {W1, W2} of shape
+ * [E][rows][K]:
+ *   M_codes  [E][rows][K/2] uint8: E2M1 codes, element 2i in the low nibble
+ *                                  and 2i+1 in the high nibble;
+ *   M_scales [E][rows][K/16] uint8: E4M3 (FN) scale of each 16-element block
+ *                                   along K;
+ *   M_ts     [E] fp32: per-expert tensor scale.
+ * The weight is w = E2M1(code) * E4M3(scale) * ts.  Unused fields are ignored.
+ */
+typedef struct lmoe_experts {
+    const void* W1;
+    const void* W2;
+    const uint8_t* W1_codes;
+    const uint8_t* W1_scales;
+    const float* W1_ts;
+    const uint8_t* W2_codes;
+    const uint8_t* W2_scales;
+    const float* W2_ts;
+} lmoe_experts;
+
+/* Shared expert in d (overview section 2.2, paragraph after the table):
+ * W_s1 [f_s][d], W_s2 [d][f_s] in the activation dtype.  Pass NULL to the
+ * entry points (and f_s = 0) for a layer without one. */
+typedef struct lmoe_shared {
+    const void* W_s1;
+    const void* W_s2;
+} lmoe_shared;
+
+/*
+ * Optional views of the intermediates of latentmoe_forward.  Each non-NULL
+ * field is used as the storage of that intermediate (no extra copy); NULL
+ * fields live in the workspace.
+ *   z [T][l] act dtype; logits [T][E] fp32 (bias included); topk_idx [T][k]
+ *   int32; topk_gate [T][k] fp32; counts [E] int32; offsets [E+1] int32;
+ *   perm [T*k] int32; inv [T*k] int32; c [T][l] act dtype.
+ */
+typedef struct lmoe_debug {
+    void* z;
+    float* logits;
+    int32_t* topk_idx;
+    float* topk_gate;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv;
+    void* c;
+} lmoe_debug;
+
+/* ---- sizing, validation, diagnostics (host only, no GPU needed) ------ */
+
+/* Bytes of device workspace the forward and staged entry points need for
+ * these sizes; 0 if dims is invalid.  The workspace is caller-owned device
+ * memory, 256-byte aligned, reusable across calls with the same or smaller
+ * sizes. */
+size_t lmoe_workspace_bytes(const lmoe_dims* dims);
+
+/* Checks sizes and dtypes (see lmoe_dims) without touching the GPU. */
+int lmoe_validate_dims(const lmoe_dims* dims);
+
+/* Short English text for a status code. */
+const char* lmoe_strerror(int status);
+
+/* hipError_t of the last failed launch in this thread (0 if none). */
+int lmoe_last_hip_error(void);
+
+/* ---- per-kernel timing (optional) ------------------------------------ */
+
+/* One timed kernel launch: the kernel's name and its duration between two
+ * hipEvents recorded on the launch's stream right before and after it. */
+typedef struct lmoe_kernel_time {
+    const char* name;
+    float ms;
+} lmoe_kernel_time;
+
+/* Starts recording: every kernel launched by the entry points from now on is
+ * bracketed by a pair of hipEvents on its stream, up to `capacity` launches
+ * (later launches are not recorded).  Events are created here, on the host
+ * thread's current device.  Not thread-safe: one recorder per process. */
+int lmoe_timing_start(int capacity);
+
+/* Waits for the recorded events, writes up to `capacity` records to `out`,
+ * sets *count to the number recorded, releases the events and stops
+ * recording.  Returns LMOE_ERR_HIP if an event query fails. */
+int lmoe_timing_stop(lmoe_kernel_time* out, int capacity, int* count);
+
+/* ---- the layer ------------------------------------------------------- */
+
+/*
+ * The whole forward: out [T][d] = LatentMoE(x).  router_bias [E] fp32 may be
+ * NULL (no bias); shared may be NULL (then dims.f_s must be 0); dbg may be
+ * NULL.  workspace must hold lmoe_workspace_bytes(dims) bytes.  The result
+ * equals running lmoe_project_route, lmoe_permute, lmoe_experts_ffn and
+ * lmoe_combine_up in that order.
+ */
+int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down,
+                      const void* W_router, const float* router_bias,
+                      const lmoe_experts* experts, const void* W_up,
+                      const lmoe_shared* shared, int k, void* out,
+                      void* workspace, size_t workspace_bytes,
+                      const lmoe_debug* dbg, void* stream);
+
+/* ---- staged entry points (same conventions) -------------------------- */
+
+/*
+ * Steps 1-4 (overview section 2.2 step 1; Ultra release news, 512 experts
+ * with top-22): z = x W_down^T [T][l] (act dtype), logits = x W_r^T + b
+ * [T][E] fp32, topk_idx [T][k] int32 in (logit desc, id asc) order,
+ * topk_gate [T][k] fp32 = softmax of the selected logits.  If shared is
+ * non-NULL also hs = (max(0, x W_s1^T))^2 [T][f_s] (act dtype), the first
+ * half of the shared expert (it reads the same x).  hs may be NULL iff
+ * shared is NULL.
+ */
+int lmoe_project_route(const lmoe_dims* dims, const void* x, const void* W_down,
+                       const void* W_router, const float* router_bias,
+                       const lmoe_shared* shared, void* z, float* logits,
+                       int32_t* topk_idx, float* topk_gate, void* hs,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Token permutation: counts[e] = number of (t, j) with topk_idx[t][j] = e;
+ * offsets[e] = sum of counts below e, offsets[E] = T*k; perm[p] = the flat
+ * pair index t*k + j at sorted position p, stable (pairs ascend within each
+ * expert); inv = perm^-1.  Integer results are exact and deterministic.
+ */
+int lmoe_permute(const lmoe_dims* dims, const int32_t* topk_idx, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Routed experts in the latent space (overview section 2.2 step 2), in
+ * sorted order: for each sorted position p with pair (t, j) = perm[p] and
+ * expert e, Y[p] = topk_gate[t][j] * W2_e (max(0, W1_e z_t))^2, Y [T*k][l]
+ * act dtype.  NVFP4 weights are decoded in the kernel.
+ */
+int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const float* topk_gate,
+                     const int32_t* offsets, const int32_t* perm,
+                     const lmoe_experts* experts, void* Y,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Combine and up-projection (overview section 2.2 step 3): c_t = sum over
+ * j = 0..k-1, in that order, of Y[inv[t*k + j]] (no atomics; deterministic),
+ * out = c W_up^T [+ hs W_s2^T if shared].  c [T][l] may be NULL (then it
+ * lives in the workspace).
+ */
+int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv,
+                    const void* W_up, const lmoe_shared* shared, const void* hs,
+                    void* c, void* out, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENTMOE_H */

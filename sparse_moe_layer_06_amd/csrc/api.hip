@@ -1,0 +1,376 @@
+// C ABI of the LatentMoE forward: host-side validation, workspace plan and
+// the launch sequence.  Every step runs in this library's kernels; nothing
+// here allocates device memory or synchronises the host.
+//
+// Launch sequence of latentmoe_forward (Nemotron 3 overview, section 2.2,
+// steps 1-3; shared expert per the paragraph after its table):
+//   1. dense MFMA GEMM  x [W_down; W_r; W_s1]^T -> z, logits (+bias), hs
+//   2. top-k + softmax gate                     -> idx, gate
+//   3. permutation (hist, scan + tile table, stable scatter)
+//   4. grouped GEMM  H = relu(z[perm] W1_e^T)^2
+//   5. grouped GEMM  Y = gate * (H W2_e^T)
+//   6. combine       c_t = sum_j Y[inv(t, j)]
+//   7. dense GEMM    out = [c | hs] [W_up | W_s2]^T
+#include <string.h>
+
+#include "lmoe_internal.hpp"
+
+namespace lmoe {
+
+hipError_t launch_dense_gemm_bf16(const DenseGemm& g, hipStream_t s);
+hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_dense_gemm_f32(const DenseGemm& g, hipStream_t s);
+hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t s);
+
+hipError_t launch_dense_gemm(const DenseGemm& g, int act_dtype, int /*T_hint*/, void* /*splitk_ws*/,
+                             size_t /*splitk_bytes*/, hipStream_t s) {
+    return act_dtype == LMOE_BF16 ? launch_dense_gemm_bf16(g, s) : launch_dense_gemm_f32(g, s);
+}
+
+hipError_t launch_grouped_gemm(const GroupedGemm& g, int act_dtype, hipStream_t s) {
+    return act_dtype == LMOE_BF16 ? launch_grouped_gemm_bf16(g, s) : launch_grouped_gemm_f32(g, s);
+}
+
+int grouped_bm(const lmoe_dims& d) {
+    if (d.act_dtype == LMOE_F32) return 64;
+    const double avg = (double)d.T * (double)d.k / (double)d.E;
+    return avg >= 96.0 ? 128 : 32;
+}
+
+static int64_t max_tiles(const lmoe_dims& d) {
+    const int64_t n = d.T * d.k;
+    const int bm = grouped_bm(d);
+    return (n + bm - 1) / bm + (d.E < n ? d.E : n);
+}
+
+struct Layout {
+    size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
+        c, hs, total;
+};
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static Layout plan(const lmoe_dims& d) {
+    const size_t es = d.act_dtype == LMOE_BF16 ? 2 : 4;
+    const size_t n = (size_t)d.T * (size_t)d.k;
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    L.z = take((size_t)d.T * d.l * es);
+    L.logits = take((size_t)d.T * d.E * 4);
+    L.idx = take(n * 4);
+    L.gate = take(n * 4);
+    L.counts = take((size_t)d.E * 4);
+    L.offsets = take(((size_t)d.E + 1) * 4);
+    L.perm = take(n * 4);
+    L.inv = take(n * 4);
+    L.hist = take((size_t)permute_nchunks((int64_t)n) * d.E * 4);
+    L.tiles = take((size_t)max_tiles(d) * 16);
+    L.tile_count = take(4);
+    L.tile_start = take((size_t)d.E * 4);
+    L.ntiles = take((size_t)d.E * 4);
+    L.H = take(n * d.f * es);
+    L.Y = take(n * d.l * es);
+    L.c = take((size_t)d.T * d.l * es);
+    L.hs = take((size_t)d.T * d.f_s * es);
+    L.total = o;
+    return L;
+}
+
+static thread_local int g_last_hip_error = 0;
+
+static int hip_status(hipError_t e) {
+    if (e == hipSuccess) return LMOE_OK;
+    g_last_hip_error = (int)e;
+    return LMOE_ERR_HIP;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p) return LMOE_ERR_NULL;
+    for (const void* p : ps)
+        if (!aligned16(p)) return LMOE_ERR_ALIGN;
+    return LMOE_OK;
+}
+
+static int check_optional(const void* p) { return (p && !aligned16(p)) ? LMOE_ERR_ALIGN : LMOE_OK; }
+
+static int check_workspace(const lmoe_dims& d, const void* ws, size_t bytes) {
+    if (!ws || bytes < plan(d).total) return LMOE_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return LMOE_ERR_ALIGN;
+    return LMOE_OK;
+}
+
+static int check_experts(const lmoe_dims& d, const lmoe_experts* x) {
+    if (!x) return LMOE_ERR_NULL;
+    if (d.expert_dtype == LMOE_NVFP4)
+        return check_ptrs({x->W1_codes, x->W1_scales, x->W1_ts, x->W2_codes, x->W2_scales, x->W2_ts});
+    return check_ptrs({x->W1, x->W2});
+}
+
+static int check_shared(const lmoe_dims& d, const lmoe_shared* sh) {
+    if ((sh != nullptr) != (d.f_s > 0)) return LMOE_ERR_SHAPE;
+    if (sh) return check_ptrs({sh->W_s1, sh->W_s2});
+    return LMOE_OK;
+}
+
+#define LMOE_TRY(expr)              \
+    do {                            \
+        const int st_ = (expr);     \
+        if (st_ != LMOE_OK) return st_; \
+    } while (0)
+
+static TileTable tile_table(const lmoe_dims& d, char* ws, const Layout& L) {
+    TileTable tt;
+    tt.tile_count = (const int*)(ws + L.tile_count);
+    tt.tiles = (const int4*)(ws + L.tiles);
+    tt.expert_tile_start = (const int*)(ws + L.tile_start);
+    tt.expert_ntiles = (const int*)(ws + L.ntiles);
+    tt.max_tiles = (int)max_tiles(d);
+    tt.bm = grouped_bm(d);
+    return tt;
+}
+
+// ---- the steps, shared by the fused and the staged entry points --------
+
+static hipError_t run_project_route(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r,
+                                    const float* bias, const lmoe_shared* sh, void* z, float* logits,
+                                    int32_t* idx, float* gate, void* hs, hipStream_t s) {
+    DenseGemm g{};
+    g.M = (int)d.T;
+    g.N = (int)(d.l + d.E + d.f_s);
+    g.nseg = 1;
+    g.A[0] = x;
+    g.lda[0] = d.d;
+    g.K[0] = (int)d.d;
+    g.ngroups = sh ? 3 : 2;
+    g.g[0] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
+    g.g[1] = NGroup{(int)d.l, (int)(d.l + d.E), {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
+    if (sh) g.g[2] = NGroup{(int)(d.l + d.E), g.N, {sh->W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
+    hipError_t e = launch_dense_gemm(g, d.act_dtype, (int)d.T, nullptr, 0, s);
+    if (e != hipSuccess) return e;
+    return launch_topk_softmax(logits, (int)d.T, (int)d.E, (int)d.k, idx, gate, s);
+}
+
+static hipError_t run_experts(const lmoe_dims& d, const void* z, const float* gate, const int32_t* perm,
+                              const lmoe_experts* ex, void* H, void* Y, const TileTable& tt, hipStream_t s) {
+    GroupedGemm g1{};
+    g1.N = (int)d.f;
+    g1.K = (int)d.l;
+    g1.tt = tt;
+    g1.A = z;
+    g1.lda = d.l;
+    g1.a_row_map = perm;
+    g1.a_row_div = (int)d.k;
+    g1.b_fmt = d.expert_dtype;
+    g1.B = ex->W1;
+    g1.B_codes = ex->W1_codes;
+    g1.B_scales = ex->W1_scales;
+    g1.B_ts = ex->W1_ts;
+    g1.epi = EPI_RELU2;
+    g1.C = H;
+    g1.ldc = d.f;
+    hipError_t e = launch_grouped_gemm(g1, d.act_dtype, s);
+    if (e != hipSuccess) return e;
+
+    GroupedGemm g2 = g1;
+    g2.N = (int)d.l;
+    g2.K = (int)d.f;
+    g2.A = H;
+    g2.lda = d.f;
+    g2.a_row_map = nullptr;
+    g2.a_row_div = 1;
+    g2.B = ex->W2;
+    g2.B_codes = ex->W2_codes;
+    g2.B_scales = ex->W2_scales;
+    g2.B_ts = ex->W2_ts;
+    g2.epi = EPI_GATE;
+    g2.gate = gate;
+    g2.gate_map = perm;
+    g2.C = Y;
+    g2.ldc = d.l;
+    return launch_grouped_gemm(g2, d.act_dtype, s);
+}
+
+static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_t* inv, const void* W_up,
+                                 const lmoe_shared* sh, const void* hs, void* c, void* out, hipStream_t s) {
+    hipError_t e = launch_combine(Y, inv, (int)d.T, (int)d.k, (int)d.l, d.act_dtype, c, s);
+    if (e != hipSuccess) return e;
+    DenseGemm g{};
+    g.M = (int)d.T;
+    g.N = (int)d.d;
+    g.nseg = sh ? 2 : 1;
+    g.A[0] = c;
+    g.lda[0] = d.l;
+    g.K[0] = (int)d.l;
+    if (sh) {
+        g.A[1] = hs;
+        g.lda[1] = d.f_s;
+        g.K[1] = (int)d.f_s;
+    }
+    g.ngroups = 1;
+    g.g[0] = NGroup{0, (int)d.d, {W_up, sh ? sh->W_s2 : nullptr}, EPI_STORE, out, d.d, nullptr};
+    return launch_dense_gemm(g, d.act_dtype, (int)d.T, nullptr, 0, s);
+}
+
+}  // namespace lmoe
+
+using namespace lmoe;
+
+extern "C" {
+
+int lmoe_validate_dims(const lmoe_dims* d) {
+    if (!d) return LMOE_ERR_NULL;
+    if (d->T < 1 || d->T > (1 << 24)) return LMOE_ERR_SHAPE;
+    if (d->d < 256 || d->d % 256 != 0 || d->d > 65536) return LMOE_ERR_SHAPE;
+    if (d->l * 4 != d->d) return LMOE_ERR_SHAPE;
+    if (d->E < 1 || d->E > 1024) return LMOE_ERR_SHAPE;
+    if (d->k < 1 || d->k > d->E) return LMOE_ERR_SHAPE;
+    if (d->f < 64 || d->f % 64 != 0 || d->f > 65536) return LMOE_ERR_SHAPE;
+    if (d->f_s < 0 || d->f_s % 64 != 0 || d->f_s > 262144) return LMOE_ERR_SHAPE;
+    if (d->T * d->k > (int64_t)1 << 30) return LMOE_ERR_SHAPE;
+    if (d->act_dtype == LMOE_F32) {
+        if (d->expert_dtype != LMOE_F32) return LMOE_ERR_DTYPE;
+        if (max_tiles(*d) > 65535) return LMOE_ERR_SHAPE;  // grid.y of the fp32 grouped kernel
+    } else if (d->act_dtype == LMOE_BF16) {
+        if (d->expert_dtype != LMOE_BF16 && d->expert_dtype != LMOE_NVFP4) return LMOE_ERR_DTYPE;
+    } else {
+        return LMOE_ERR_DTYPE;
+    }
+    return LMOE_OK;
+}
+
+size_t lmoe_workspace_bytes(const lmoe_dims* d) {
+    if (lmoe_validate_dims(d) != LMOE_OK) return 0;
+    return plan(*d).total;
+}
+
+const char* lmoe_strerror(int st) {
+    switch (st) {
+        case LMOE_OK: return "ok";
+        case LMOE_ERR_NULL: return "a required pointer is NULL";
+        case LMOE_ERR_SHAPE: return "a size is out of range";
+        case LMOE_ERR_DTYPE: return "unsupported dtype or dtype combination";
+        case LMOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case LMOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case LMOE_ERR_HIP: return "a HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int lmoe_last_hip_error(void) { return g_last_hip_error; }
+
+int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,
+                      const float* router_bias, const lmoe_experts* experts, const void* W_up,
+                      const lmoe_shared* shared, int k, void* out, void* workspace, size_t workspace_bytes,
+                      const lmoe_debug* dbg, void* stream) {
+    LMOE_TRY(lmoe_validate_dims(dims));
+    const lmoe_dims& d = *dims;
+    if (k != d.k) return LMOE_ERR_SHAPE;
+    LMOE_TRY(check_ptrs({x, W_down, W_router, W_up, out}));
+    LMOE_TRY(check_optional(router_bias));
+    LMOE_TRY(check_experts(d, experts));
+    LMOE_TRY(check_shared(d, shared));
+    lmoe_debug dv{};
+    if (dbg) dv = *dbg;
+    LMOE_TRY(check_optional(dv.z));
+    LMOE_TRY(check_optional(dv.logits));
+    LMOE_TRY(check_optional(dv.topk_idx));
+    LMOE_TRY(check_optional(dv.topk_gate));
+    LMOE_TRY(check_optional(dv.counts));
+    LMOE_TRY(check_optional(dv.offsets));
+    LMOE_TRY(check_optional(dv.perm));
+    LMOE_TRY(check_optional(dv.inv));
+    LMOE_TRY(check_optional(dv.c));
+    // the workspace is checked last in every entry point
+    LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
+
+    char* ws = (char*)workspace;
+    const Layout L = plan(d);
+    hipStream_t s = (hipStream_t)stream;
+    void* z = dv.z ? dv.z : ws + L.z;
+    float* logits = dv.logits ? dv.logits : (float*)(ws + L.logits);
+    int32_t* idx = dv.topk_idx ? dv.topk_idx : (int32_t*)(ws + L.idx);
+    float* gate = dv.topk_gate ? dv.topk_gate : (float*)(ws + L.gate);
+    int32_t* counts = dv.counts ? dv.counts : (int32_t*)(ws + L.counts);
+    int32_t* offsets = dv.offsets ? dv.offsets : (int32_t*)(ws + L.offsets);
+    int32_t* perm = dv.perm ? dv.perm : (int32_t*)(ws + L.perm);
+    int32_t* inv = dv.inv ? dv.inv : (int32_t*)(ws + L.inv);
+    void* c = dv.c ? dv.c : ws + L.c;
+    void* hs = ws + L.hs;
+    const TileTable tt = tile_table(d, ws, L);
+
+    hipError_t e = run_project_route(d, x, W_down, W_router, router_bias, shared, z, logits, idx, gate, hs, s);
+    if (e == hipSuccess)
+        e = launch_permute(idx, d.T * d.k, (int)d.E, (int32_t*)(ws + L.hist), counts, offsets, perm, inv, &tt, s);
+    if (e == hipSuccess) e = run_experts(d, z, gate, perm, experts, ws + L.H, ws + L.Y, tt, s);
+    if (e == hipSuccess) e = run_combine_up(d, ws + L.Y, inv, W_up, shared, hs, c, out, s);
+    return hip_status(e);
+}
+
+int lmoe_project_route(const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,
+                       const float* router_bias, const lmoe_shared* shared, void* z, float* logits,
+                       int32_t* topk_idx, float* topk_gate, void* hs, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    LMOE_TRY(lmoe_validate_dims(dims));
+    const lmoe_dims& d = *dims;
+    LMOE_TRY(check_ptrs({x, W_down, W_router, z, logits, topk_idx, topk_gate}));
+    LMOE_TRY(check_optional(router_bias));
+    LMOE_TRY(check_shared(d, shared));
+    if (shared) LMOE_TRY(check_ptrs({hs}));
+    LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
+    return hip_status(run_project_route(d, x, W_down, W_router, router_bias, shared, z, logits, topk_idx,
+                                        topk_gate, hs, (hipStream_t)stream));
+}
+
+int lmoe_permute(const lmoe_dims* dims, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* inv, void* workspace, size_t workspace_bytes, void* stream) {
+    LMOE_TRY(lmoe_validate_dims(dims));
+    const lmoe_dims& d = *dims;
+    LMOE_TRY(check_ptrs({topk_idx, counts, offsets, perm, inv}));
+    LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
+    char* ws = (char*)workspace;
+    const Layout L = plan(d);
+    return hip_status(launch_permute(topk_idx, d.T * d.k, (int)d.E, (int32_t*)(ws + L.hist), counts, offsets,
+                                     perm, inv, nullptr, (hipStream_t)stream));
+}
+
+int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const float* topk_gate, const int32_t* offsets,
+                     const int32_t* perm, const lmoe_experts* experts, void* Y, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    LMOE_TRY(lmoe_validate_dims(dims));
+    const lmoe_dims& d = *dims;
+    LMOE_TRY(check_ptrs({z, topk_gate, offsets, perm, Y}));
+    LMOE_TRY(check_experts(d, experts));
+    LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
+    char* ws = (char*)workspace;
+    const Layout L = plan(d);
+    const TileTable tt = tile_table(d, ws, L);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_build_tiles(offsets, (int)d.E, tt, s);
+    if (e == hipSuccess) e = run_experts(d, z, topk_gate, perm, experts, ws + L.H, Y, tt, s);
+    return hip_status(e);
+}
+
+int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv, const void* W_up,
+                    const lmoe_shared* shared, const void* hs, void* c, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    LMOE_TRY(lmoe_validate_dims(dims));
+    const lmoe_dims& d = *dims;
+    LMOE_TRY(check_ptrs({Y, inv, W_up, out}));
+    LMOE_TRY(check_shared(d, shared));
+    if (shared) LMOE_TRY(check_ptrs({hs}));
+    LMOE_TRY(check_optional(c));
+    LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
+    char* ws = (char*)workspace;
+    const Layout L = plan(d);
+    return hip_status(run_combine_up(d, Y, inv, W_up, shared, hs, c ? c : ws + L.c, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "latentmoe.h"
+
+namespace lmoe {
+
+// Epilogue of a GEMM output group.
+enum Epi : int {
+    EPI_STORE = 0,     // C = acc, stored in the activation dtype
+    EPI_F32_BIAS = 1,  // C = acc (+ bias[col]), stored fp32
+    EPI_RELU2 = 2,     // C = max(0, acc * scale)^2, activation dtype
+    EPI_GATE = 3,      // C = acc * scale * gate[gate_map[row]], activation dtype
+};
+
+// One contiguous range of output columns [n_begin, n_end) of a dense GEMM,
+// with its own B rows (one pointer per K segment, rows of K[s] elements) and
+// its own output tensor (column n - n_begin, leading dimension ldc).
+struct NGroup {
+    int n_begin, n_end;
+    const void* B[2];
+    int epi;
+    void* C;
+    int64_t ldc;
+    const float* bias;
+};
+
+// C[M][N] = sum over K segments s of A_s[M][K_s] * B_s[N][K_s]^T.
+// Segment 1 (if nseg == 2) continues the same accumulation: this fuses
+// "c W_up^T + hs W_s2^T" into one GEMM.  All K_s are multiples of 64.
+struct DenseGemm {
+    int M, N;
+    int nseg;
+    const void* A[2];
+    int64_t lda[2];
+    int K[2];
+    int ngroups;
+    NGroup g[3];
+};
+
+// Device tile table of a grouped GEMM: M-tiles of BM sorted rows per expert.
+// tiles[i] = {expert, first sorted row, rows, 0}; expert_tile_start/ntiles
+// give each expert's tile range.  Built on the device from the offsets.
+struct TileTable {
+    const int* tile_count;
+    const int4* tiles;
+    const int* expert_tile_start;
+    const int* expert_ntiles;
+    int max_tiles;
+    int bm;
+};
+
+// Per-expert GEMM over sorted rows: for every tile (expert e, rows p),
+// C[p][n] = epi( sum_k A[arow(p)][k] * W_e[n][k] ), with
+// arow(p) = a_row_map ? a_row_map[p] / a_row_div : p.
+struct GroupedGemm {
+    int N, K;
+    TileTable tt;
+    const void* A;
+    int64_t lda;
+    const int* a_row_map;
+    int a_row_div;
+    int b_fmt;  // LMOE_F32 / LMOE_BF16 dense stack [E][N][K], or LMOE_NVFP4
+    const void* B;
+    const uint8_t* B_codes;   // [E][N][K/2]
+    const uint8_t* B_scales;  // [E][N][K/16]
+    const float* B_ts;        // [E]
+    int epi;                  // EPI_RELU2 or EPI_GATE
+    const float* gate;
+    const int* gate_map;
+    void* C;
+    int64_t ldc;
+};
+
+// ---- optional per-launch event timing (timing.hip) -----------------------
+
+void timer_mark_begin(const char* name, hipStream_t s);
+void timer_mark_end(hipStream_t s);
+
+// Enqueues one kernel launch, bracketed by timing events when recording is on.
+#define LMOE_LAUNCH(name, stream, ...)            \
+    do {                                          \
+        ::lmoe::timer_mark_begin(name, stream);   \
+        __VA_ARGS__;                              \
+        ::lmoe::timer_mark_end(stream);           \
+    } while (0)
+
+// ---- launchers (return hipSuccess or the launch error) ------------------
+
+hipError_t launch_dense_gemm(const DenseGemm& g, int act_dtype, int T_hint, void* splitk_ws,
+                             size_t splitk_bytes, hipStream_t s);
+hipError_t launch_grouped_gemm(const GroupedGemm& g, int act_dtype, hipStream_t s);
+
+// Grouped-GEMM M-tile height for these sizes (the tile table is built for it).
+int grouped_bm(const lmoe_dims& d);
+
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx,
+                               float* gate, hipStream_t s);
+
+// Permutation: hist scratch is [nchunks][E] ints.  If tiles is non-null the
+// scan also writes the grouped-GEMM tile table for tile height bm.
+int permute_nchunks(int64_t n_pairs);
+hipError_t launch_permute(const int32_t* idx, int64_t n_pairs, int E, int32_t* hist,
+                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          const TileTable* tiles, hipStream_t s);
+// Tile table from offsets alone (staged entry point).
+hipError_t launch_build_tiles(const int32_t* offsets, int E, const TileTable& tt, hipStream_t s);
+
+hipError_t launch_combine(const void* Y, const int32_t* inv, int T, int k, int l, int act_dtype,
+                          void* c, hipStream_t s);
+
+}  // namespace lmoe

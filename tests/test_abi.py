@@ -1,0 +1,144 @@
+"""The C ABI, checked on the host without a GPU.
+
+The library must load, export every function include/latentmoe.h declares,
+and reject bad arguments before anything is enqueued.  Every call here fails
+validation (the workspace check comes last and is always given too few
+bytes), so no kernel is ever launched with the placeholder pointers.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_moe_layer_06_amd import binding as B
+from sparse_moe_layer_06_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "latentmoe.h")
+
+FAKE = 0x100000  # aligned placeholder, never dereferenced
+MIS = FAKE + 8   # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    fns = declared_functions()
+    assert sorted(B.EXPORTED) == fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def dims(**kw):
+    cfg = synth.CONFIGS["mid_bf16"].with_(**kw) if kw else synth.CONFIGS["mid_bf16"]
+    return B.dims_of(cfg)
+
+
+def test_validate_accepts_every_workload():
+    for cfg in synth.CONFIGS.values():
+        assert B.validate_dims(B.dims_of(cfg)) == B.LMOE_OK, cfg.name
+        assert B.workspace_bytes(cfg) > 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("l", 1000, B.LMOE_ERR_SHAPE),      # l != d/4
+    ("d", 4000, B.LMOE_ERR_SHAPE),      # d not a multiple of 256
+    ("T", 0, B.LMOE_ERR_SHAPE),
+    ("E", 1025, B.LMOE_ERR_SHAPE),
+    ("E", 0, B.LMOE_ERR_SHAPE),
+    ("k", 0, B.LMOE_ERR_SHAPE),
+    ("k", 129, B.LMOE_ERR_SHAPE),       # k > E
+    ("f", 100, B.LMOE_ERR_SHAPE),
+    ("f_s", 32, B.LMOE_ERR_SHAPE),
+    ("act_dtype", 7, B.LMOE_ERR_DTYPE),
+    ("expert_dtype", B.LMOE_F32, B.LMOE_ERR_DTYPE),  # fp32 experts with bf16 activations
+])
+def test_validate_rejects(field, value, code):
+    d = dims()
+    setattr(d, field, value)
+    assert B.validate_dims(d) == code
+    assert B.lib().lmoe_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_workspace_grows_with_tokens():
+    cfg = synth.CONFIGS["mid_bf16"]
+    assert B.workspace_bytes(cfg, 1) < B.workspace_bytes(cfg, 64) < B.workspace_bytes(cfg, 2048)
+
+
+def _forward(d, *, x=FAKE, W_down=FAKE, W_r=FAKE, bias=None, experts=None, W_up=FAKE, shared="auto",
+             k=None, out=FAKE, ws=FAKE, ws_bytes=None, dbg=None):
+    L = B.lib()
+    ex = experts if experts is not None else B.Experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    if shared == "auto":
+        shared = B.Shared(FAKE, FAKE) if d.f_s > 0 else None
+    need = L.lmoe_workspace_bytes(ctypes.byref(d))
+    ws_bytes = need - 1 if ws_bytes is None else ws_bytes
+    assert ws_bytes < max(need, 1)  # guard: validation can never pass
+    return L.latentmoe_forward(ctypes.byref(d), x, W_down, W_r, bias, ctypes.byref(ex), W_up,
+                               ctypes.byref(shared) if shared is not None else None,
+                               d.k if k is None else k, out, ws, ws_bytes,
+                               ctypes.byref(dbg) if dbg is not None else None, None)
+
+
+def test_forward_error_paths():
+    d = dims()
+    assert _forward(d) == B.LMOE_ERR_WORKSPACE
+    assert _forward(d, ws=None, ws_bytes=0) == B.LMOE_ERR_WORKSPACE
+    assert _forward(d, x=None) == B.LMOE_ERR_NULL
+    assert _forward(d, out=None) == B.LMOE_ERR_NULL
+    assert _forward(d, W_up=MIS) == B.LMOE_ERR_ALIGN
+    assert _forward(d, bias=MIS) == B.LMOE_ERR_ALIGN
+    assert _forward(d, k=d.k + 1) == B.LMOE_ERR_SHAPE
+    assert _forward(d, shared=None) == B.LMOE_ERR_SHAPE  # f_s > 0 but no shared weights
+    assert _forward(d, experts=B.Experts(FAKE, None, None, None, None, None, None, None)) == B.LMOE_ERR_NULL
+    dbg = B.Debug(z=MIS)
+    assert _forward(d, dbg=dbg) == B.LMOE_ERR_ALIGN
+    bad = dims()
+    bad.l = 1
+    assert _forward(bad) == B.LMOE_ERR_SHAPE
+
+
+def test_forward_nvfp4_requires_codes():
+    d = B.dims_of(synth.CONFIGS["prefill_nvfp4"])
+    ex = B.Experts(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert _forward(d, experts=ex) == B.LMOE_ERR_NULL
+
+
+def test_staged_error_paths():
+    L = B.lib()
+    d = dims()
+    need = L.lmoe_workspace_bytes(ctypes.byref(d))
+    sh = B.Shared(FAKE, FAKE)
+    assert L.lmoe_project_route(ctypes.byref(d), FAKE, FAKE, FAKE, None, ctypes.byref(sh), FAKE, FAKE, FAKE,
+                                FAKE, None, FAKE, need - 1, None) == B.LMOE_ERR_NULL  # hs missing
+    assert L.lmoe_project_route(ctypes.byref(d), FAKE, FAKE, FAKE, None, ctypes.byref(sh), FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, need - 1, None) == B.LMOE_ERR_WORKSPACE
+    assert L.lmoe_permute(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == B.LMOE_ERR_NULL
+    assert L.lmoe_permute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == B.LMOE_ERR_WORKSPACE
+    ex = B.Experts(FAKE, FAKE, None, None, None, None, None, None)
+    assert L.lmoe_experts_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.byref(ex), MIS, FAKE, need - 1,
+                              None) == B.LMOE_ERR_ALIGN
+    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, need - 1,
+                             None) == B.LMOE_ERR_SHAPE  # f_s > 0 without shared weights
+    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(sh), FAKE, None, FAKE, FAKE,
+                             need - 1, None) == B.LMOE_ERR_WORKSPACE
+
+
+def test_strerror_and_last_error():
+    L = B.lib()
+    for code in range(-6, 1):
+        assert L.lmoe_strerror(code)
+    assert L.lmoe_last_hip_error() == 0

@@ -1,0 +1,176 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs a gfx950 GPU).
+
+Small shapes run whole; the full-size workloads check the routing and the
+permutation for every token and the outputs on sampled tokens.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+from oracle import latentmoe_oracle as O
+from sparse_moe_layer_06_amd import binding as B
+from sparse_moe_layer_06_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+CFG = synth.CONFIGS
+TINY = CFG["tiny_f32"]
+# Small layers that still span several MFMA tiles with ragged edges.
+SMALL = {
+    "bf16_ragged": TINY.with_(name="bf16_ragged", T=193, d=256, l=64, E=12, k=3, f=192, f_s=192,
+                              act="bf16", experts="bf16"),
+    # >= 96 rows per expert on average: the 128-row expert tiles
+    "bf16_deep": TINY.with_(name="bf16_deep", T=500, d=512, l=128, E=8, k=2, f=256, f_s=320,
+                            act="bf16", experts="bf16"),
+    "nvfp4_deep": TINY.with_(name="nvfp4_deep", T=300, d=512, l=128, E=4, k=2, f=256, f_s=0,
+                             act="bf16", experts="nvfp4"),
+    "nvfp4_sparse": TINY.with_(name="nvfp4_sparse", T=70, d=256, l=64, E=16, k=3, f=128, f_s=0,
+                               act="bf16", experts="nvfp4"),
+    "zipf_small": TINY.with_(name="zipf_small", T=64, d=512, l=128, E=64, k=6, f=256, f_s=0,
+                             act="bf16", experts="bf16", zipf_bias=True),
+    "f32_ragged": TINY.with_(name="f32_ragged", T=77, d=256, l=64, E=9, k=3, f=192, f_s=128),
+    "T1_bf16": TINY.with_(name="T1_bf16", T=1, d=256, l=64, E=16, k=4, f=128, f_s=64, act="bf16",
+                          experts="bf16"),
+    "k1_bf16": TINY.with_(name="k1_bf16", T=128, d=256, l=64, E=8, k=1, f=128, act="bf16", experts="bf16"),
+    "kE_bf16": TINY.with_(name="kE_bf16", T=64, d=256, l=64, E=5, k=5, f=64, act="bf16", experts="bf16"),
+    "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
+    "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def small_inputs(cfg, seed=0):
+    inp = synth.make_inputs(cfg, seed, "cpu")
+    return {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.empty_cache()
+
+
+def test_tiny_f32_matches_oracle_everywhere():
+    log("case tiny_f32 T=64 d=256 E=16 k=4")
+    errs, _, _ = P.run_and_check(TINY, small_inputs(TINY), report=log)
+    assert errs["tokens_checked"] == TINY.T - errs["tie_substitutions"]
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layers_match_oracle(name):
+    cfg = SMALL[name]
+    log(f"case {name} {cfg}")
+    P.run_and_check(cfg, small_inputs(cfg), report=log)
+
+
+def test_all_tokens_to_one_expert():
+    cfg = SMALL["bf16_ragged"]
+    inp = small_inputs(cfg)
+    bias = torch.full((cfg.E,), -30.0, dtype=torch.float32)
+    bias[[3, 7, 1]] = torch.tensor([30.0, 20.0, 10.0])  # every token: experts 3, 7, 1 in that order
+    inp["b_r"] = bias.cuda()
+    log("case one-expert-takes-all")
+    errs, _, dbg = P.run_and_check(cfg, inp, report=log)
+    counts = dbg["counts"].cpu().numpy()
+    assert counts[3] == counts[7] == counts[1] == cfg.T and counts.sum() == cfg.T * cfg.k
+
+
+def test_exact_logit_ties_break_to_lower_id():
+    # x = 0 makes every logit equal to its bias; equal biases must pick the lower ids.
+    cfg = SMALL["bf16_ragged"].with_(f_s=0)
+    inp = small_inputs(cfg)
+    inp["x"].zero_()
+    inp["b_r"] = torch.tensor([0.5, 1.0, 1.0, 0.0, 1.0, 0.5, 2.0, 1.0, 0, 0, 0, 0], dtype=torch.float32).cuda()
+    dbg = P.debug_buffers(cfg, cfg.T)
+    B.forward(cfg, inp, debug=dbg)
+    torch.cuda.synchronize()
+    idx = dbg["topk_idx"].cpu().numpy()
+    assert np.all(idx == np.array([6, 1, 2])), idx[:2]
+
+
+def test_staged_entry_points_compose_to_forward():
+    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged"):
+        cfg = SMALL[name]
+        log(f"case staged {name}")
+        inp = small_inputs(cfg)
+        ws = B.alloc_workspace(cfg)
+        fused = B.forward(cfg, inp, workspace=ws)
+        r = B.project_route(cfg, inp, ws)
+        p = B.permute(cfg, r["idx"], ws)
+        Y = B.experts_ffn(cfg, inp, r["z"], r["gate"], p["offsets"], p["perm"], ws)
+        o = B.combine_up(cfg, inp, Y, p["inv"], r["hs"], ws, cfg.T)
+        torch.cuda.synchronize()
+        assert torch.equal(o["out"], fused), name
+
+
+def test_repeated_runs_are_bit_identical():
+    cfg = SMALL["bf16_deep"]
+    inp = small_inputs(cfg)
+    ws = B.alloc_workspace(cfg)
+    a = B.forward(cfg, inp, workspace=ws).clone()
+    for _ in range(5):
+        b = B.forward(cfg, inp, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_invalid_expert_ids_are_left_out_of_the_permutation():
+    cfg = SMALL["bf16_ragged"]
+    ws = B.alloc_workspace(cfg)
+    idx = torch.randint(0, cfg.E, (cfg.T, cfg.k), dtype=torch.int32, generator=torch.Generator().manual_seed(3))
+    idx[5, 1] = cfg.E + 3
+    idx[9, 0] = -1
+    p = B.permute(cfg, idx.cuda(), ws)
+    torch.cuda.synchronize()
+    inv = p["inv"].cpu().numpy()
+    assert inv[5 * cfg.k + 1] == -1 and inv[9 * cfg.k] == -1
+    valid = idx.numpy().reshape(-1)
+    valid = valid[(valid >= 0) & (valid < cfg.E)]
+    assert np.array_equal(p["counts"].cpu().numpy(), np.bincount(valid, minlength=cfg.E))
+
+
+# ---- full-size workloads --------------------------------------------------
+
+@pytest.mark.timeout(900)
+def test_mid_bf16_full_size():
+    cfg = CFG["mid_bf16"]
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=96, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_bf16_full_size():
+    cfg = CFG["prefill_bf16"]
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=24, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_decode_zipf_full_size():
+    cfg = CFG["decode_bf16_zipf"]
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    errs, _, dbg = P.run_and_check(cfg, inp, lazy_experts=True, report=log)
+    counts = dbg["counts"].cpu().numpy()
+    log(f"experts touched {int((counts > 0).sum())}, expert 0 rows {counts[0]}")
+    assert counts[0] == cfg.T  # the largest bias: every token picks expert 0
+
+
+@pytest.mark.timeout(900)
+def test_prefill_nvfp4_full_size():
+    cfg = CFG["prefill_nvfp4"]
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=16, lazy_experts=True, report=log)
