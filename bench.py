@@ -155,7 +155,7 @@ def cpu_baseline(cfg, inp, n_tokens, synth):
     for e in np.unique(idx):
         h["W1"][e], h["W2"][e]
     t0 = time.perf_counter()
-    O.forward(h, cfg.k, tokens=tokens, experts=O.ExpertWeights(h, cache_size=cfg.E))
+    O.forward(h, cfg.k, tokens=tokens, experts=O.ExpertWeights(h))
     dt = time.perf_counter() - t0
     return dict(value=n_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{n_tokens} evenly spaced tokens of {cfg.name} (routing, experts, up-projection "
@@ -169,7 +169,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--decode-steps", type=int, default=100)
-    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()

@@ -1,11 +1,12 @@
 """Comparison protocol between the HIP path and the CPU oracle.
 
 * logits: max-norm relative error <= 1e-5 (both fp32; different summation).
-* top-k: the GPU's ordered selection must equal the oracle's for every token
-  whose oracle gap between the k-th and (k+1)-th logit exceeds 1e-3.  Where
-  the gap is smaller several selections are correct: the GPU's must then be a
-  valid top-k of the oracle logits within 1e-3.
-* permutation: bit-exact against the oracle when every selection matched;
+* top-k: the GPU's ordered selection must equal the oracle's except at near
+  ties (logits within 1e-3), where several answers are correct: a different
+  set only where the oracle gap between the k-th and (k+1)-th logit is
+  <= 1e-3 and the GPU set is then a valid top-k within 1e-3; a different
+  order only between picks whose oracle logits are within 1e-3.
+* permutation: bit-exact against the oracle when every ordered selection matched;
   otherwise checked as the unique stable counting sort of the GPU's own
   selection (counts, offsets, order within segments, inverse).
 * gates, z, c, out: compared on the tokens whose selection matched, with
@@ -72,23 +73,33 @@ def debug_buffers(cfg, T, device="cuda"):
     )
 
 
-def check_topk(gpu_idx: np.ndarray, s: np.ndarray, ref_idx: np.ndarray, k: int) -> np.ndarray:
-    """Returns the mask of tokens whose selection equals the oracle's."""
+def check_topk(gpu_idx: np.ndarray, s: np.ndarray, ref_idx: np.ndarray, k: int):
+    """Returns (ordered_same, set_same) masks over tokens.
+
+    A token whose GPU selection differs from the oracle's must sit at a near
+    tie: if the sets differ, the oracle gap at rank k is <= 1e-3 and the GPU
+    set is a valid top-k within 1e-3; if only the order differs, every pair
+    of consecutive GPU picks is descending in the oracle logits within 1e-3.
+    """
     T, E = s.shape
-    same = np.all(gpu_idx == ref_idx, axis=1)
+    ordered_same = np.all(gpu_idx == ref_idx, axis=1)
+    set_same = np.all(np.sort(gpu_idx, axis=1) == np.sort(ref_idx, axis=1), axis=1)
     if k < E:
         sv = -np.sort(-s.astype(np.float64), axis=1)
         gap = sv[:, k - 1] - sv[:, k]
     else:
         gap = np.full(T, np.inf)
-    for t in np.nonzero(~same)[0]:
-        assert gap[t] <= GAP_TOL, f"token {t}: selection differs at gap {gap[t]}"
+    for t in np.nonzero(~ordered_same)[0]:
         sel = gpu_idx[t]
         assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < E, f"token {t}: bad ids"
-        mask = np.zeros(E, bool)
-        mask[sel] = True
-        assert s[t, mask].min() >= s[t, ~mask].max() - GAP_TOL, f"token {t}: not a valid top-k"
-    return same
+        v = s[t, sel].astype(np.float64)
+        assert np.all(v[:-1] >= v[1:] - GAP_TOL), f"token {t}: order not descending within tolerance"
+        if not set_same[t]:
+            assert gap[t] <= GAP_TOL, f"token {t}: selection differs at gap {gap[t]}"
+            mask = np.zeros(E, bool)
+            mask[sel] = True
+            assert s[t, mask].min() >= s[t, ~mask].max() - GAP_TOL, f"token {t}: not a valid top-k"
+    return ordered_same, set_same
 
 
 def check_permutation(cfg, gpu: dict, gpu_idx: np.ndarray, ref_idx: np.ndarray, all_same: bool):
@@ -133,14 +144,18 @@ def run_and_check(cfg, inp, n_sample: int = 1 << 30, lazy_experts: bool = False,
     assert errs["logits"] <= LOGIT_TOL, errs
 
     gpu_idx = dbg["topk_idx"].cpu().numpy()
-    same = check_topk(gpu_idx, s, ref_idx, cfg.k)
+    ordered_same, same = check_topk(gpu_idx, s, ref_idx, cfg.k)
+    errs["tie_reorders"] = int((~ordered_same & same).sum())
     errs["tie_substitutions"] = int((~same).sum())
-    check_permutation(cfg, dbg, gpu_idx, ref_idx, bool(same.all()))
+    check_permutation(cfg, dbg, gpu_idx, ref_idx, bool(ordered_same.all()))
 
     gpu_gate = dbg["topk_gate"].cpu().numpy()
     errs["gate_sum"] = float(np.max(np.abs(gpu_gate.sum(1) - 1.0)))
     assert errs["gate_sum"] <= 1e-6
-    errs["gate"] = float(np.max(np.abs(gpu_gate[same] - ref_gate[same]))) if same.any() else 0.0
+    # gates compared per expert id (a near-tie reorder permutes them)
+    og = np.take_along_axis(gpu_gate, np.argsort(gpu_idx, axis=1), 1)
+    orf = np.take_along_axis(ref_gate, np.argsort(ref_idx, axis=1), 1)
+    errs["gate"] = float(np.max(np.abs(og[same] - orf[same]))) if same.any() else 0.0
     assert errs["gate"] <= 1e-5, errs
 
     tokens = sample_tokens(T, n_sample)
