@@ -34,7 +34,7 @@ hipError_t launch_grouped_gemm(const GroupedGemm& g, int act_dtype, hipStream_t 
 int grouped_bm(const lmoe_dims& d) {
     if (d.act_dtype == LMOE_F32) return 64;
     const double avg = (double)d.T * (double)d.k / (double)d.E;
-    return avg >= 96.0 ? 128 : 32;
+    return avg >= 96.0 ? 192 : 32;
 }
 
 static int64_t max_tiles(const lmoe_dims& d) {

@@ -9,12 +9,19 @@
 //   dense   [c | hs] [W_up | W_s2]^T -> out (two K segments, one accumulator)
 //   grouped per-expert z[perm] W1_e^T -> H = relu(.)^2 ; H W2_e^T -> Y * gate
 //
-// Block tile BM x BN x 64, 4 waves in a WAVES_M x WAVES_N grid, each wave a
-// (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA tiles.  Global -> register
-// staging of tile k+1 overlaps the MFMAs of tile k; two LDS buffers, one
-// barrier per K step.  LDS rows are 64 bf16 = 8 16-byte chunks, stored with
-// chunk' = chunk ^ (row & 7) so the fragment reads of 32 rows at one chunk
-// spread over the banks.
+// Block tile BM x BN x BK over WAVES_M x WAVES_N waves; each wave owns a
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 32x32 MFMA tiles.  Operand tiles
+// go through a ring of STAGES LDS stages, so STAGES - 1 K tiles are in
+// flight while one is multiplied; they reach LDS one of two ways:
+//   DMA   global_load_lds_dwordx4: each wave instruction moves 64 16-byte
+//         chunks from global memory straight into 1 KB of LDS, no registers,
+//         no LDS write instructions; per K step one vmcnt wait for the oldest
+//         tile and one barrier.
+//   REG   16-byte global loads into registers, then LDS writes (needed when
+//         the tile is transformed on the way, as for the NVFP4 weights).
+// Tile rows are stored as 16-byte chunks XOR-swizzled by row (swz_bits), so
+// the fragment reads (32 consecutive rows at one logical chunk) hit distinct
+// bank groups both per 8 and per 16 lanes.
 //
 // Block -> tile mapping is XCD-aware: consecutive block ids go round-robin to
 // the 8 XCDs, so block b is the (b/8)-th block of XCD b%8; each XCD is given
@@ -25,21 +32,94 @@
 
 namespace lmoe {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool DMA_, int BK_ = 64, int STAGES_ = 2, int MINB_ = 1>
 struct MfmaCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+    static constexpr int MINB = MINB_;  // blocks per CU the register budget is sized for
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int NT = 64 * NW;
+    static constexpr bool DMA = DMA_;
+    static constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int TM = WM / 32, TN = WN / 32;
-    static constexpr int RPP = NT / 8;  // rows covered by one pass of 16-byte chunk loads
-    static constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
-    static constexpr int LDS_CHUNKS = 2 * (BM + BN) * 8;
+    static constexpr int RPP = NT / CPR;  // rows per pass of one chunk per thread
+    static constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
+    static_assert(BK == 32 || BK == 64, "K step is 32 or 64");
+    static_assert(STAGES >= 2, "at least double buffering");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of NT/8");
 };
 
-__device__ __forceinline__ int swz(int row, int ch) { return (row << 3) | (ch ^ (row & 7)); }
+// Physical chunk of logical chunk c in tile row r.  The fragment reads touch
+// 32 consecutive rows at one logical chunk; the XOR keeps every 8 and every
+// 16 consecutive lanes on distinct 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz_bits(int r) {
+    if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+    return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
+
+template <class C>
+__device__ __forceinline__ int lds_idx(int row, int c) { return row * C::CPR + (c ^ swz_bits<C::CPR>(row)); }
+
+// Load slots: each thread moves one 16-byte chunk per slot and K step.
+//   DMA: wave w owns LDS chunks [w*CPW, (w+1)*CPW) of the tile; slot j is one
+//        instruction covering chunks w*CPW + 64 j + lane (lanes past CPW are
+//        inactive).  Chunk q is physical chunk q % CPR of row q / CPR.
+//   REG: slot j of thread t covers row t/CPR + j*RPP, logical chunk t % CPR.
+template <class C, int ROWS>
+struct Slots {
+    static constexpr int CPW = C::DMA ? ROWS * C::CPR / C::NW : 0;  // chunks per wave
+    static constexpr int N = C::DMA ? (CPW + 63) / 64 : ROWS / C::RPP;
+    static_assert(!C::DMA || (ROWS * C::CPR) % C::NW == 0, "DMA chunks must split evenly over the waves");
+    static_assert(C::DMA || ROWS % C::RPP == 0, "register slots must tile the rows");
+    __device__ static __forceinline__ int chunk(int j, int tid) { return (tid >> 6) * CPW + j * 64 + (tid & 63); }
+    __device__ static __forceinline__ bool active(int j, int tid) { return !C::DMA || j * 64 + (tid & 63) < CPW; }
+    __device__ static __forceinline__ int row(int j, int tid) {
+        if constexpr (C::DMA) return min(chunk(j, tid), ROWS * C::CPR - 1) / C::CPR;
+        return tid / C::CPR + j * C::RPP;
+    }
+    __device__ static __forceinline__ int lchunk(int j, int tid) {
+        if constexpr (C::DMA) return (chunk(j, tid) % C::CPR) ^ swz_bits<C::CPR>(row(j, tid));
+        return tid % C::CPR;
+    }
+    // LDS destination of DMA slot j for wave `wave` (wave-uniform)
+    __device__ static __forceinline__ u32x4_t* dst(u32x4_t* base, int wave, int j) { return base + wave * CPW + j * 64; }
+};
+
+// One LDS-DMA instruction: 16 bytes per lane from `src` into LDS starting at
+// the wave-uniform `dst` (lane i lands at dst + 16 i).
+__device__ __forceinline__ void dma16(const void* src, u32x4_t* dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt(N) only (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Waits until at most `ahead` K tiles of this wave's DMA are still in flight
+// (`per_tile` instructions each), then the workgroup barrier.  The empty asm
+// statements keep the compiler from moving memory accesses across.
+template <int MAXAHEAD, int PER_TILE>
+__device__ __forceinline__ void wait_tiles_barrier(int ahead) {
+    asm volatile("" ::: "memory");
+    if constexpr (MAXAHEAD >= 3) {
+        if (ahead >= 3) wait_vmcnt<3 * PER_TILE>();
+    }
+    if constexpr (MAXAHEAD >= 2) {
+        if (ahead == 2) wait_vmcnt<2 * PER_TILE>();
+    }
+    if constexpr (MAXAHEAD >= 1) {
+        if (ahead == 1) wait_vmcnt<PER_TILE>();
+    }
+    if (ahead <= 0) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Output (m, n) of register r of the 32x32 tile for this lane, when the MFMA
 // is issued as mfma(B-fragment, A-fragment): m = lane % 32,
@@ -52,9 +132,11 @@ __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u
         const int ch = ks * 2 + (lane >> 5);
         bf16x8_t af[C::TM], bfr[C::TN];
 #pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm) af[tm] = as_bf16x8(As[swz(wm * C::WM + tm * 32 + (lane & 31), ch)]);
+        for (int tm = 0; tm < C::TM; ++tm)
+            af[tm] = as_bf16x8(As[lds_idx<C>(wm * C::WM + tm * 32 + (lane & 31), ch)]);
 #pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn) bfr[tn] = as_bf16x8(Bs[swz(wn * C::WN + tn * 32 + (lane & 31), ch)]);
+        for (int tn = 0; tn < C::TN; ++tn)
+            bfr[tn] = as_bf16x8(Bs[lds_idx<C>(wn * C::WN + tn * 32 + (lane & 31), ch)]);
 #pragma unroll
         for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
@@ -62,25 +144,37 @@ __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u
     }
 }
 
-// Software pipeline over nk K-tiles.  gload(kt) fetches tile kt into the
-// caller's staging registers, lstore(As, Bs) writes them to one LDS buffer.
-template <class C, class GLoad, class LStore>
-__device__ __forceinline__ void mainloop(int nk, GLoad&& gload, LStore&& lstore, u32x4_t* smem,
-                                         f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
-    constexpr int BUF = (C::BM + C::BN) * 8;
-    gload(0);
-    lstore(smem, smem + C::BM * 8);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) gload(kt + 1);
-        u32x4_t* cur = smem + (kt & 1) * BUF;
-        mma_tile<C>(cur, cur + C::BM * 8, acc, wm, wn, lane);
-        if (more) {
-            u32x4_t* nxt = smem + ((kt + 1) & 1) * BUF;
-            lstore(nxt, nxt + C::BM * 8);
+// K loop over nk tiles through a ring of C::STAGES LDS stages.
+//   fill(kt, As, Bs)  starts moving tile kt into a stage (DMA issue, and/or
+//                     global loads into registers);
+//   land(As, Bs)      finishes the move (writes staged registers to LDS).
+// Tile kt + STAGES - 1 is issued while tile kt is multiplied, so up to
+// STAGES - 1 tiles are in flight.  PER_TILE is the number of DMA
+// instructions per tile and wave; 0 means "wait for everything" (register
+// staged operands already wait in land).
+template <class C, int PER_TILE, class Fill, class Land>
+__device__ __forceinline__ void kloop(int nk, Fill&& fill, Land&& land, u32x4_t* ring,
+                                      f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
+    constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS, AOFF = C::BM * C::CPR;
+    constexpr int MAXAHEAD = PER_TILE > 0 ? S - 2 : 0;
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) {
+        if (s < nk) {
+            fill(s, ring + s * STG, ring + s * STG + AOFF);
+            land(ring + s * STG, ring + s * STG + AOFF);
         }
-        __syncthreads();
+    }
+    int cur = 0, nxt = S - 1;  // stage of tile kt, stage for tile kt + S - 1
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_tiles_barrier<MAXAHEAD, PER_TILE>(min(MAXAHEAD, nk - 1 - kt));
+        const bool more = kt + S - 1 < nk;
+        u32x4_t* ns = ring + nxt * STG;
+        if (more) fill(kt + S - 1, ns, ns + AOFF);
+        u32x4_t* cs = ring + cur * STG;
+        mma_tile<C>(cs, cs + AOFF, acc, wm, wn, lane);
+        if (more) land(ns, ns + AOFF);
+        cur = (cur + 1 == S) ? 0 : cur + 1;
+        nxt = (nxt + 1 == S) ? 0 : nxt + 1;
     }
 }
 
@@ -114,12 +208,11 @@ __device__ __forceinline__ const NGroup& pick_group(const DenseGemm& g, int n) {
     return g.g[0];
 }
 
-__device__ __forceinline__ float apply_epi(int epi, float v, float bias_v) {
+__device__ __forceinline__ float apply_epi(int epi, float v) {
     if (epi == EPI_RELU2) {
         v = fmaxf(v, 0.f);
         return v * v;
     }
-    if (epi == EPI_F32_BIAS) return v + bias_v;
     return v;
 }
 
@@ -130,7 +223,7 @@ __device__ __forceinline__ void dense_store1(const DenseGemm& g, int m, int n, f
     if (G.epi == EPI_F32_BIAS) {
         ((float*)G.C)[off] = v + (G.bias ? G.bias[nc] : 0.f);
     } else {
-        ((uint16_t*)G.C)[off] = f32_to_bf16_rne(apply_epi(G.epi, v, 0.f));
+        ((uint16_t*)G.C)[off] = f32_to_bf16_rne(apply_epi(G.epi, v));
     }
 }
 
@@ -152,8 +245,8 @@ __device__ __forceinline__ void dense_store4(const DenseGemm& g, int m, int n, c
             *reinterpret_cast<float4*>((float*)G.C + off) = o;
         } else {
             uint2 o;
-            o.x = pack_bf16x2(apply_epi(G.epi, v[0], 0.f), apply_epi(G.epi, v[1], 0.f));
-            o.y = pack_bf16x2(apply_epi(G.epi, v[2], 0.f), apply_epi(G.epi, v[3], 0.f));
+            o.x = pack_bf16x2(apply_epi(G.epi, v[0]), apply_epi(G.epi, v[1]));
+            o.y = pack_bf16x2(apply_epi(G.epi, v[2]), apply_epi(G.epi, v[3]));
             *reinterpret_cast<uint2*>((uint16_t*)G.C + off) = o;
         }
         return;
@@ -164,10 +257,11 @@ __device__ __forceinline__ void dense_store4(const DenseGemm& g, int m, int n, c
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT, 1) void dense_gemm_kernel(DenseGemm g, int tiles_m, int tiles_n,
+__global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g, int tiles_m, int tiles_n,
                                                               int group_m) {
-    __shared__ u32x4_t smem[C::LDS_CHUNKS];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
     const int w = xcd_work_index(blockIdx.x, tiles_m * tiles_n);
@@ -178,20 +272,21 @@ __global__ __launch_bounds__(C::NT, 1) void dense_gemm_kernel(DenseGemm g, int t
     const int m0 = (first_m + (w % width) % gsz) * C::BM;
     const int n0 = ((w % width) / gsz) * C::BN;
 
-    const int ch = tid & 7, r0 = tid >> 3;
-    const uint16_t* a_ptr[C::A_LD];
-    const uint16_t* b_ptr[C::B_LD];
+    using SA = Slots<C, C::BM>;
+    using SB = Slots<C, C::BN>;
+    const uint16_t* a_ptr[SA::N];
+    const uint16_t* b_ptr[SB::N];
     auto setup_seg = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) {
-            const int m = min(m0 + r0 + i * C::RPP, g.M - 1);
-            a_ptr[i] = (const uint16_t*)g.A[s] + (int64_t)m * g.lda[s] + ch * 8;
+        for (int j = 0; j < SA::N; ++j) {
+            const int m = min(m0 + SA::row(j, tid), g.M - 1);
+            a_ptr[j] = (const uint16_t*)g.A[s] + (int64_t)m * g.lda[s] + SA::lchunk(j, tid) * 8;
         }
 #pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) {
-            const int n = min(n0 + r0 + i * C::RPP, g.N - 1);
+        for (int j = 0; j < SB::N; ++j) {
+            const int n = min(n0 + SB::row(j, tid), g.N - 1);
             const NGroup& G = pick_group(g, n);
-            b_ptr[i] = (const uint16_t*)G.B[s] + (int64_t)(n - G.n_begin) * g.K[s] + ch * 8;
+            b_ptr[j] = (const uint16_t*)G.B[s] + (int64_t)(n - G.n_begin) * g.K[s] + SB::lchunk(j, tid) * 8;
         }
     };
 
@@ -200,28 +295,39 @@ __global__ __launch_bounds__(C::NT, 1) void dense_gemm_kernel(DenseGemm g, int t
     int cur_seg = 0;
     setup_seg(0);
 
-    u32x4_t ra[C::A_LD], rb[C::B_LD];
-    auto gload = [&](int kt) __attribute__((always_inline)) {
+    u32x4_t ra[C::DMA ? 1 : SA::N], rb[C::DMA ? 1 : SB::N];
+    auto fill = [&](int kt, u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
         if (kt == nk0 && cur_seg == 0) {
             cur_seg = 1;
             setup_seg(1);
         }
         const int kk = (kt - (cur_seg ? nk0 : 0)) * C::BK;
+        if constexpr (C::DMA) {
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_ptr[i] + kk);
+            for (int j = 0; j < SA::N; ++j)
+                if (SA::active(j, tid)) dma16(a_ptr[j] + kk, SA::dst(As, wave, j));
 #pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(b_ptr[i] + kk);
+            for (int j = 0; j < SB::N; ++j)
+                if (SB::active(j, tid)) dma16(b_ptr[j] + kk, SB::dst(Bs, wave, j));
+        } else {
+#pragma unroll
+            for (int j = 0; j < SA::N; ++j) ra[j] = *reinterpret_cast<const u32x4_t*>(a_ptr[j] + kk);
+#pragma unroll
+            for (int j = 0; j < SB::N; ++j) rb[j] = *reinterpret_cast<const u32x4_t*>(b_ptr[j] + kk);
+        }
     };
-    auto lstore = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+    auto land = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+        if constexpr (!C::DMA) {
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) As[swz(r0 + i * C::RPP, ch)] = ra[i];
+            for (int j = 0; j < SA::N; ++j) As[lds_idx<C>(SA::row(j, tid), SA::lchunk(j, tid))] = ra[j];
 #pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) Bs[swz(r0 + i * C::RPP, ch)] = rb[i];
+            for (int j = 0; j < SB::N; ++j) Bs[lds_idx<C>(SB::row(j, tid), SB::lchunk(j, tid))] = rb[j];
+        }
     };
 
     f32x16_t acc[C::TM][C::TN];
     zero_acc<C>(acc);
-    mainloop<C>(nk, gload, lstore, smem, acc, wm, wn, lane);
+    kloop<C, C::DMA ? SA::N + SB::N : 0>(nk, fill, land, ring, acc, wm, wn, lane);
 
 #pragma unroll
     for (int tm = 0; tm < C::TM; ++tm) {
@@ -283,108 +389,214 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float scale) {
     return r;
 }
 
+// Persistent grouped GEMM.  One block per CU walks a list of work items,
+// each one M tile of one expert (tiles[i] = {expert, first sorted row, rows})
+// times one BN-wide N tile, in M-tile-major order: item w is M tile w / nN,
+// N tile w % nN.  An XCD's blocks (block b runs on XCD b % 8) take its
+// contiguous range of items round-robin, so in each round they cover
+// consecutive items: all N tiles of an M tile (shared A rows) and the M
+// tiles of an expert (shared weights) are in L2 together.
+//
+// The K steps of all the block's items form one flattened loop through the
+// LDS ring: the first stages of the next item are in flight while the
+// current item finishes and writes its epilogue, and the next item's
+// descriptor is fetched one item ahead, so short-K items (K = l or f) do not
+// pay a pipeline fill each.
+//
+// A (gathered activation rows) always uses the tile's loader policy; B is a
+// dense bf16 expert stack (same policy) or NVFP4 codes (always through
+// registers, decoded on the way to LDS).
 template <class C, int BFMT>
-__global__ __launch_bounds__(C::NT, 1) void grouped_gemm_kernel(GroupedGemm g, int nN) {
-    __shared__ u32x4_t smem[C::LDS_CHUNKS];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGemm g, int nN) {
+    __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-
-    const int total_tiles = *g.tt.tile_count;
-    const int w = xcd_work_index(blockIdx.x, total_tiles * nN);
-    if (w < 0) return;
-    // Work order: expert-major, then N tile, then M tile, so the M tiles of one
-    // (expert, N tile) pair run back to back on the same XCD.
-    const int e = g.tt.tiles[w / nN].x;
-    const int ts0 = g.tt.expert_tile_start[e], nt = g.tt.expert_ntiles[e];
-    const int local = w - ts0 * nN;
-    const int n0 = (local / nt) * C::BN;
-    const int4 tile = g.tt.tiles[ts0 + local % nt];
-    const int row0 = tile.y, rows = tile.z;
-
-    const int ch = tid & 7, r0 = tid >> 3;
     const int N = g.N, K = g.K;
-    const uint16_t* a_ptr[C::A_LD];
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) {
-        const int p = row0 + min(r0 + i * C::RPP, rows - 1);
-        const int ar = g.a_row_map ? g.a_row_map[p] / g.a_row_div : p;
-        a_ptr[i] = (const uint16_t*)g.A + (int64_t)ar * g.lda + ch * 8;
-    }
-    const uint16_t* b_ptr[C::B_LD];
-    const uint32_t* c_ptr[C::B_LD];
-    const uint8_t* s_ptr[C::B_LD];
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-        const int64_t n = (int64_t)e * N + min(n0 + r0 + i * C::RPP, N - 1);
-        if constexpr (BFMT == LMOE_NVFP4) {
-            c_ptr[i] = (const uint32_t*)(g.B_codes + n * (K / 2)) + ch;
-            s_ptr[i] = g.B_scales + n * (K / 16) + (ch >> 1);
-        } else {
-            b_ptr[i] = (const uint16_t*)g.B + n * K + ch * 8;
-        }
-    }
+    const int nk = K / C::BK;
 
-    u32x4_t ra[C::A_LD], rb[C::B_LD];
-    uint32_t rc[C::B_LD], rs[C::B_LD];
-    auto gload = [&](int kt) __attribute__((always_inline)) {
-        const int kk = kt * C::BK;
+    const int W = *g.tt.tile_count * nN;
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+    const int per = W >> 3, rem = W & 7;
+    const int first = x * per + min(x, rem);
+    const int end = first + per + (x < rem ? 1 : 0);
+    if (first + slot >= end) return;
+    const int n_items = (end - 1 - first - slot) / nbx + 1;
+    const int total = n_items * nk;
+    // descriptor {expert, first sorted row, rows, n0} of this block's item i
+    auto load_item = [&](int i) __attribute__((always_inline)) {
+        const int w = first + slot + min(i, n_items - 1) * nbx;
+        const int4 t = g.tt.tiles[w / nN];
+        return make_int4(t.x, t.y, t.z, (w % nN) * C::BN);
+    };
+
+    constexpr bool B_DMA = C::DMA && BFMT != LMOE_NVFP4;
+    using SA = Slots<C, C::BM>;
+    using SB = Slots<C, C::BN>;
+    using C_REG = MfmaCfg<C::BM, C::BN, C::WAVES_M, C::WAVES_N, false, C::BK, C::STAGES, C::MINB>;
+    using SBR = Slots<C_REG, C::BN>;  // register slots for the NVFP4 weights
+
+    // ---- fill side: pointers of the item whose K steps are being issued
+    const uint16_t* a_ptr[SA::N];
+    const uint16_t* b_ptr[BFMT == LMOE_NVFP4 ? 1 : SB::N];
+    const uint32_t* c_ptr[BFMT == LMOE_NVFP4 ? SBR::N : 1];
+    const uint8_t* s_ptr[BFMT == LMOE_NVFP4 ? SBR::N : 1];
+    int4 fdesc = load_item(0);
+    int4 fnext = load_item(1);
+    int f_item = 0, f_kt = 0;
+    auto setup = [&](const int4& d) __attribute__((always_inline)) {
+        const int e = d.x, row0 = d.y, rows = d.z, n0 = d.w;
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_ptr[i] + kk);
+        for (int j = 0; j < SA::N; ++j) {
+            const int p = row0 + min(SA::row(j, tid), rows - 1);
+            const int ar = g.a_row_map ? g.a_row_map[p] / g.a_row_div : p;
+            a_ptr[j] = (const uint16_t*)g.A + (int64_t)ar * g.lda + SA::lchunk(j, tid) * 8;
+        }
+        if constexpr (BFMT == LMOE_NVFP4) {
 #pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) {
-            if constexpr (BFMT == LMOE_NVFP4) {
-                rc[i] = c_ptr[i][kt * 8];  // 32 code bytes per row per K tile
-                rs[i] = s_ptr[i][kt * 4];  // 4 scale bytes per row per K tile
-            } else {
-                rb[i] = *reinterpret_cast<const u32x4_t*>(b_ptr[i] + kk);
+            for (int j = 0; j < SBR::N; ++j) {
+                const int64_t n = (int64_t)e * N + min(n0 + SBR::row(j, tid), N - 1);
+                const int ch = SBR::lchunk(j, tid);
+                c_ptr[j] = (const uint32_t*)(g.B_codes + n * (K / 2)) + ch;
+                s_ptr[j] = g.B_scales + n * (K / 16) + (ch >> 1);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < SB::N; ++j) {
+                const int64_t n = (int64_t)e * N + min(n0 + SB::row(j, tid), N - 1);
+                b_ptr[j] = (const uint16_t*)g.B + n * K + SB::lchunk(j, tid) * 8;
             }
         }
     };
-    auto lstore = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+    setup(fdesc);
+
+    u32x4_t ra[C::DMA ? 1 : SA::N], rb[B_DMA || BFMT == LMOE_NVFP4 ? 1 : SB::N];
+    uint32_t rc[BFMT == LMOE_NVFP4 ? SBR::N : 1], rs[BFMT == LMOE_NVFP4 ? SBR::N : 1];
+    // issues the next K step of the fill item into stage (As, Bs)
+    auto fill_next = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+        if (f_kt == nk) {  // next item: its descriptor was fetched one item ahead
+            f_kt = 0;
+            ++f_item;
+            fdesc = fnext;
+            setup(fdesc);
+            fnext = load_item(f_item + 1);
+        }
+        const int kt = f_kt++;
+        const int kk = kt * C::BK;
+        if constexpr (BFMT == LMOE_NVFP4) {
+            // register loads first, so waiting for them does not wait for the DMA
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) As[swz(r0 + i * C::RPP, ch)] = ra[i];
+            for (int j = 0; j < SBR::N; ++j) {
+                rc[j] = c_ptr[j][kt * C::CPR];        // K/2 code bytes per row per K tile
+                rs[j] = s_ptr[j][kt * (C::BK / 16)];  // one scale byte per 16 elements
+            }
+        } else if constexpr (B_DMA) {
 #pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) {
-            if constexpr (BFMT == LMOE_NVFP4)
-                Bs[swz(r0 + i * C::RPP, ch)] = decode_e2m1x8(rc[i], e4m3_to_f32(rs[i]));
-            else
-                Bs[swz(r0 + i * C::RPP, ch)] = rb[i];
+            for (int j = 0; j < SB::N; ++j)
+                if (SB::active(j, tid)) dma16(b_ptr[j] + kk, SB::dst(Bs, wave, j));
+        } else {
+#pragma unroll
+            for (int j = 0; j < SB::N; ++j) rb[j] = *reinterpret_cast<const u32x4_t*>(b_ptr[j] + kk);
+        }
+        if constexpr (C::DMA) {
+#pragma unroll
+            for (int j = 0; j < SA::N; ++j)
+                if (SA::active(j, tid)) dma16(a_ptr[j] + kk, SA::dst(As, wave, j));
+        } else {
+#pragma unroll
+            for (int j = 0; j < SA::N; ++j) ra[j] = *reinterpret_cast<const u32x4_t*>(a_ptr[j] + kk);
+        }
+    };
+    auto land = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+        if constexpr (!C::DMA) {
+#pragma unroll
+            for (int j = 0; j < SA::N; ++j) As[lds_idx<C>(SA::row(j, tid), SA::lchunk(j, tid))] = ra[j];
+        }
+        if constexpr (BFMT == LMOE_NVFP4) {
+#pragma unroll
+            for (int j = 0; j < SBR::N; ++j)
+                Bs[lds_idx<C>(SBR::row(j, tid), SBR::lchunk(j, tid))] = decode_e2m1x8(rc[j], e4m3_to_f32(rs[j]));
+        } else if constexpr (!B_DMA) {
+#pragma unroll
+            for (int j = 0; j < SB::N; ++j) Bs[lds_idx<C>(SB::row(j, tid), SB::lchunk(j, tid))] = rb[j];
         }
     };
 
+    // ---- multiply side: the item whose K steps are being multiplied.  Its
+    // per-row epilogue scale (gate, NVFP4 tensor scale) is fetched at the
+    // item's first step, well before the epilogue needs it.
+    int4 mdesc = fdesc;
+    float row_scale[C::TM];
+    auto fetch_scales = [&](const int4& d) __attribute__((always_inline)) {
+        const float ts = (BFMT == LMOE_NVFP4) ? g.B_ts[d.x] : 1.0f;
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) {
+            const int ml = min(wm * C::WM + tm * 32 + (lane & 31), d.z - 1);
+            row_scale[tm] = (g.epi == EPI_GATE) ? ts * g.gate[g.gate_map[d.y + ml]] : ts;
+        }
+    };
+    fetch_scales(mdesc);
+    auto epilogue = [&](const int4& d, f32x16_t (&acc)[C::TM][C::TN]) __attribute__((always_inline)) {
+        const int row0 = d.y, rows = d.z, n0 = d.w;
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) {
+            const int ml = wm * C::WM + tm * 32 + (lane & 31);
+            if (ml >= rows) continue;
+            const int p = row0 + ml;
+            uint16_t* crow = (uint16_t*)g.C + (int64_t)p * g.ldc;
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * C::WN + tn * 32 + q * 8 + (lane >> 5) * 4;
+                    if (n >= N) continue;
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[i] = acc[tm][tn][q * 4 + i] * row_scale[tm];
+                        if (g.epi == EPI_RELU2) {
+                            v[i] = fmaxf(v[i], 0.f);
+                            v[i] *= v[i];
+                        }
+                    }
+                    uint2 o;
+                    o.x = pack_bf16x2(v[0], v[1]);
+                    o.y = pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<uint2*>(crow + n) = o;
+                }
+        }
+    };
+
+    constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS, AOFF = C::BM * C::CPR;
+    constexpr int PER_TILE = (C::DMA && B_DMA) ? SA::N + SB::N : 0;
+    constexpr int MAXAHEAD = PER_TILE > 0 ? S - 2 : 0;
     f32x16_t acc[C::TM][C::TN];
     zero_acc<C>(acc);
-    mainloop<C>(K / C::BK, gload, lstore, smem, acc, wm, wn, lane);
-
-    const float scale = (BFMT == LMOE_NVFP4) ? g.B_ts[e] : 1.0f;
 #pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm) {
-        const int ml = wm * C::WM + tm * 32 + (lane & 31);
-        if (ml >= rows) continue;
-        const int p = row0 + ml;
-        float rs_ = scale;
-        if (g.epi == EPI_GATE) rs_ *= g.gate[g.gate_map[p]];
-        uint16_t* crow = (uint16_t*)g.C + (int64_t)p * g.ldc;
-#pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * C::WN + tn * 32 + q * 8 + (lane >> 5) * 4;
-                if (n >= N) continue;
-                float v[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[i] = acc[tm][tn][q * 4 + i] * rs_;
-                    if (g.epi == EPI_RELU2) {
-                        v[i] = fmaxf(v[i], 0.f);
-                        v[i] *= v[i];
-                    }
-                }
-                uint2 o;
-                o.x = pack_bf16x2(v[0], v[1]);
-                o.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(crow + n) = o;
-            }
+    for (int st = 0; st < S - 1; ++st) {
+        if (st < total) {
+            fill_next(ring + st * STG, ring + st * STG + AOFF);
+            land(ring + st * STG, ring + st * STG + AOFF);
+        }
+    }
+    int cur = 0, nxt = S - 1, m_kt = 0;
+    for (int q = 0; q < total; ++q) {
+        wait_tiles_barrier<MAXAHEAD, PER_TILE>(min(MAXAHEAD, total - 1 - q));
+        const bool more = q + S - 1 < total;
+        u32x4_t* ns = ring + nxt * STG;
+        if (more) fill_next(ns, ns + AOFF);
+        u32x4_t* cs = ring + cur * STG;
+        mma_tile<C>(cs, cs + AOFF, acc, wm, wn, lane);
+        if (more) land(ns, ns + AOFF);
+        cur = (cur + 1 == S) ? 0 : cur + 1;
+        nxt = (nxt + 1 == S) ? 0 : nxt + 1;
+        if (++m_kt == nk) {
+            m_kt = 0;
+            epilogue(mdesc, acc);
+            zero_acc<C>(acc);
+            mdesc = fdesc;  // the fill side is already on the next item
+            fetch_scales(mdesc);
+        }
     }
 }
 
@@ -399,15 +611,23 @@ static hipError_t run_dense(const DenseGemm& g, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_dense_gemm_bf16(const DenseGemm& g, hipStream_t s) {
-    if (g.M <= 64) return run_dense<MfmaCfg<64, 64, 2, 2>>(g, s);
-    return run_dense<MfmaCfg<128, 256, 2, 2>>(g, s);
+// Persistent grid: one block per CU (a multiple of 8, one slot per XCD),
+// times the blocks per CU the tile configuration is sized for.
+static int persistent_grid() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    return (cus + 7) / 8 * 8;
 }
 
 template <class C>
 static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
     const int nN = (g.N + C::BN - 1) / C::BN;
-    const int grid = g.tt.max_tiles * nN;
+    const int grid = persistent_grid() * C::MINB;
     if (g.b_fmt == LMOE_NVFP4)
         LMOE_LAUNCH("grouped_gemm_nvfp4", s, grouped_gemm_kernel<C, LMOE_NVFP4><<<grid, C::NT, 0, s>>>(g, nN));
     else
@@ -415,10 +635,23 @@ static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+#ifndef LMOE_GEMM_VARIANTS
+// Dense: 256x256 tiles over 8 waves (2 per SIMD), each wave 64 x 128; the
+// fastest shape measured for the 8192-wide projections.  Decode-sized M
+// uses 64x64 tiles.
+hipError_t launch_dense_gemm_bf16(const DenseGemm& g, hipStream_t s) {
+    if (g.M <= 64) return run_dense<MfmaCfg<64, 64, 2, 2, true>>(g, s);
+    return run_dense<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, s);
+}
+
+// Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to
+// 384) by 256 columns over 8 waves, each wave 96 x 64; few-row experts at
+// decode use 32-row tiles.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
-    if (g.tt.bm == 128) return run_grouped<MfmaCfg<128, 256, 2, 2>>(g, s);
-    if (g.tt.bm == 32) return run_grouped<MfmaCfg<32, 128, 1, 4>>(g, s);
+    if (g.tt.bm == 192) return run_grouped<MfmaCfg<192, 256, 2, 4, true, 64, 2>>(g, s);
+    if (g.tt.bm == 32) return run_grouped<MfmaCfg<32, 128, 1, 4, true, 64, 2, 4>>(g, s);
     return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace lmoe
