@@ -211,24 +211,23 @@ int lmoe_permute(const lmoe_dims* dims, const int32_t* topk_idx, int32_t* counts
 /*
  * Routed experts in the latent space (overview section 2.2 step 2), in
  * sorted order: for each sorted position p with pair (t, j) = perm[p] and
- * expert e, Y[p] = topk_gate[t][j] * W2_e (max(0, W1_e z_t))^2, Y [T*k][l]
- * act dtype.  NVFP4 weights are decoded in the kernel.
+ * expert e, Y[p] = W2_e (max(0, W1_e z_t))^2, Y [T*k][l] act dtype (the gate
+ * is applied by the combine).  NVFP4 weights are decoded in the kernel.
  */
-int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const float* topk_gate,
-                     const int32_t* offsets, const int32_t* perm,
-                     const lmoe_experts* experts, void* Y,
+int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const int32_t* offsets,
+                     const int32_t* perm, const lmoe_experts* experts, void* Y,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Combine and up-projection (overview section 2.2 step 3): c_t = sum over
- * j = 0..k-1, in that order, of Y[inv[t*k + j]] (no atomics; deterministic),
- * out = c W_up^T [+ hs W_s2^T if shared].  c [T][l] may be NULL (then it
- * lives in the workspace).
+ * j = 0..k-1, in that order, of topk_gate[t][j] * Y[inv[t*k + j]] in fp32 (no
+ * atomics; deterministic), out = c W_up^T [+ hs W_s2^T if shared].
+ * c [T][l] may be NULL (then it lives in the workspace).
  */
 int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv,
-                    const void* W_up, const lmoe_shared* shared, const void* hs,
-                    void* c, void* out, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    const float* topk_gate, const void* W_up,
+                    const lmoe_shared* shared, const void* hs, void* c, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -90,8 +90,8 @@ def lib() -> ctypes.CDLL:
         L.lmoe_project_route.argtypes = [pd, vp, vp, vp, vp, ctypes.POINTER(Shared), vp, vp, vp, vp,
                                          vp, vp, sz, vp]
         L.lmoe_permute.argtypes = [pd, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.lmoe_experts_ffn.argtypes = [pd, vp, vp, vp, vp, ctypes.POINTER(Experts), vp, vp, sz, vp]
-        L.lmoe_combine_up.argtypes = [pd, vp, vp, vp, ctypes.POINTER(Shared), vp, vp, vp, vp, sz, vp]
+        L.lmoe_experts_ffn.argtypes = [pd, vp, vp, vp, ctypes.POINTER(Experts), vp, vp, sz, vp]
+        L.lmoe_combine_up.argtypes = [pd, vp, vp, vp, vp, ctypes.POINTER(Shared), vp, vp, vp, vp, sz, vp]
         L.lmoe_timing_start.argtypes = [ctypes.c_int]
         L.lmoe_timing_start.restype = ctypes.c_int
         L.lmoe_timing_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -259,25 +259,25 @@ def permute(cfg: LayerDims, idx: torch.Tensor, workspace, stream=None):
     return dict(counts=counts, offsets=offsets, perm=perm, inv=inv)
 
 
-def experts_ffn(cfg: LayerDims, inp, z, gate, offsets, perm, workspace, stream=None):
+def experts_ffn(cfg: LayerDims, inp, z, offsets, perm, workspace, stream=None):
     T, dev = z.shape[0], z.device
     Y = torch.empty((T * cfg.k, cfg.l), dtype=act_dtype(cfg), device=dev)
     ex = experts_struct(inp)
     d = dims_of(cfg, T)
-    _check(lib().lmoe_experts_ffn(ctypes.byref(d), _p(z), _p(gate), _p(offsets), _p(perm),
+    _check(lib().lmoe_experts_ffn(ctypes.byref(d), _p(z), _p(offsets), _p(perm),
                                   ctypes.byref(ex), _p(Y), _p(workspace), workspace.numel(),
                                   _stream(stream)), "lmoe_experts_ffn")
     return Y
 
 
-def combine_up(cfg: LayerDims, inp, Y, inv, hs, workspace, T: int, stream=None):
+def combine_up(cfg: LayerDims, inp, Y, inv, gate, hs, workspace, T: int, stream=None):
     dev = Y.device
     dt = act_dtype(cfg)
     c = torch.empty((T, cfg.l), dtype=dt, device=dev)
     out = torch.empty((T, cfg.d), dtype=dt, device=dev)
     sh = shared_struct(inp)
     d = dims_of(cfg, T)
-    _check(lib().lmoe_combine_up(ctypes.byref(d), _p(Y), _p(inv), _p(inp["W_up"]), _byref_opt(sh),
+    _check(lib().lmoe_combine_up(ctypes.byref(d), _p(Y), _p(inv), _p(gate), _p(inp["W_up"]), _byref_opt(sh),
                                  _p(hs), _p(c), _p(out), _p(workspace), workspace.numel(),
                                  _stream(stream)), "lmoe_combine_up")
     return dict(c=c, out=out)

@@ -8,8 +8,8 @@
 //   2. top-k + softmax gate                     -> idx, gate
 //   3. permutation (hist, scan + tile table, stable scatter)
 //   4. grouped GEMM  H = relu(z[perm] W1_e^T)^2
-//   5. grouped GEMM  Y = gate * (H W2_e^T)
-//   6. combine       c_t = sum_j Y[inv(t, j)]
+//   5. grouped GEMM  Y = H W2_e^T
+//   6. combine       c_t = sum_j gate_tj Y[inv(t, j)]
 //   7. dense GEMM    out = [c | hs] [W_up | W_s2]^T
 #include <string.h>
 
@@ -17,14 +17,15 @@
 
 namespace lmoe {
 
-hipError_t launch_dense_gemm_bf16(const DenseGemm& g, hipStream_t s);
+hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s);
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_dense_gemm_f32(const DenseGemm& g, hipStream_t s);
 hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t s);
 
-hipError_t launch_dense_gemm(const DenseGemm& g, int act_dtype, int /*T_hint*/, void* /*splitk_ws*/,
-                             size_t /*splitk_bytes*/, hipStream_t s) {
-    return act_dtype == LMOE_BF16 ? launch_dense_gemm_bf16(g, s) : launch_dense_gemm_f32(g, s);
+hipError_t launch_dense_gemm(const DenseGemm& g, int act_dtype, int /*T_hint*/, void* splitk_ws,
+                             size_t splitk_bytes, hipStream_t s) {
+    return act_dtype == LMOE_BF16 ? launch_dense_gemm_bf16(g, splitk_ws, splitk_bytes, s)
+                                  : launch_dense_gemm_f32(g, s);
 }
 
 hipError_t launch_grouped_gemm(const GroupedGemm& g, int act_dtype, hipStream_t s) {
@@ -34,7 +35,7 @@ hipError_t launch_grouped_gemm(const GroupedGemm& g, int act_dtype, hipStream_t 
 int grouped_bm(const lmoe_dims& d) {
     if (d.act_dtype == LMOE_F32) return 64;
     const double avg = (double)d.T * (double)d.k / (double)d.E;
-    return avg >= 96.0 ? 192 : 32;
+    return avg >= 96.0 ? 192 : 64;
 }
 
 static int64_t max_tiles(const lmoe_dims& d) {
@@ -45,7 +46,7 @@ static int64_t max_tiles(const lmoe_dims& d) {
 
 struct Layout {
     size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
-        c, hs, total;
+        c, hs, splitk, splitk_bytes, total;
 };
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -77,6 +78,10 @@ static Layout plan(const lmoe_dims& d) {
     L.Y = take(n * d.l * es);
     L.c = take((size_t)d.T * d.l * es);
     L.hs = take((size_t)d.T * d.f_s * es);
+    // fp32 split-K partials of the dense GEMMs of few-token (decode) calls
+    const size_t widest = (size_t)((max(d.l + d.E + d.f_s, d.d) + 3) / 4 * 4);
+    L.splitk_bytes = (d.act_dtype == LMOE_BF16 && d.T <= 64) ? 16 * (size_t)d.T * widest * 4 : 0;
+    L.splitk = take(L.splitk_bytes);
     L.total = o;
     return L;
 }
@@ -141,7 +146,8 @@ static TileTable tile_table(const lmoe_dims& d, char* ws, const Layout& L) {
 
 static hipError_t run_project_route(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r,
                                     const float* bias, const lmoe_shared* sh, void* z, float* logits,
-                                    int32_t* idx, float* gate, void* hs, hipStream_t s) {
+                                    int32_t* idx, float* gate, void* hs, char* ws, const Layout& L,
+                                    hipStream_t s) {
     DenseGemm g{};
     g.M = (int)d.T;
     g.N = (int)(d.l + d.E + d.f_s);
@@ -153,13 +159,13 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
     g.g[0] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
     g.g[1] = NGroup{(int)d.l, (int)(d.l + d.E), {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
     if (sh) g.g[2] = NGroup{(int)(d.l + d.E), g.N, {sh->W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
-    hipError_t e = launch_dense_gemm(g, d.act_dtype, (int)d.T, nullptr, 0, s);
+    hipError_t e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
     if (e != hipSuccess) return e;
     return launch_topk_softmax(logits, (int)d.T, (int)d.E, (int)d.k, idx, gate, s);
 }
 
-static hipError_t run_experts(const lmoe_dims& d, const void* z, const float* gate, const int32_t* perm,
-                              const lmoe_experts* ex, void* H, void* Y, const TileTable& tt, hipStream_t s) {
+static hipError_t run_experts(const lmoe_dims& d, const void* z, const int32_t* perm, const lmoe_experts* ex,
+                              void* H, void* Y, const TileTable& tt, hipStream_t s) {
     GroupedGemm g1{};
     g1.N = (int)d.f;
     g1.K = (int)d.l;
@@ -168,6 +174,7 @@ static hipError_t run_experts(const lmoe_dims& d, const void* z, const float* ga
     g1.lda = d.l;
     g1.a_row_map = perm;
     g1.a_row_div = (int)d.k;
+    g1.n_rows = (int)(d.T * d.k);
     g1.b_fmt = d.expert_dtype;
     g1.B = ex->W1;
     g1.B_codes = ex->W1_codes;
@@ -190,17 +197,16 @@ static hipError_t run_experts(const lmoe_dims& d, const void* z, const float* ga
     g2.B_codes = ex->W2_codes;
     g2.B_scales = ex->W2_scales;
     g2.B_ts = ex->W2_ts;
-    g2.epi = EPI_GATE;
-    g2.gate = gate;
-    g2.gate_map = perm;
+    g2.epi = EPI_STORE;
     g2.C = Y;
     g2.ldc = d.l;
     return launch_grouped_gemm(g2, d.act_dtype, s);
 }
 
-static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_t* inv, const void* W_up,
-                                 const lmoe_shared* sh, const void* hs, void* c, void* out, hipStream_t s) {
-    hipError_t e = launch_combine(Y, inv, (int)d.T, (int)d.k, (int)d.l, d.act_dtype, c, s);
+static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_t* inv, const float* gate,
+                                 const void* W_up, const lmoe_shared* sh, const void* hs, void* c, void* out,
+                                 char* ws, const Layout& L, hipStream_t s) {
+    hipError_t e = launch_combine(Y, inv, gate, (int)d.T, (int)d.k, (int)d.l, d.act_dtype, c, s);
     if (e != hipSuccess) return e;
     DenseGemm g{};
     g.M = (int)d.T;
@@ -216,7 +222,7 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
     }
     g.ngroups = 1;
     g.g[0] = NGroup{0, (int)d.d, {W_up, sh ? sh->W_s2 : nullptr}, EPI_STORE, out, d.d, nullptr};
-    return launch_dense_gemm(g, d.act_dtype, (int)d.T, nullptr, 0, s);
+    return launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
 }
 
 }  // namespace lmoe
@@ -306,11 +312,12 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, 
     void* hs = ws + L.hs;
     const TileTable tt = tile_table(d, ws, L);
 
-    hipError_t e = run_project_route(d, x, W_down, W_router, router_bias, shared, z, logits, idx, gate, hs, s);
+    hipError_t e =
+        run_project_route(d, x, W_down, W_router, router_bias, shared, z, logits, idx, gate, hs, ws, L, s);
     if (e == hipSuccess)
         e = launch_permute(idx, d.T * d.k, (int)d.E, (int32_t*)(ws + L.hist), counts, offsets, perm, inv, &tt, s);
-    if (e == hipSuccess) e = run_experts(d, z, gate, perm, experts, ws + L.H, ws + L.Y, tt, s);
-    if (e == hipSuccess) e = run_combine_up(d, ws + L.Y, inv, W_up, shared, hs, c, out, s);
+    if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, ws + L.Y, tt, s);
+    if (e == hipSuccess) e = run_combine_up(d, ws + L.Y, inv, gate, W_up, shared, hs, c, out, ws, L, s);
     return hip_status(e);
 }
 
@@ -325,8 +332,9 @@ int lmoe_project_route(const lmoe_dims* dims, const void* x, const void* W_down,
     LMOE_TRY(check_shared(d, shared));
     if (shared) LMOE_TRY(check_ptrs({hs}));
     LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
+    const Layout L = plan(d);
     return hip_status(run_project_route(d, x, W_down, W_router, router_bias, shared, z, logits, topk_idx,
-                                        topk_gate, hs, (hipStream_t)stream));
+                                        topk_gate, hs, (char*)workspace, L, (hipStream_t)stream));
 }
 
 int lmoe_permute(const lmoe_dims* dims, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -341,12 +349,11 @@ int lmoe_permute(const lmoe_dims* dims, const int32_t* topk_idx, int32_t* counts
                                      perm, inv, nullptr, (hipStream_t)stream));
 }
 
-int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const float* topk_gate, const int32_t* offsets,
-                     const int32_t* perm, const lmoe_experts* experts, void* Y, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const int32_t* offsets, const int32_t* perm,
+                     const lmoe_experts* experts, void* Y, void* workspace, size_t workspace_bytes, void* stream) {
     LMOE_TRY(lmoe_validate_dims(dims));
     const lmoe_dims& d = *dims;
-    LMOE_TRY(check_ptrs({z, topk_gate, offsets, perm, Y}));
+    LMOE_TRY(check_ptrs({z, offsets, perm, Y}));
     LMOE_TRY(check_experts(d, experts));
     LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
     char* ws = (char*)workspace;
@@ -354,23 +361,24 @@ int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const float* topk_gat
     const TileTable tt = tile_table(d, ws, L);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_build_tiles(offsets, (int)d.E, tt, s);
-    if (e == hipSuccess) e = run_experts(d, z, topk_gate, perm, experts, ws + L.H, Y, tt, s);
+    if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, Y, tt, s);
     return hip_status(e);
 }
 
-int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv, const void* W_up,
-                    const lmoe_shared* shared, const void* hs, void* c, void* out, void* workspace,
+int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv, const float* topk_gate,
+                    const void* W_up, const lmoe_shared* shared, const void* hs, void* c, void* out, void* workspace,
                     size_t workspace_bytes, void* stream) {
     LMOE_TRY(lmoe_validate_dims(dims));
     const lmoe_dims& d = *dims;
-    LMOE_TRY(check_ptrs({Y, inv, W_up, out}));
+    LMOE_TRY(check_ptrs({Y, inv, topk_gate, W_up, out}));
     LMOE_TRY(check_shared(d, shared));
     if (shared) LMOE_TRY(check_ptrs({hs}));
     LMOE_TRY(check_optional(c));
     LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
     char* ws = (char*)workspace;
     const Layout L = plan(d);
-    return hip_status(run_combine_up(d, Y, inv, W_up, shared, hs, c ? c : ws + L.c, out, (hipStream_t)stream));
+    return hip_status(run_combine_up(d, Y, inv, topk_gate, W_up, shared, hs, c ? c : ws + L.c, out, ws, L,
+                                     (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -110,12 +110,11 @@ __global__ __launch_bounds__(256) void grouped_fma_kernel(GroupedGemm g) {
         const int ml = ty * 4 + i;
         if (ml >= rows) continue;
         const int p = row0 + ml;
-        const float rs = (g.epi == EPI_GATE) ? g.gate[g.gate_map[p]] : 1.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n = n0 + tx * 4 + j;
             if (n >= g.N) continue;
-            float v = acc[i][j] * rs;
+            float v = acc[i][j];
             if (g.epi == EPI_RELU2) {
                 v = fmaxf(v, 0.f);
                 v *= v;

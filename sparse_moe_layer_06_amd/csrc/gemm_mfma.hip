@@ -71,6 +71,7 @@ template <class C, int ROWS>
 struct Slots {
     static constexpr int CPW = C::DMA ? ROWS * C::CPR / C::NW : 0;  // chunks per wave
     static constexpr int N = C::DMA ? (CPW + 63) / 64 : ROWS / C::RPP;
+    static constexpr int RPI = 64 / C::CPR;  // rows per DMA instruction
     static_assert(!C::DMA || (ROWS * C::CPR) % C::NW == 0, "DMA chunks must split evenly over the waves");
     static_assert(C::DMA || ROWS % C::RPP == 0, "register slots must tile the rows");
     __device__ static __forceinline__ int chunk(int j, int tid) { return (tid >> 6) * CPW + j * 64 + (tid & 63); }
@@ -92,6 +93,46 @@ struct Slots {
 __device__ __forceinline__ void dma16(const void* src, u32x4_t* dst) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// Scalar-memory loads of wave-uniform data.  They complete on lgkmcnt, which
+// the asm waits for before returning, so using their result never makes the
+// compiler drain the vector-memory counter that tracks the DMA tiles still
+// in flight (it cannot count those across loop iterations and would wait for
+// all of them).  Reads only; the pointer is made uniform explicitly.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t u = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ i32x4_t sload4(const void* p) {
+    i32x4_t v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ i32x8_t sload8(const void* p) {
+    i32x8_t v;
+    asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ i32x16_t sload16(const void* p) {
+    i32x16_t v;
+    asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ float sload_f32(const float* p) {
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
+    return __int_as_float(v);
 }
 
 // s_waitcnt with vmcnt(N) only (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
@@ -256,16 +297,23 @@ __device__ __forceinline__ void dense_store4(const DenseGemm& g, int m, int n, c
         if (n + i < g.N) dense_store1(g, m, n + i, v[i]);
 }
 
+// With splits > 1 (split-K, for few-row GEMMs whose tiles alone cannot fill
+// the GPU), block (tile, split) accumulates the K steps
+// [split * nk / splits, (split + 1) * nk / splits) and stores its fp32
+// partial tile to partial[split][M][ldp]; splitk_reduce_kernel sums the
+// splits in order and applies the column-group epilogue.
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g, int tiles_m, int tiles_n,
-                                                              int group_m) {
+                                                              int group_m, int splits, float* partial,
+                                                              int ldp) {
     __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-    const int w = xcd_work_index(blockIdx.x, tiles_m * tiles_n);
-    if (w < 0) return;
+    const int ws_ = xcd_work_index(blockIdx.x, tiles_m * tiles_n * splits);
+    if (ws_ < 0) return;
+    const int split = ws_ % splits, w = ws_ / splits;
     const int width = group_m * tiles_n;
     const int first_m = (w / width) * group_m;
     const int gsz = min(tiles_m - first_m, group_m);
@@ -292,12 +340,17 @@ __global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g,
 
     const int nk0 = g.K[0] / C::BK;
     const int nk = nk0 + (g.nseg > 1 ? g.K[1] / C::BK : 0);
-    int cur_seg = 0;
-    setup_seg(0);
+    const int kb = split * nk / splits, ke = (split + 1) * nk / splits;
+    int cur_seg = kb >= nk0 ? 1 : 0;
+    if (cur_seg)  // constant segment indices keep the argument arrays out of scratch
+        setup_seg(1);
+    else
+        setup_seg(0);
 
     u32x4_t ra[C::DMA ? 1 : SA::N], rb[C::DMA ? 1 : SB::N];
-    auto fill = [&](int kt, u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
-        if (kt == nk0 && cur_seg == 0) {
+    auto fill = [&](int kt_local, u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+        const int kt = kb + kt_local;
+        if (kt >= nk0 && cur_seg == 0) {
             cur_seg = 1;
             setup_seg(1);
         }
@@ -327,7 +380,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g,
 
     f32x16_t acc[C::TM][C::TN];
     zero_acc<C>(acc);
-    kloop<C, C::DMA ? SA::N + SB::N : 0>(nk, fill, land, ring, acc, wm, wn, lane);
+    kloop<C, C::DMA ? SA::N + SB::N : 0>(ke - kb, fill, land, ring, acc, wm, wn, lane);
 
 #pragma unroll
     for (int tm = 0; tm < C::TM; ++tm) {
@@ -341,8 +394,37 @@ __global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g,
                 if (n >= g.N) continue;
                 const float v[4] = {acc[tm][tn][q * 4 + 0], acc[tm][tn][q * 4 + 1], acc[tm][tn][q * 4 + 2],
                                     acc[tm][tn][q * 4 + 3]};
-                dense_store4(g, m, n, v);
+                if (partial) {
+                    // ldp is a multiple of 4, so the 4 columns are one aligned float4
+                    *reinterpret_cast<float4*>(partial + ((int64_t)split * g.M + m) * ldp + n) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    dense_store4(g, m, n, v);
+                }
             }
+    }
+}
+
+// Sums the split-K partials in split order (deterministic) and applies the
+// epilogue.  One thread per 4 consecutive columns of one row.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseGemm g, int splits, const float* __restrict__ partial,
+                                                            int ldp) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int q = ldp / 4;
+    const int m = (int)(i / q), n = (int)(i % q) * 4;
+    if (m >= g.M || n >= g.N) return;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp) {
+        const float4 p = *reinterpret_cast<const float4*>(partial + ((int64_t)sp * g.M + m) * ldp + n);
+        v[0] += p.x;
+        v[1] += p.y;
+        v[2] += p.z;
+        v[3] += p.w;
+    }
+    if (n + 3 < g.N) {
+        dense_store4(g, m, n, v);
+    } else {
+        for (int c = 0; c < 4 && n + c < g.N; ++c) dense_store1(g, m, n + c, v[c]);
     }
 }
 
@@ -406,7 +488,10 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float scale) {
 // A (gathered activation rows) always uses the tile's loader policy; B is a
 // dense bf16 expert stack (same policy) or NVFP4 codes (always through
 // registers, decoded on the way to LDS).
-template <class C, int BFMT>
+// A-row gather modes of the grouped GEMM.
+enum Gather : int { GATHER_NONE = 0, GATHER_SCALAR = 1, GATHER_LANE = 2 };
+
+template <class C, int BFMT, int GATHER>
 __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGemm g, int nN) {
     __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -425,8 +510,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     const int total = n_items * nk;
     // descriptor {expert, first sorted row, rows, n0} of this block's item i
     auto load_item = [&](int i) __attribute__((always_inline)) {
-        const int w = first + slot + min(i, n_items - 1) * nbx;
-        const int4 t = g.tt.tiles[w / nN];
+        const int w = __builtin_amdgcn_readfirstlane(first + slot + min(i, n_items - 1) * nbx);
+        const i32x4_t t = sload4(g.tt.tiles + w / nN);
         return make_int4(t.x, t.y, t.z, (w % nN) * C::BN);
     };
 
@@ -444,12 +529,41 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     int4 fdesc = load_item(0);
     int4 fnext = load_item(1);
     int f_item = 0, f_kt = 0;
+    // A row of sorted row p for slot j.  GATHER_SCALAR (DMA slots): the
+    // slot's RPI rows are read with one scalar load of the permutation
+    // (clamped inside [0, n_rows)) and each lane picks its row.
+    constexpr int RPI = SA::RPI;
+    static_assert(GATHER != GATHER_SCALAR || (C::DMA && (RPI == 8 || RPI == 16)), "scalar gather needs DMA slots");
+    auto a_row = [&](int j, int row0, int rows) __attribute__((always_inline)) {
+        const int p = row0 + min(SA::row(j, tid), rows - 1);
+        if constexpr (GATHER == GATHER_NONE) {
+            return p;
+        } else if constexpr (GATHER == GATHER_SCALAR) {
+            const int rb = __builtin_amdgcn_readfirstlane((wave * SA::CPW + j * 64) / C::CPR);
+            const int q0 = __builtin_amdgcn_readfirstlane(min(row0 + rb, g.n_rows - RPI));
+            const int idx = min(max(p - q0, 0), RPI - 1);
+            int v;
+            if constexpr (RPI == 8) {
+                const i32x8_t r = sload8(g.a_row_map + q0);
+                v = r[0];
+#pragma unroll
+                for (int t = 1; t < 8; ++t) v = (idx == t) ? r[t] : v;
+            } else {
+                const i32x16_t r = sload16(g.a_row_map + q0);
+                v = r[0];
+#pragma unroll
+                for (int t = 1; t < 16; ++t) v = (idx == t) ? r[t] : v;
+            }
+            return v / g.a_row_div;
+        } else {
+            return g.a_row_map[p] / g.a_row_div;
+        }
+    };
     auto setup = [&](const int4& d) __attribute__((always_inline)) {
         const int e = d.x, row0 = d.y, rows = d.z, n0 = d.w;
 #pragma unroll
         for (int j = 0; j < SA::N; ++j) {
-            const int p = row0 + min(SA::row(j, tid), rows - 1);
-            const int ar = g.a_row_map ? g.a_row_map[p] / g.a_row_div : p;
+            const int ar = a_row(j, row0, rows);
             a_ptr[j] = (const uint16_t*)g.A + (int64_t)ar * g.lda + SA::lchunk(j, tid) * 8;
         }
         if constexpr (BFMT == LMOE_NVFP4) {
@@ -522,20 +636,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         }
     };
 
-    // ---- multiply side: the item whose K steps are being multiplied.  Its
-    // per-row epilogue scale (gate, NVFP4 tensor scale) is fetched at the
-    // item's first step, well before the epilogue needs it.
+    // ---- multiply side: the item whose K steps are being multiplied, and its
+    // epilogue scale (the NVFP4 tensor scale, 1 for dense weights).
     int4 mdesc = fdesc;
-    float row_scale[C::TM];
-    auto fetch_scales = [&](const int4& d) __attribute__((always_inline)) {
-        const float ts = (BFMT == LMOE_NVFP4) ? g.B_ts[d.x] : 1.0f;
-#pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm) {
-            const int ml = min(wm * C::WM + tm * 32 + (lane & 31), d.z - 1);
-            row_scale[tm] = (g.epi == EPI_GATE) ? ts * g.gate[g.gate_map[d.y + ml]] : ts;
-        }
+    float mscale = 1.0f;
+    auto fetch_scale = [&](const int4& d) __attribute__((always_inline)) {
+        if constexpr (BFMT == LMOE_NVFP4) mscale = sload_f32(g.B_ts + d.x);
     };
-    fetch_scales(mdesc);
+    fetch_scale(mdesc);
     auto epilogue = [&](const int4& d, f32x16_t (&acc)[C::TM][C::TN]) __attribute__((always_inline)) {
         const int row0 = d.y, rows = d.z, n0 = d.w;
 #pragma unroll
@@ -553,7 +661,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
                     float v[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        v[i] = acc[tm][tn][q * 4 + i] * row_scale[tm];
+                        v[i] = acc[tm][tn][q * 4 + i] * mscale;
                         if (g.epi == EPI_RELU2) {
                             v[i] = fmaxf(v[i], 0.f);
                             v[i] *= v[i];
@@ -595,7 +703,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             epilogue(mdesc, acc);
             zero_acc<C>(acc);
             mdesc = fdesc;  // the fill side is already on the next item
-            fetch_scales(mdesc);
+            fetch_scale(mdesc);
         }
     }
 }
@@ -604,10 +712,38 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 // Launchers
 // ---------------------------------------------------------------------------
 
+static int persistent_grid();
+
+// Split-K factor for a dense GEMM whose tiles alone cannot fill the GPU:
+// aim for 4 tile-splits per CU, keep >= 4 K steps per split, and fit the
+// fp32 partials in the given workspace.
+static int splitk_factor(int tiles, int nk, int M, int ldp, size_t ws_bytes) {
+    const int cus = persistent_grid();
+    if (ws_bytes == 0 || tiles >= 2 * cus) return 1;
+    int splits = (4 * cus + tiles - 1) / tiles;
+    const int by_k = nk / 4 > 1 ? nk / 4 : 1;
+    if (splits > by_k) splits = by_k;
+    const size_t per = (size_t)M * ldp * sizeof(float);
+    const size_t by_ws = ws_bytes / per < 64 ? ws_bytes / per : 64;
+    if ((size_t)splits > by_ws) splits = (int)by_ws;
+    return splits > 1 ? splits : 1;
+}
+
 template <class C>
-static hipError_t run_dense(const DenseGemm& g, hipStream_t s) {
+static hipError_t run_dense(const DenseGemm& g, void* ws, size_t ws_bytes, hipStream_t s) {
     const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
-    LMOE_LAUNCH("dense_gemm", s, dense_gemm_kernel<C><<<tiles_m * tiles_n, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8));
+    const int nk = g.K[0] / C::BK + (g.nseg > 1 ? g.K[1] / C::BK : 0);
+    const int ldp = (g.N + 3) / 4 * 4;
+    const int splits = splitk_factor(tiles_m * tiles_n, nk, g.M, ldp, ws_bytes);
+    float* partial = splits > 1 ? (float*)ws : nullptr;
+    LMOE_LAUNCH("dense_gemm", s,
+                dense_gemm_kernel<C><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
+                                                                                  partial, ldp));
+    if (splits > 1) {
+        const int64_t threads = (int64_t)g.M * (ldp / 4);
+        LMOE_LAUNCH("splitk_reduce", s,
+                    splitk_reduce_kernel<<<(int)((threads + 255) / 256), 256, 0, s>>>(g, splits, partial, ldp));
+    }
     return hipGetLastError();
 }
 
@@ -624,14 +760,27 @@ static int persistent_grid() {
     return (cus + 7) / 8 * 8;
 }
 
+template <class C, int BFMT>
+static void launch_grouped_fmt(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
+    constexpr bool can_scalar = C::DMA && (Slots<C, C::BM>::RPI == 8 || Slots<C, C::BM>::RPI == 16);
+    const char* name = BFMT == LMOE_NVFP4 ? "grouped_gemm_nvfp4" : "grouped_gemm";
+    if (!g.a_row_map)
+        LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_NONE><<<grid, C::NT, 0, s>>>(g, nN));
+    else if (can_scalar && g.n_rows >= Slots<C, C::BM>::RPI)
+        LMOE_LAUNCH(name, s,
+                    grouped_gemm_kernel<C, BFMT, can_scalar ? GATHER_SCALAR : GATHER_LANE><<<grid, C::NT, 0, s>>>(g, nN));
+    else
+        LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_LANE><<<grid, C::NT, 0, s>>>(g, nN));
+}
+
 template <class C>
 static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
     const int nN = (g.N + C::BN - 1) / C::BN;
     const int grid = persistent_grid() * C::MINB;
     if (g.b_fmt == LMOE_NVFP4)
-        LMOE_LAUNCH("grouped_gemm_nvfp4", s, grouped_gemm_kernel<C, LMOE_NVFP4><<<grid, C::NT, 0, s>>>(g, nN));
+        launch_grouped_fmt<C, LMOE_NVFP4>(g, grid, nN, s);
     else
-        LMOE_LAUNCH("grouped_gemm", s, grouped_gemm_kernel<C, LMOE_BF16><<<grid, C::NT, 0, s>>>(g, nN));
+        launch_grouped_fmt<C, LMOE_BF16>(g, grid, nN, s);
     return hipGetLastError();
 }
 
@@ -639,17 +788,17 @@ static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
 // Dense: 256x256 tiles over 8 waves (2 per SIMD), each wave 64 x 128; the
 // fastest shape measured for the 8192-wide projections.  Decode-sized M
 // uses 64x64 tiles.
-hipError_t launch_dense_gemm_bf16(const DenseGemm& g, hipStream_t s) {
-    if (g.M <= 64) return run_dense<MfmaCfg<64, 64, 2, 2, true>>(g, s);
-    return run_dense<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, s);
+hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s) {
+    if (g.M <= 64) return run_dense<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2>>(g, splitk_ws, splitk_bytes, s);
+    return run_dense<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
 }
 
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to
 // 384) by 256 columns over 8 waves, each wave 96 x 64; few-row experts at
-// decode use 32-row tiles.
+// decode use 64-row tiles, 4 LDS stages, to keep weight streams in flight.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
     if (g.tt.bm == 192) return run_grouped<MfmaCfg<192, 256, 2, 4, true, 64, 2>>(g, s);
-    if (g.tt.bm == 32) return run_grouped<MfmaCfg<32, 128, 1, 4, true, 64, 2, 4>>(g, s);
+    if (g.tt.bm == 64) return run_grouped<MfmaCfg<64, 128, 2, 2, true, 64, 4, 2>>(g, s);
     return hipErrorInvalidValue;
 }
 #endif

@@ -14,7 +14,6 @@ enum Epi : int {
     EPI_STORE = 0,     // C = acc, stored in the activation dtype
     EPI_F32_BIAS = 1,  // C = acc (+ bias[col]), stored fp32
     EPI_RELU2 = 2,     // C = max(0, acc * scale)^2, activation dtype
-    EPI_GATE = 3,      // C = acc * scale * gate[gate_map[row]], activation dtype
 };
 
 // One contiguous range of output columns [n_begin, n_end) of a dense GEMM,
@@ -55,8 +54,9 @@ struct TileTable {
 };
 
 // Per-expert GEMM over sorted rows: for every tile (expert e, rows p),
-// C[p][n] = epi( sum_k A[arow(p)][k] * W_e[n][k] ), with
-// arow(p) = a_row_map ? a_row_map[p] / a_row_div : p.
+// C[p][n] = epi( scale_e * sum_k A[arow(p)][k] * W_e[n][k] ), with
+// arow(p) = a_row_map ? a_row_map[p] / a_row_div : p and scale_e the NVFP4
+// tensor scale (1 for dense weights).
 struct GroupedGemm {
     int N, K;
     TileTable tt;
@@ -64,14 +64,13 @@ struct GroupedGemm {
     int64_t lda;
     const int* a_row_map;
     int a_row_div;
+    int n_rows;  // sorted rows in total (T * k): bound of a_row_map
     int b_fmt;  // LMOE_F32 / LMOE_BF16 dense stack [E][N][K], or LMOE_NVFP4
     const void* B;
     const uint8_t* B_codes;   // [E][N][K/2]
     const uint8_t* B_scales;  // [E][N][K/16]
     const float* B_ts;        // [E]
-    int epi;                  // EPI_RELU2 or EPI_GATE
-    const float* gate;
-    const int* gate_map;
+    int epi;                  // EPI_RELU2 or EPI_STORE
     void* C;
     int64_t ldc;
 };
@@ -110,7 +109,7 @@ hipError_t launch_permute(const int32_t* idx, int64_t n_pairs, int E, int32_t* h
 // Tile table from offsets alone (staged entry point).
 hipError_t launch_build_tiles(const int32_t* offsets, int E, const TileTable& tt, hipStream_t s);
 
-hipError_t launch_combine(const void* Y, const int32_t* inv, int T, int k, int l, int act_dtype,
-                          void* c, hipStream_t s);
+hipError_t launch_combine(const void* Y, const int32_t* inv, const float* gate, int T, int k, int l,
+                          int act_dtype, void* c, hipStream_t s);
 
 }  // namespace lmoe

@@ -129,11 +129,13 @@ def test_staged_error_paths():
     assert L.lmoe_permute(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == B.LMOE_ERR_NULL
     assert L.lmoe_permute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == B.LMOE_ERR_WORKSPACE
     ex = B.Experts(FAKE, FAKE, None, None, None, None, None, None)
-    assert L.lmoe_experts_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.byref(ex), MIS, FAKE, need - 1,
+    assert L.lmoe_experts_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(ex), MIS, FAKE, need - 1,
                               None) == B.LMOE_ERR_ALIGN
-    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, need - 1,
+    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, None, FAKE, ctypes.byref(sh), FAKE, None, FAKE, FAKE,
+                             need - 1, None) == B.LMOE_ERR_NULL  # gate missing
+    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, need - 1,
                              None) == B.LMOE_ERR_SHAPE  # f_s > 0 without shared weights
-    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(sh), FAKE, None, FAKE, FAKE,
+    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, ctypes.byref(sh), FAKE, None, FAKE, FAKE,
                              need - 1, None) == B.LMOE_ERR_WORKSPACE
 
 

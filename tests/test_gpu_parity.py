@@ -107,8 +107,8 @@ def test_staged_entry_points_compose_to_forward():
         fused = B.forward(cfg, inp, workspace=ws)
         r = B.project_route(cfg, inp, ws)
         p = B.permute(cfg, r["idx"], ws)
-        Y = B.experts_ffn(cfg, inp, r["z"], r["gate"], p["offsets"], p["perm"], ws)
-        o = B.combine_up(cfg, inp, Y, p["inv"], r["hs"], ws, cfg.T)
+        Y = B.experts_ffn(cfg, inp, r["z"], p["offsets"], p["perm"], ws)
+        o = B.combine_up(cfg, inp, Y, p["inv"], r["gate"], r["hs"], ws, cfg.T)
         torch.cuda.synchronize()
         assert torch.equal(o["out"], fused), name
 
