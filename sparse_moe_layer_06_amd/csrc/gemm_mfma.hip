@@ -382,27 +382,27 @@ __global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g,
     zero_acc<C>(acc);
     kloop<C, C::DMA ? SA::N + SB::N : 0>(ke - kb, fill, land, ring, acc, wm, wn, lane);
 
-#pragma unroll
-    for (int tm = 0; tm < C::TM; ++tm) {
+    static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
+        constexpr int tm = decltype(tmc)::value;
         const int m = m0 + wm * C::WM + tm * 32 + (lane & 31);
-        if (m >= g.M) continue;
-#pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
+        if (m < g.M) {
+            static_for<C::TN * 4>([&](auto tqc) __attribute__((always_inline)) {
+                constexpr int tn = decltype(tqc)::value / 4, q = decltype(tqc)::value % 4;
                 const int n = n0 + wn * C::WN + tn * 32 + q * 8 + (lane >> 5) * 4;
-                if (n >= g.N) continue;
-                const float v[4] = {acc[tm][tn][q * 4 + 0], acc[tm][tn][q * 4 + 1], acc[tm][tn][q * 4 + 2],
-                                    acc[tm][tn][q * 4 + 3]};
-                if (partial) {
-                    // ldp is a multiple of 4, so the 4 columns are one aligned float4
-                    *reinterpret_cast<float4*>(partial + ((int64_t)split * g.M + m) * ldp + n) =
-                        make_float4(v[0], v[1], v[2], v[3]);
-                } else {
-                    dense_store4(g, m, n, v);
+                if (n < g.N) {
+                    const float v[4] = {acc[tm][tn][q * 4 + 0], acc[tm][tn][q * 4 + 1], acc[tm][tn][q * 4 + 2],
+                                        acc[tm][tn][q * 4 + 3]};
+                    if (partial) {
+                        // ldp is a multiple of 4, so the 4 columns are one aligned float4
+                        *reinterpret_cast<float4*>(partial + ((int64_t)split * g.M + m) * ldp + n) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
+                        dense_store4(g, m, n, v);
+                    }
                 }
-            }
-    }
+            });
+        }
+    });
 }
 
 // Sums the split-K partials in split order (deterministic) and applies the
@@ -646,33 +646,32 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     fetch_scale(mdesc);
     auto epilogue = [&](const int4& d, f32x16_t (&acc)[C::TM][C::TN]) __attribute__((always_inline)) {
         const int row0 = d.y, rows = d.z, n0 = d.w;
-#pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm) {
+        static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
+            constexpr int tm = decltype(tmc)::value;
             const int ml = wm * C::WM + tm * 32 + (lane & 31);
-            if (ml >= rows) continue;
-            const int p = row0 + ml;
-            uint16_t* crow = (uint16_t*)g.C + (int64_t)p * g.ldc;
-#pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
+            if (ml < rows) {
+                uint16_t* crow = (uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc;
+                static_for<C::TN * 4>([&](auto tqc) __attribute__((always_inline)) {
+                    constexpr int tn = decltype(tqc)::value / 4, q = decltype(tqc)::value % 4;
                     const int n = n0 + wn * C::WN + tn * 32 + q * 8 + (lane >> 5) * 4;
-                    if (n >= N) continue;
-                    float v[4];
+                    if (n < N) {
+                        float v[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        v[i] = acc[tm][tn][q * 4 + i] * mscale;
-                        if (g.epi == EPI_RELU2) {
-                            v[i] = fmaxf(v[i], 0.f);
-                            v[i] *= v[i];
+                        for (int i = 0; i < 4; ++i) {
+                            v[i] = acc[tm][tn][q * 4 + i] * mscale;
+                            if (g.epi == EPI_RELU2) {
+                                v[i] = fmaxf(v[i], 0.f);
+                                v[i] *= v[i];
+                            }
                         }
+                        uint2 o;
+                        o.x = pack_bf16x2(v[0], v[1]);
+                        o.y = pack_bf16x2(v[2], v[3]);
+                        *reinterpret_cast<uint2*>(crow + n) = o;
                     }
-                    uint2 o;
-                    o.x = pack_bf16x2(v[0], v[1]);
-                    o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(crow + n) = o;
-                }
-        }
+                });
+            }
+        });
     };
 
     constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS, AOFF = C::BM * C::CPR;
