@@ -32,6 +32,8 @@ hipError_t launch_grouped_gemm(const GroupedGemm& g, int act_dtype, hipStream_t 
     return act_dtype == LMOE_BF16 ? launch_grouped_gemm_bf16(g, s) : launch_grouped_gemm_f32(g, s);
 }
 
+// Rows per expert tile, which also picks the expert GEMM configuration:
+// 192-row tiles when experts see many rows, 64-row tiles otherwise.
 int grouped_bm(const lmoe_dims& d) {
     if (d.act_dtype == LMOE_F32) return 64;
     const double avg = (double)d.T * (double)d.k / (double)d.E;

@@ -5,11 +5,14 @@
 // Each token's k rows are gathered and summed in fixed j order in fp32, so
 // there are no atomics and the result is bit-identical run to run.  One
 // block per (token, 2048-column slab); each thread owns one 16-byte vector
-// of columns.  inv and gate entries are block-uniform loads.
+// of columns.  The rows are fetched kGroup at a time, all loads of a group
+// in flight together, then accumulated in j order.
 #include "device_common.hpp"
 #include "lmoe_internal.hpp"
 
 namespace lmoe {
+
+constexpr int kGroup = 8;
 
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ Y,
                                                            const int32_t* __restrict__ inv,
@@ -23,16 +26,28 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     const int32_t* row = inv + (int64_t)t * k;
     const float* grow = gate + (int64_t)t * k;
-    for (int j = 0; j < k; ++j) {
-        const int p = row[j];
-        if (p < 0) continue;  // pair left out by the permutation (invalid expert id)
-        const float gj = grow[j];
-        const uint4 v = *reinterpret_cast<const uint4*>(Y + (int64_t)p * l + col);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        int p[kGroup];
+        float gj[kGroup];
+        uint4 v[kGroup];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = fmaf(gj, __uint_as_float(w[i] << 16), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(gj, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        for (int i = 0; i < kGroup; ++i) {
+            // p < 0: pair left out by the permutation (invalid expert id)
+            p[i] = (j0 + i < k) ? row[j0 + i] : -1;
+            gj[i] = (j0 + i < k) ? grow[j0 + i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i)
+            v[i] = (p[i] >= 0) ? *reinterpret_cast<const uint4*>(Y + (int64_t)p[i] * l + col) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            if (p[i] < 0) continue;
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(gj[i], __uint_as_float(w[q] << 16), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(gj[i], __uint_as_float(w[q] & 0xFFFF0000u), acc[2 * q + 1]);
+            }
         }
     }
     uint4 o;
@@ -52,15 +67,28 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
     if (col >= l) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     const int32_t* row = inv + (int64_t)t * k;
-    for (int j = 0; j < k; ++j) {
-        const int p = row[j];
-        if (p < 0) continue;
-        const float gj = gate[(int64_t)t * k + j];
-        const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)p * l + col);
-        acc.x = fmaf(gj, v.x, acc.x);
-        acc.y = fmaf(gj, v.y, acc.y);
-        acc.z = fmaf(gj, v.z, acc.z);
-        acc.w = fmaf(gj, v.w, acc.w);
+    const float* grow = gate + (int64_t)t * k;
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+        int p[kGroup];
+        float gj[kGroup];
+        float4 v[kGroup];
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            p[i] = (j0 + i < k) ? row[j0 + i] : -1;
+            gj[i] = (j0 + i < k) ? grow[j0 + i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i)
+            v[i] = (p[i] >= 0) ? *reinterpret_cast<const float4*>(Y + (int64_t)p[i] * l + col)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            if (p[i] < 0) continue;
+            acc.x = fmaf(gj[i], v[i].x, acc.x);
+            acc.y = fmaf(gj[i], v[i].y, acc.y);
+            acc.z = fmaf(gj[i], v[i].z, acc.z);
+            acc.w = fmaf(gj[i], v[i].w, acc.w);
+        }
     }
     *reinterpret_cast<float4*>(c + (int64_t)t * l + col) = acc;
 }

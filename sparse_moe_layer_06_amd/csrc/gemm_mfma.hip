@@ -32,10 +32,14 @@
 
 namespace lmoe {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool DMA_, int BK_ = 64, int STAGES_ = 2, int MINB_ = 1>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool DMA_, int BK_ = 64, int STAGES_ = 2, int MINB_ = 1,
+          bool B_NT_ = false>
 struct MfmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
     static constexpr int MINB = MINB_;  // blocks per CU the register budget is sized for
+    // Weights fetched with the non-temporal hint: for weight streams read once
+    // per call (few rows per expert); it costs L2 reuse when tiles share weights.
+    static constexpr bool B_NT = B_NT_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = 64 * NW;
@@ -90,9 +94,11 @@ struct Slots {
 
 // One LDS-DMA instruction: 16 bytes per lane from `src` into LDS starting at
 // the wave-uniform `dst` (lane i lands at dst + 16 i).
+// AUX is the instruction's cache-policy field; 2 sets the non-temporal bit.
+template <int AUX = 0>
 __device__ __forceinline__ void dma16(const void* src, u32x4_t* dst) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, AUX);
 }
 
 // Scalar-memory loads of wave-uniform data.  They complete on lgkmcnt, which
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g,
                 if (SA::active(j, tid)) dma16(a_ptr[j] + kk, SA::dst(As, wave, j));
 #pragma unroll
             for (int j = 0; j < SB::N; ++j)
-                if (SB::active(j, tid)) dma16(b_ptr[j] + kk, SB::dst(Bs, wave, j));
+                if (SB::active(j, tid)) dma16<C::B_NT ? 2 : 0>(b_ptr[j] + kk, SB::dst(Bs, wave, j));
         } else {
 #pragma unroll
             for (int j = 0; j < SA::N; ++j) ra[j] = *reinterpret_cast<const u32x4_t*>(a_ptr[j] + kk);
@@ -607,7 +613,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         } else if constexpr (B_DMA) {
 #pragma unroll
             for (int j = 0; j < SB::N; ++j)
-                if (SB::active(j, tid)) dma16(b_ptr[j] + kk, SB::dst(Bs, wave, j));
+                if (SB::active(j, tid)) dma16<C::B_NT ? 2 : 0>(b_ptr[j] + kk, SB::dst(Bs, wave, j));
         } else {
 #pragma unroll
             for (int j = 0; j < SB::N; ++j) rb[j] = *reinterpret_cast<const u32x4_t*>(b_ptr[j] + kk);
@@ -714,12 +720,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 static int persistent_grid();
 
 // Split-K factor for a dense GEMM whose tiles alone cannot fill the GPU:
-// aim for 4 tile-splits per CU, keep >= 4 K steps per split, and fit the
-// fp32 partials in the given workspace.
-static int splitk_factor(int tiles, int nk, int M, int ldp, size_t ws_bytes) {
+// aim for as many tile-splits as blocks fit on the GPU at once (more splits
+// only add fp32 partial traffic), keep >= 4 K steps per split, and fit the
+// partials in the given workspace.
+static int splitk_factor(int tiles, int nk, int M, int ldp, size_t ws_bytes, int blocks_per_cu) {
     const int cus = persistent_grid();
     if (ws_bytes == 0 || tiles >= 2 * cus) return 1;
-    int splits = (4 * cus + tiles - 1) / tiles;
+    int splits = (blocks_per_cu * cus + tiles - 1) / tiles;
     const int by_k = nk / 4 > 1 ? nk / 4 : 1;
     if (splits > by_k) splits = by_k;
     const size_t per = (size_t)M * ldp * sizeof(float);
@@ -733,7 +740,7 @@ static hipError_t run_dense(const DenseGemm& g, void* ws, size_t ws_bytes, hipSt
     const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
     const int nk = g.K[0] / C::BK + (g.nseg > 1 ? g.K[1] / C::BK : 0);
     const int ldp = (g.N + 3) / 4 * 4;
-    const int splits = splitk_factor(tiles_m * tiles_n, nk, g.M, ldp, ws_bytes);
+    const int splits = splitk_factor(tiles_m * tiles_n, nk, g.M, ldp, ws_bytes, C::MINB);
     float* partial = splits > 1 ? (float*)ws : nullptr;
     LMOE_LAUNCH("dense_gemm", s,
                 dense_gemm_kernel<C><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
@@ -761,11 +768,12 @@ static int persistent_grid() {
 
 template <class C, int BFMT>
 static void launch_grouped_fmt(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
-    constexpr bool can_scalar = C::DMA && (Slots<C, C::BM>::RPI == 8 || Slots<C, C::BM>::RPI == 16);
+    constexpr int RPI = Slots<C, C::BM>::RPI;
+    constexpr bool can_scalar = C::DMA && (RPI == 8 || RPI == 16);
     const char* name = BFMT == LMOE_NVFP4 ? "grouped_gemm_nvfp4" : "grouped_gemm";
     if (!g.a_row_map)
         LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_NONE><<<grid, C::NT, 0, s>>>(g, nN));
-    else if (can_scalar && g.n_rows >= Slots<C, C::BM>::RPI)
+    else if (can_scalar && g.n_rows >= RPI)
         LMOE_LAUNCH(name, s,
                     grouped_gemm_kernel<C, BFMT, can_scalar ? GATHER_SCALAR : GATHER_LANE><<<grid, C::NT, 0, s>>>(g, nN));
     else
@@ -788,16 +796,18 @@ static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
 // fastest shape measured for the 8192-wide projections.  Decode-sized M
 // uses 64x64 tiles.
 hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s) {
-    if (g.M <= 64) return run_dense<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2>>(g, splitk_ws, splitk_bytes, s);
+    if (g.M <= 64)  // weight streaming: 64x64 tiles, 4 stages, 2 blocks per CU, split-K
+        return run_dense<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, splitk_ws, splitk_bytes, s);
     return run_dense<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
 }
 
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to
-// 384) by 256 columns over 8 waves, each wave 96 x 64; few-row experts at
-// decode use 64-row tiles, 4 LDS stages, to keep weight streams in flight.
+// 384) by 256 columns over 8 waves, each wave 96 x 64.  Few-row experts
+// (decode) stream their weights: 64x64 tiles, 4 LDS stages, two blocks per
+// CU, and the non-temporal hint on the weights, which each call reads once.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
     if (g.tt.bm == 192) return run_grouped<MfmaCfg<192, 256, 2, 4, true, 64, 2>>(g, s);
-    if (g.tt.bm == 64) return run_grouped<MfmaCfg<64, 128, 2, 2, true, 64, 4, 2>>(g, s);
+    if (g.tt.bm == 64) return run_grouped<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, s);
     return hipErrorInvalidValue;
 }
 #endif

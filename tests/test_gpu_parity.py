@@ -36,6 +36,12 @@ SMALL = {
                           experts="bf16"),
     "k1_bf16": TINY.with_(name="k1_bf16", T=128, d=256, l=64, E=8, k=1, f=128, act="bf16", experts="bf16"),
     "kE_bf16": TINY.with_(name="kE_bf16", T=64, d=256, l=64, E=5, k=5, f=64, act="bf16", experts="bf16"),
+    # few rows per expert: the weight-streaming expert kernel (16-row tiles),
+    # K rings of 4/2 steps (l=128, f=192) and of 16 steps (l=f=512)
+    "stream_ragged": TINY.with_(name="stream_ragged", T=37, d=512, l=128, E=32, k=5, f=192, f_s=64,
+                                act="bf16", experts="bf16"),
+    "stream_deepK": TINY.with_(name="stream_deepK", T=20, d=2048, l=512, E=16, k=4, f=512, f_s=0,
+                               act="bf16", experts="bf16"),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
