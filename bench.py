@@ -174,6 +174,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device-to-device 3 times (scale for HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer is benchmarked on a single MI355X "
@@ -181,6 +183,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        # A plain copy of known size: under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+        # it gives the factor between those counters and bytes moved.
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
 
     from sparse_moe_layer_06_amd import binding as B
     from sparse_moe_layer_06_amd import synth
