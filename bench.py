@@ -14,9 +14,11 @@ Prints one JSON line:
                 the launch stream, against the bf16 dense MFMA peak
   decode        the weight-streaming decode layer (T=64, skewed routing):
                 tokens/s and algorithmic HBM bytes / time against 8 TB/s
+  other_workloads  the NVFP4-expert prefill layer and the mid-size layer:
+                tokens/s, layer TFLOP/s and the grouped GEMM's rate
   cpu_baseline  the CPU oracle on a bounded token sample of the same workload
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-extra]
 """
 from __future__ import annotations
 
@@ -135,6 +137,24 @@ def decode(cfg, steps, torch, B, synth):
                 "1 GiB buffer read between steps (cache eviction)" % steps)
 
 
+def secondary(name, steps, warmup, torch, B, synth):
+    """The other MFMA-bound workloads (same metric, reported beside the headline)."""
+    cfg = synth.CONFIGS[name]
+    inp, out, ms, _, kernels = prefill(cfg, steps, warmup, torch, B, synth)
+    gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
+    g = kernels.get(gname)
+    res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
+                        f"{cfg.experts} experts", ms_per_step=ms, tokens_per_s=cfg.T / (ms * 1e-3),
+               layer_tflops=cfg.flops / (ms * 1e-3) / 1e12, layer_mfma_frac=cfg.flops / (ms * 1e-3) / PEAK_BF16_FLOPS)
+    if g:
+        ach = 2.0 * cfg.T * cfg.k * cfg.l * cfg.f / (g["avg_ms"] * 1e-3)
+        res["grouped"] = dict(kernel=gname, avg_launch_ms=g["avg_ms"], achieved_tflops=ach / 1e12,
+                              mfma_frac=ach / PEAK_BF16_FLOPS)
+    del inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, inp, n_tokens, synth):
     import numpy as np
     from oracle import latentmoe_oracle as O
@@ -174,6 +194,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the mid_bf16 and prefill_nvfp4 lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (scale for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -243,6 +264,9 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = decode(synth.CONFIGS["decode_bf16_zipf"], args.decode_steps, torch, B, synth)
+    if not args.no_extra:
+        result["other_workloads"] = {n: secondary(n, max(args.steps // 2, 3), args.warmup, torch, B, synth)
+                                     for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload}
     if not args.no_cpu:
         log("bench: cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens, synth)

@@ -172,23 +172,41 @@ __device__ __forceinline__ void wait_tiles_barrier(int ahead) {
 // is issued as mfma(B-fragment, A-fragment): m = lane % 32,
 // n = 8 * (r / 4) + 4 * (lane / 32) + r % 4.
 template <class C>
+// The fragments of 16-wide K sub-step ks + 1 are read into the second of two
+// register sets while the MFMAs of sub-step ks run, so each LDS read has a
+// whole MFMA group to land.  Each sub-step first waits for the reads issued
+// one group earlier (lgkmcnt(0) while only those are in flight: they have
+// landed by then), then issues the next reads, then its MFMAs; the compiler
+// would otherwise wait for all reads right before the MFMAs, including the
+// ones just issued.
 __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u32x4_t* __restrict__ Bs,
                                          f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
-#pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
+    constexpr int KS = C::BK / 16;
+    bf16x8_t af[2][C::TM], bfr[2][C::TN];
+    auto read = [&](int ks, int b) __attribute__((always_inline)) {
         const int ch = ks * 2 + (lane >> 5);
-        bf16x8_t af[C::TM], bfr[C::TN];
 #pragma unroll
         for (int tm = 0; tm < C::TM; ++tm)
-            af[tm] = as_bf16x8(As[lds_idx<C>(wm * C::WM + tm * 32 + (lane & 31), ch)]);
+            af[b][tm] = as_bf16x8(As[lds_idx<C>(wm * C::WM + tm * 32 + (lane & 31), ch)]);
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn)
-            bfr[tn] = as_bf16x8(Bs[lds_idx<C>(wn * C::WN + tn * 32 + (lane & 31), ch)]);
+            bfr[b][tn] = as_bf16x8(Bs[lds_idx<C>(wn * C::WN + tn * 32 + (lane & 31), ch)]);
+    };
+    read(0, 0);
+    static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(kc)::value, b = ks & 1;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks + 1 < KS) read(ks + 1, b ^ 1);
+        // keep the reads of the next sub-step ahead of this sub-step's MFMAs
+        // (the scheduler would otherwise sink them to their use)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = mfma32x32x16(bfr[tn], af[tm], acc[tm][tn]);
-    }
+            for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = mfma32x32x16(bfr[b][tn], af[b][tm], acc[tm][tn]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 // K loop over nk tiles through a ring of C::STAGES LDS stages.
@@ -438,42 +456,31 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseGemm g, int spl
 // Grouped (per-expert) GEMM
 // ---------------------------------------------------------------------------
 
-// 8 E2M1 codes (one 32-bit word, element i in bits 4i..4i+3) times an E4M3
-// block scale -> 8 bf16.  E2M1: sign bit 3, exponent bits 2-1 (bias 1),
-// mantissa bit 0, so the magnitudes are {0, .5, 1, 1.5, 2, 3, 4, 6}; the
-// product with an E4M3 value has at most 6 significant bits and is exact in
-// bf16 (Nemotron 3 overview, section 3.1.1: E2M1 elements, 16-element
-// micro-blocks, E4M3 block scale).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+// NVFP4 weight decode (Nemotron 3 overview, section 3.1.1: E2M1 elements,
+// 16-element micro-blocks, E4M3 block scale).  An E4M3 scale byte is split
+// into a power of two pw and a factor mt: normal 2^(e-7) * (1 + m/8),
+// subnormal 2^-6 * (m/8), the sign on mt (0x7F / 0xFF is NaN).
+__device__ __forceinline__ void e4m3_parts(uint32_t b, float& pw, float& mt) {
     const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    float v = (e == 0) ? (float)m * 0.001953125f  // 2^-9
-                       : __uint_as_float(((e + 120u) << 23) | (m << 20));
-    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
-    return (b & 0x80u) ? -v : v;
+    pw = __uint_as_float((e == 0u ? 121u : e + 120u) << 23);
+    mt = (e == 0u ? 0.f : 1.f) + (float)m * 0.125f;
+    if (e == 15u && m == 7u) mt = __uint_as_float(0x7FC00000u);
+    if (b & 0x80u) mt = -mt;
 }
 
-__device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float scale) {
-    // twice the magnitude of each 3-bit code, 4 bits per entry
-    constexpr uint32_t kMag2 = 0xC8643210u;
-    const float hs = 0.5f * scale;
-    uint32_t out[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t h[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t c = (codes >> (8 * i + 4 * j)) & 15u;
-            const float mag = (float)((kMag2 >> ((c & 7u) * 4u)) & 15u) * hs;
-            const uint32_t bits = __float_as_uint(mag) ^ ((c & 8u) << 28);
-            h[j] = bits >> 16;  // exact: no rounding needed
-        }
-        out[i] = h[0] | (h[1] << 16);
-    }
+// 8 E2M1 codes (one 32-bit word, element i in bits 4i..4i+3, so byte j holds
+// elements 2j and 2j+1) -> 8 bf16.  The hardware conversion scales by the
+// power of two exactly; the product with mt has at most 5 significant bits
+// (an E2M1 value has 2, an E4M3 factor 4), so it is exact in fp32 and its
+// upper half is the exact bf16.
+__device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float pw, float mt) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
     u32x4_t r;
-    r.x = out[0];
-    r.y = out[1];
-    r.z = out[2];
-    r.w = out[3];
+    static_for<4>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, pw, j);
+        r[j] = __builtin_amdgcn_perm(__float_as_uint(v.y * mt), __float_as_uint(v.x * mt), 0x07060302u);
+    });
     return r;
 }
 
@@ -524,14 +531,19 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     constexpr bool B_DMA = C::DMA && BFMT != LMOE_NVFP4;
     using SA = Slots<C, C::BM>;
     using SB = Slots<C, C::BN>;
-    using C_REG = MfmaCfg<C::BM, C::BN, C::WAVES_M, C::WAVES_N, false, C::BK, C::STAGES, C::MINB>;
-    using SBR = Slots<C_REG, C::BN>;  // register slots for the NVFP4 weights
+    // NVFP4 weights: each weight row's K step is split over LPR lanes, EPL
+    // elements (EPL/2 code bytes, EPL/16 scale bytes) per lane, loaded into
+    // registers and decoded into the LDS tile.
+    constexpr int LPR = C::NT / C::BN, EPL = C::BK / (LPR > 0 ? LPR : 1);
+    static_assert(BFMT != LMOE_NVFP4 || (C::NT % C::BN == 0 && (LPR == 2 || LPR == 4) && C::BK == 64),
+                  "NVFP4 tiles: 2 or 4 lanes per weight row, K step 64");
+    typedef uint32_t code_words_t __attribute__((ext_vector_type(EPL >= 16 ? EPL / 8 : 2)));
 
     // ---- fill side: pointers of the item whose K steps are being issued
     const uint16_t* a_ptr[SA::N];
     const uint16_t* b_ptr[BFMT == LMOE_NVFP4 ? 1 : SB::N];
-    const uint32_t* c_ptr[BFMT == LMOE_NVFP4 ? SBR::N : 1];
-    const uint8_t* s_ptr[BFMT == LMOE_NVFP4 ? SBR::N : 1];
+    const uint8_t* c_ptr = nullptr;  // NVFP4: this lane's codes and scales
+    const uint8_t* s_ptr = nullptr;
     int4 fdesc = load_item(0);
     int4 fnext = load_item(1);
     int f_item = 0, f_kt = 0;
@@ -573,13 +585,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             a_ptr[j] = (const uint16_t*)g.A + (int64_t)ar * g.lda + SA::lchunk(j, tid) * 8;
         }
         if constexpr (BFMT == LMOE_NVFP4) {
-#pragma unroll
-            for (int j = 0; j < SBR::N; ++j) {
-                const int64_t n = (int64_t)e * N + min(n0 + SBR::row(j, tid), N - 1);
-                const int ch = SBR::lchunk(j, tid);
-                c_ptr[j] = (const uint32_t*)(g.B_codes + n * (K / 2)) + ch;
-                s_ptr[j] = g.B_scales + n * (K / 16) + (ch >> 1);
-            }
+            const int64_t n = (int64_t)e * N + min(n0 + tid / LPR, N - 1);
+            c_ptr = g.B_codes + n * (K / 2) + (tid % LPR) * (EPL / 2);
+            s_ptr = g.B_scales + n * (K / 16) + (tid % LPR) * (EPL / 16);
         } else {
 #pragma unroll
             for (int j = 0; j < SB::N; ++j) {
@@ -591,7 +599,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     setup(fdesc);
 
     u32x4_t ra[C::DMA ? 1 : SA::N], rb[B_DMA || BFMT == LMOE_NVFP4 ? 1 : SB::N];
-    uint32_t rc[BFMT == LMOE_NVFP4 ? SBR::N : 1], rs[BFMT == LMOE_NVFP4 ? SBR::N : 1];
+    code_words_t rc;  // NVFP4: EPL codes
+    uint32_t rs = 0;  // NVFP4: EPL/16 scale bytes
     // issues the next K step of the fill item into stage (As, Bs)
     auto fill_next = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
         if (f_kt == nk) {  // next item: its descriptor was fetched one item ahead
@@ -605,11 +614,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         const int kk = kt * C::BK;
         if constexpr (BFMT == LMOE_NVFP4) {
             // register loads first, so waiting for them does not wait for the DMA
-#pragma unroll
-            for (int j = 0; j < SBR::N; ++j) {
-                rc[j] = c_ptr[j][kt * C::CPR];        // K/2 code bytes per row per K tile
-                rs[j] = s_ptr[j][kt * (C::BK / 16)];  // one scale byte per 16 elements
-            }
+            rc = *reinterpret_cast<const code_words_t*>(c_ptr + kt * (C::BK / 2));
+            if constexpr (EPL == 32)
+                rs = *reinterpret_cast<const uint16_t*>(s_ptr + kt * (C::BK / 16));
+            else
+                rs = s_ptr[kt * (C::BK / 16)];
         } else if constexpr (B_DMA) {
 #pragma unroll
             for (int j = 0; j < SB::N; ++j)
@@ -633,9 +642,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             for (int j = 0; j < SA::N; ++j) As[lds_idx<C>(SA::row(j, tid), SA::lchunk(j, tid))] = ra[j];
         }
         if constexpr (BFMT == LMOE_NVFP4) {
-#pragma unroll
-            for (int j = 0; j < SBR::N; ++j)
-                Bs[lds_idx<C>(SBR::row(j, tid), SBR::lchunk(j, tid))] = decode_e2m1x8(rc[j], e4m3_to_f32(rs[j]));
+            static_for<EPL / 8>([&](auto wc) __attribute__((always_inline)) {
+                constexpr int w = decltype(wc)::value;  // 8 elements; scale block w / 2
+                float pw, mt;
+                e4m3_parts((rs >> (8 * (w / 2))) & 0xFFu, pw, mt);
+                Bs[lds_idx<C>(tid / LPR, (tid % LPR) * (EPL / 8) + w)] = decode_e2m1x8(rc[w], pw, mt);
+            });
         } else if constexpr (!B_DMA) {
 #pragma unroll
             for (int j = 0; j < SB::N; ++j) Bs[lds_idx<C>(SB::row(j, tid), SB::lchunk(j, tid))] = rb[j];
