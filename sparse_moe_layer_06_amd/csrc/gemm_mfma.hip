@@ -804,12 +804,19 @@ static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
 }
 
 #ifndef LMOE_GEMM_VARIANTS
-// Dense: 256x256 tiles over 8 waves (2 per SIMD), each wave 64 x 128; the
-// fastest shape measured for the 8192-wide projections.  Decode-sized M
-// uses 64x64 tiles.
+// Dense: 256x256 tiles over 8 waves (2 per SIMD), each wave 64 x 128, the
+// fastest shape measured for the 8192-wide projections; 256x192 where that
+// fills the GPU better (narrow N, few M tiles).  Decode-sized M uses 64x64
+// tiles with split-K.
 hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s) {
     if (g.M <= 64)  // weight streaming: 64x64 tiles, 4 stages, 2 blocks per CU, split-K
         return run_dense<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, splitk_ws, splitk_bytes, s);
+    // 256-wide tiles unless 192-wide ones leave clearly fewer idle CUs: the
+    // cost of a shape is its rounds of tiles over the CUs times the tile width.
+    const int cus = persistent_grid(), tiles_m = (g.M + 255) / 256;
+    const double r256 = (double)((tiles_m * ((g.N + 255) / 256) + cus - 1) / cus);
+    const double r192 = (double)((tiles_m * ((g.N + 191) / 192) + cus - 1) / cus) * 0.75;
+    if (r192 < 0.85 * r256) return run_dense<MfmaCfg<256, 192, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
     return run_dense<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
 }
 

@@ -42,6 +42,10 @@ SMALL = {
                                 act="bf16", experts="bf16"),
     "stream_deepK": TINY.with_(name="stream_deepK", T=20, d=2048, l=512, E=16, k=4, f=512, f_s=0,
                                act="bf16", experts="bf16"),
+    # top-k beyond one register slot per lane: k = 100 of E = 256, and E = 1024
+    "k100_E256": TINY.with_(name="k100_E256", T=16, d=256, l=64, E=256, k=100, f=64, act="bf16",
+                            experts="bf16"),
+    "E1024": TINY.with_(name="E1024", T=32, d=256, l=64, E=1024, k=8, f=64, act="bf16", experts="bf16"),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
@@ -143,6 +147,24 @@ def test_invalid_expert_ids_are_left_out_of_the_permutation():
     valid = idx.numpy().reshape(-1)
     valid = valid[(valid >= 0) & (valid < cfg.E)]
     assert np.array_equal(p["counts"].cpu().numpy(), np.bincount(valid, minlength=cfg.E))
+
+
+@pytest.mark.parametrize("T,k,E", [(4096, 8, 256), (4097, 8, 256), (300, 22, 1024), (1, 1, 1), (2048, 1, 7)])
+def test_permutation_matches_oracle_on_both_paths(T, k, E):
+    # 4096 x 8 = 32768 pairs is the largest single-block permutation; 4097 x 8
+    # takes the histogram / chunk-scan / scatter kernels.
+    cfg = TINY.with_(name="perm", T=T, k=k, E=E, act="bf16", experts="bf16")
+    log(f"case permutation T={T} k={k} E={E}")
+    ws = B.alloc_workspace(cfg)
+    g = torch.Generator().manual_seed(T * 31 + E)
+    idx = torch.argsort(torch.rand(T, E, generator=g), dim=1)[:, :k].to(torch.int32).contiguous()
+    p = B.permute(cfg, idx.cuda(), ws)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = O.permutation(idx.numpy(), E)
+    assert np.array_equal(p["counts"].cpu().numpy(), rc)
+    assert np.array_equal(p["offsets"].cpu().numpy(), ro)
+    assert np.array_equal(p["perm"].cpu().numpy(), rp)
+    assert np.array_equal(p["inv"].cpu().numpy(), ri)
 
 
 # ---- full-size workloads --------------------------------------------------
