@@ -168,20 +168,21 @@ __device__ __forceinline__ void wait_tiles_barrier(int ahead) {
     asm volatile("" ::: "memory");
 }
 
-// Output (m, n) of register r of the 32x32 tile for this lane, when the MFMA
-// is issued as mfma(B-fragment, A-fragment): m = lane % 32,
-// n = 8 * (r / 4) + 4 * (lane / 32) + r % 4.
-template <class C>
+// One LDS tile of MFMAs for this wave.  Output (m, n) of register r of each
+// 32x32 block for this lane, when the MFMA is issued as mfma(B-fragment,
+// A-fragment): m = lane % 32, n = 8 * (r / 4) + 4 * (lane / 32) + r % 4.
+//
 // The fragments of 16-wide K sub-step ks + 1 are read into the second of two
-// register sets while the MFMAs of sub-step ks run, so each LDS read has a
-// whole MFMA group to land.  Each sub-step first waits for the reads issued
-// one group earlier (lgkmcnt(0) while only those are in flight: they have
-// landed by then), then issues the next reads, then its MFMAs; the compiler
-// would otherwise wait for all reads right before the MFMAs, including the
-// ones just issued.
+// register sets while the MFMAs of sub-step ks run, one read issued after
+// each MFMA, so each read has most of an MFMA group to land and the MFMA pipe
+// is fed while the reads go out.  Each sub-step first waits for the reads
+// issued one group earlier (lgkmcnt(0) while only those are in flight: they
+// have landed by then); the compiler would otherwise wait for all reads
+// right before the MFMAs, including the ones just issued.
+template <class C>
 __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u32x4_t* __restrict__ Bs,
                                          f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
-    constexpr int KS = C::BK / 16;
+    constexpr int KS = C::BK / 16, NM = C::TM * C::TN, NR = C::TM + C::TN;
     bf16x8_t af[2][C::TM], bfr[2][C::TN];
     auto read = [&](int ks, int b) __attribute__((always_inline)) {
         const int ch = ks * 2 + (lane >> 5);
@@ -198,13 +199,17 @@ __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt unconstrained
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ks + 1 < KS) read(ks + 1, b ^ 1);
-        // keep the reads of the next sub-step ahead of this sub-step's MFMAs
-        // (the scheduler would otherwise sink them to their use)
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = mfma32x32x16(bfr[b][tn], af[b][tm], acc[tm][tn]);
+        if constexpr (ks + 1 < KS) {  // issue order: MFMA m, then its share of the reads
+            static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value, r = (m + 1) * NR / NM - m * NR / NM;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS read
+            });
+        }
         __builtin_amdgcn_sched_barrier(0);
     });
 }
