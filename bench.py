@@ -6,6 +6,8 @@ permutation, both expert GEMMs, combine, up-projection + shared expert) over
 one batch of seeded synthetic inputs already resident in HBM.  The default
 workload is the Ultra-shape prefill layer: T=8192 tokens, d=8192, l=2048,
 E=512, top-22, f=2048, shared expert 8192, bf16 with fp32 accumulation.
+bf16 expert weights are packed once into the tiled layout before timing
+(lmoe_pack_expert_weights; --expert-layout rowmajor skips that).
 
 Prints one JSON line:
   value         whole-layer tokens/s over the K timed steps
@@ -78,12 +80,20 @@ def time_steps(call, steps, torch):
     return a.elapsed_time(b) / steps, wall
 
 
-def prefill(cfg, steps, warmup, torch, B, synth):
+def prepared(cfg, inp, layout, B):
+    """The config and inputs the GPU runs: bf16 expert stacks packed once into
+    the tiled layout (weight preparation, outside every timed region)."""
+    if layout == "tiled" and cfg.experts == "bf16":
+        return B.pack_experts(cfg, inp)
+    return cfg, inp
+
+
+def prefill(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     log(f"bench: generating inputs {cfg.name}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
     ws = B.alloc_workspace(cfg)
-    call = B.Call(cfg, inp, out, ws)
+    call = B.Call(*prepared(cfg, inp, layout, B), out, ws)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -103,13 +113,13 @@ def prefill(cfg, steps, warmup, torch, B, synth):
     return inp, out, ms, wall, kernels
 
 
-def decode(cfg, steps, torch, B, synth):
+def decode(cfg, steps, torch, B, synth, layout="tiled"):
     log(f"bench: generating inputs {cfg.name}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
     ws = B.alloc_workspace(cfg)
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    call = B.Call(cfg, inp, out, ws, debug=dict(counts=counts))
+    call = B.Call(*prepared(cfg, inp, layout, B), out, ws, debug=dict(counts=counts))
     # Reading 1 GiB between steps evicts L2 and the 256 MB Infinity Cache; a read
     # leaves only clean lines, so the timed step pays no write-back of flush data.
     flush = torch.ones(1 << 29, dtype=torch.float16, device="cuda")
@@ -131,16 +141,17 @@ def decode(cfg, steps, torch, B, synth):
     l, f, d, E, T = cfg.l, cfg.f, cfg.d, cfg.E, cfg.T
     bytes_alg = touched * 2 * l * f * 2 + (2 * d * l + d * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
-    return dict(workload=f"{cfg.name} T={T} d={d} l={l} E={E} k={cfg.k} f={f}", tokens_per_s=T / (ms * 1e-3),
+    return dict(workload=f"{cfg.name} T={T} d={d} l={l} E={E} k={cfg.k} f={f}, {cfg.experts} experts "
+                         f"({layout if cfg.experts == 'bf16' else 'as stored'})", tokens_per_s=T / (ms * 1e-3),
                 ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
                 hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
                 "1 GiB buffer read between steps (cache eviction)" % steps)
 
 
-def secondary(name, steps, warmup, torch, B, synth):
+def secondary(name, steps, warmup, torch, B, synth, layout="tiled"):
     """The other MFMA-bound workloads (same metric, reported beside the headline)."""
     cfg = synth.CONFIGS[name]
-    inp, out, ms, _, kernels = prefill(cfg, steps, warmup, torch, B, synth)
+    inp, out, ms, _, kernels = prefill(cfg, steps, warmup, torch, B, synth, layout)
     gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
     g = kernels.get(gname)
     res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
@@ -195,6 +206,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the mid_bf16 and prefill_nvfp4 lines")
+    ap.add_argument("--expert-layout", choices=("tiled", "rowmajor"), default="tiled",
+                    help="bf16 expert weights as packed by lmoe_pack_expert_weights (default) or row-major")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (scale for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -222,7 +235,7 @@ def main():
 
     B.lib()
     cfg = synth.CONFIGS[args.workload]
-    inp, out, ms, wall, kernels = prefill(cfg, args.steps, args.warmup, torch, B, synth)
+    inp, out, ms, wall, kernels = prefill(cfg, args.steps, args.warmup, torch, B, synth, args.expert_layout)
     tokens_per_s = cfg.T / (ms * 1e-3)
     layer_tflops = cfg.flops / (ms * 1e-3) / 1e12
 
@@ -254,7 +267,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: LatentMoE layer T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} "
-                               f"k={cfg.k} f={cfg.f} f_s={cfg.f_s}, {cfg.experts} experts, seed 0",
+                               f"k={cfg.k} f={cfg.f} f_s={cfg.f_s}, {cfg.experts} experts"
+                               f"{' (' + args.expert_layout + ' layout)' if cfg.experts == 'bf16' else ''}, seed 0",
                    "global_batch": cfg.T, "parallelism": "single GPU"},
         "layer_tflops": layer_tflops,
         "layer_mfma_frac": layer_tflops * 1e12 / PEAK_BF16_FLOPS,
@@ -263,9 +277,11 @@ def main():
         "kernels": kernels,
     }
     if not args.no_decode:
-        result["decode"] = decode(synth.CONFIGS["decode_bf16_zipf"], args.decode_steps, torch, B, synth)
+        result["decode"] = decode(synth.CONFIGS["decode_bf16_zipf"], args.decode_steps, torch, B, synth,
+                                  args.expert_layout)
     if not args.no_extra:
-        result["other_workloads"] = {n: secondary(n, max(args.steps // 2, 3), args.warmup, torch, B, synth)
+        result["other_workloads"] = {n: secondary(n, max(args.steps // 2, 3), args.warmup, torch, B, synth,
+                                                  args.expert_layout)
                                      for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload}
     if not args.no_cpu:
         log("bench: cpu baseline (oracle)")

@@ -59,6 +59,7 @@ extern "C" {
 #define LMOE_F32   0  /* IEEE binary32 */
 #define LMOE_BF16  1  /* bfloat16 */
 #define LMOE_NVFP4 2  /* routed-expert weights only, see lmoe_experts */
+#define LMOE_BF16_TILED 3  /* routed-expert bf16 weights in the tiled layout, see lmoe_pack_expert_weights */
 
 /*
  * Layer sizes.  Constraints (LMOE_ERR_SHAPE otherwise):
@@ -67,7 +68,8 @@ extern "C" {
  *   f >= 64 and f % 64 == 0; f_s == 0 (no shared expert) or f_s % 64 == 0.
  * Dtypes (LMOE_ERR_DTYPE otherwise):
  *   act_dtype LMOE_F32 with expert_dtype LMOE_F32, or
- *   act_dtype LMOE_BF16 with expert_dtype LMOE_BF16 or LMOE_NVFP4.
+ *   act_dtype LMOE_BF16 with expert_dtype LMOE_BF16, LMOE_BF16_TILED or
+ *   LMOE_NVFP4.
  */
 typedef struct lmoe_dims {
     int64_t T, d, l, E, k, f, f_s;
@@ -87,7 +89,10 @@ typedef struct lmoe_dims {
  *   M_scales [E][rows][K/16] uint8: E4M3 (FN) scale of each 16-element block
  *                                   along K;
  *   M_ts     [E] fp32: per-expert tensor scale.
- * The weight is w = E2M1(code) * E4M3(scale) * ts.  Unused fields are ignored.
+ * The weight is w = E2M1(code) * E4M3(scale) * ts.  LMOE_BF16_TILED uses
+ * W1 and W2 as written by lmoe_pack_expert_weights from the BF16 stacks (the
+ * same values; results are identical to passing the BF16 stacks).  Unused
+ * fields are ignored.
  */
 typedef struct lmoe_experts {
     const void* W1;
@@ -164,6 +169,21 @@ int lmoe_timing_start(int capacity);
  * sets *count to the number recorded, releases the events and stops
  * recording.  Returns LMOE_ERR_HIP if an event query fails. */
 int lmoe_timing_stop(lmoe_kernel_time* out, int capacity, int* count);
+
+/* ---- weight preparation --------------------------------------------- */
+
+/*
+ * Repacks one routed-expert bf16 weight stack W [E][rows][cols] (row-major:
+ * W1 with rows = f, cols = l; W2 with rows = l, cols = f) into the
+ * LMOE_BF16_TILED layout: 64-row slabs of 64x64 tiles, each tile stored in
+ * the order the expert GEMMs keep it in LDS, so that weight streaming reads
+ * whole contiguous kilobytes.  A one-time preparation of static weights, not
+ * part of the forward.  packed must hold E*rows*cols*2 bytes, may not
+ * overlap W, and both must be 16-byte aligned.  rows and cols must be
+ * positive multiples of 64 (LMOE_ERR_SHAPE).  Asynchronous on stream.
+ */
+int lmoe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const void* W, void* packed,
+                             void* stream);
 
 /* ---- the layer ------------------------------------------------------- */
 

@@ -24,12 +24,12 @@ LMOE_ERR_ALIGN = -4
 LMOE_ERR_WORKSPACE = -5
 LMOE_ERR_HIP = -6
 
-LMOE_F32, LMOE_BF16, LMOE_NVFP4 = 0, 1, 2
-DTYPE_CODE = {"f32": LMOE_F32, "bf16": LMOE_BF16, "nvfp4": LMOE_NVFP4}
+LMOE_F32, LMOE_BF16, LMOE_NVFP4, LMOE_BF16_TILED = 0, 1, 2, 3
+DTYPE_CODE = {"f32": LMOE_F32, "bf16": LMOE_BF16, "nvfp4": LMOE_NVFP4, "bf16_tiled": LMOE_BF16_TILED}
 
 EXPORTED = ["lmoe_workspace_bytes", "lmoe_validate_dims", "lmoe_strerror", "lmoe_last_hip_error",
             "latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
-            "lmoe_combine_up", "lmoe_timing_start", "lmoe_timing_stop"]
+            "lmoe_combine_up", "lmoe_timing_start", "lmoe_timing_stop", "lmoe_pack_expert_weights"]
 
 
 class Dims(ctypes.Structure):
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.lmoe_timing_start.restype = ctypes.c_int
         L.lmoe_timing_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         L.lmoe_timing_stop.restype = ctypes.c_int
+        L.lmoe_pack_expert_weights.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+        L.lmoe_pack_expert_weights.restype = ctypes.c_int
         for n in ("latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
                   "lmoe_combine_up"):
             getattr(L, n).restype = ctypes.c_int
@@ -149,6 +151,28 @@ def experts_struct(inp: Dict[str, Optional[torch.Tensor]]) -> Experts:
     g = inp.get
     return Experts(_p(g("W1")), _p(g("W2")), _p(g("W1_codes")), _p(g("W1_scales")), _p(g("W1_ts")),
                    _p(g("W2_codes")), _p(g("W2_scales")), _p(g("W2_ts")))
+
+
+def pack_expert_weights(W: torch.Tensor, stream=None) -> torch.Tensor:
+    """The LMOE_BF16_TILED image of one bf16 expert stack W [E][rows][cols]."""
+    if W.dtype != torch.bfloat16 or W.dim() != 3 or not W.is_contiguous():
+        raise LatentMoEError(LMOE_ERR_DTYPE, "pack_expert_weights needs a contiguous [E][rows][cols] bf16 stack")
+    P = torch.empty_like(W)
+    E, rows, cols = W.shape
+    _check(lib().lmoe_pack_expert_weights(E, rows, cols, _p(W), _p(P), _stream(stream)),
+           "lmoe_pack_expert_weights")
+    return P
+
+
+def pack_experts(cfg: LayerDims, inp, stream=None):
+    """(cfg, inputs) of the same layer with W1 and W2 in the tiled layout: the
+    config says experts='bf16_tiled' and the inputs hold the packed stacks."""
+    if cfg.experts != "bf16":
+        raise LatentMoEError(LMOE_ERR_DTYPE, "only bf16 expert stacks are packed")
+    out = dict(inp)
+    out["W1"] = pack_expert_weights(inp["W1"], stream)
+    out["W2"] = pack_expert_weights(inp["W2"], stream)
+    return cfg.with_(experts="bf16_tiled"), out
 
 
 def shared_struct(inp) -> Optional[Shared]:

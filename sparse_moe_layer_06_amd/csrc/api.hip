@@ -247,7 +247,8 @@ int lmoe_validate_dims(const lmoe_dims* d) {
         if (d->expert_dtype != LMOE_F32) return LMOE_ERR_DTYPE;
         if (max_tiles(*d) > 65535) return LMOE_ERR_SHAPE;  // grid.y of the fp32 grouped kernel
     } else if (d->act_dtype == LMOE_BF16) {
-        if (d->expert_dtype != LMOE_BF16 && d->expert_dtype != LMOE_NVFP4) return LMOE_ERR_DTYPE;
+        if (d->expert_dtype != LMOE_BF16 && d->expert_dtype != LMOE_BF16_TILED && d->expert_dtype != LMOE_NVFP4)
+            return LMOE_ERR_DTYPE;
     } else {
         return LMOE_ERR_DTYPE;
     }
@@ -273,6 +274,16 @@ const char* lmoe_strerror(int st) {
 }
 
 int lmoe_last_hip_error(void) { return g_last_hip_error; }
+
+int lmoe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const void* W, void* packed, void* stream) {
+    if (E < 1 || E > 1024 || rows < 64 || rows % 64 != 0 || cols < 64 || cols % 64 != 0 || rows > 65536 ||
+        cols > 65536)
+        return LMOE_ERR_SHAPE;
+    LMOE_TRY(check_ptrs({W, packed}));
+    const uintptr_t a = (uintptr_t)W, b = (uintptr_t)packed, n = (uintptr_t)(E * rows * cols * 2);
+    if (a < b + n && b < a + n) return LMOE_ERR_SHAPE;  // overlapping buffers
+    return hip_status(launch_pack_experts(W, packed, E, (int)rows, (int)cols, (hipStream_t)stream));
+}
 
 int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,
                       const float* router_bias, const lmoe_experts* experts, const void* W_up,

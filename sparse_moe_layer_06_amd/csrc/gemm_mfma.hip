@@ -534,6 +534,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     };
 
     constexpr bool B_DMA = C::DMA && BFMT != LMOE_NVFP4;
+    static_assert(BFMT != LMOE_BF16_TILED || (C::DMA && C::BK == 64 && C::BN % 64 == 0),
+                  "tiled weights: LDS-DMA, K step 64, whole 64-row slabs");
     using SA = Slots<C, C::BM>;
     using SB = Slots<C, C::BN>;
     // NVFP4 weights: each weight row's K step is split over LPR lanes, EPL
@@ -593,6 +595,16 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             const int64_t n = (int64_t)e * N + min(n0 + tid / LPR, N - 1);
             c_ptr = g.B_codes + n * (K / 2) + (tid % LPR) * (EPL / 2);
             s_ptr = g.B_scales + n * (K / 16) + (tid % LPR) * (EPL / 16);
+        } else if constexpr (BFMT == LMOE_BF16_TILED) {
+            // 64-row slabs of 64x64 tiles, each stored in the swizzled order of
+            // the LDS tile (the swizzle repeats every 16 rows and n0 is a
+            // multiple of 64): LDS chunk q comes from tile chunk q of its slab
+#pragma unroll
+            for (int j = 0; j < SB::N; ++j) {
+                const int n = min(n0 + SB::row(j, tid), N - 1);
+                const int pc = SB::chunk(j, tid) % C::CPR;
+                b_ptr[j] = (const uint16_t*)g.B + ((int64_t)e * N + (n & ~63)) * K + (n & 63) * 64 + pc * 8;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < SB::N; ++j) {
@@ -625,9 +637,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             else
                 rs = s_ptr[kt * (C::BK / 16)];
         } else if constexpr (B_DMA) {
+            // tiled weights: K step kt is the kt-th 64x64 tile of the slab
+            const int bk = BFMT == LMOE_BF16_TILED ? kt * 64 * 64 : kk;
 #pragma unroll
             for (int j = 0; j < SB::N; ++j)
-                if (SB::active(j, tid)) dma16<C::B_NT ? 2 : 0>(b_ptr[j] + kk, SB::dst(Bs, wave, j));
+                if (SB::active(j, tid)) dma16<C::B_NT ? 2 : 0>(b_ptr[j] + bk, SB::dst(Bs, wave, j));
         } else {
 #pragma unroll
             for (int j = 0; j < SB::N; ++j) rb[j] = *reinterpret_cast<const u32x4_t*>(b_ptr[j] + kk);
@@ -731,6 +745,43 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 }
 
 // ---------------------------------------------------------------------------
+// Repacking of bf16 expert weights into the tiled layout
+// ---------------------------------------------------------------------------
+//
+// W [E][rows][cols] row-major -> 64-row slabs of 64x64 tiles,
+// P[e][slab][kt][r][pc] (16-byte chunks) = W[e][64 slab + r][64 kt + 8 (pc ^ swz(r)) ..+8]:
+// each tile is stored exactly as the grouped GEMM's LDS tile holds it (K step
+// 64, 8 chunks per row, the swizzle of those tiles), so one LDS-DMA
+// instruction of the GEMM reads 1 KB of contiguous weights.
+constexpr int kPackTile = 64;
+using PackCfg = MfmaCfg<64, 64, 2, 2, true, kPackTile>;  // the tile geometry (CPR 8) of the packed layout
+
+__global__ __launch_bounds__(256) void pack_experts_kernel(const u32x4_t* __restrict__ W, u32x4_t* __restrict__ P,
+                                                           int64_t n_chunks, int rows, int cols) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= n_chunks) return;
+    constexpr int CPR = PackCfg::CPR;
+    const int kts = cols / kPackTile, slabs = rows / kPackTile;
+    const int pc = (int)(o % CPR), r = (int)((o / CPR) % kPackTile);
+    const int64_t tile = o / (CPR * kPackTile);  // (e, slab, kt)
+    const int kt = (int)(tile % kts);
+    const int64_t es = tile / kts;              // e * slabs + slab
+    const int64_t row = (es / slabs) * rows + (es % slabs) * kPackTile + r;
+    const int c = pc ^ swz_bits<CPR>(r);
+    P[o] = W[row * (cols / 8) + kt * CPR + c];
+}
+
+hipError_t launch_pack_experts(const void* W, void* P, int64_t E, int rows, int cols, hipStream_t s) {
+    const int64_t n_chunks = E * rows * (int64_t)cols / 8;
+    const int64_t blocks = (n_chunks + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    LMOE_LAUNCH("pack_experts", s,
+                pack_experts_kernel<<<(unsigned)blocks, 256, 0, s>>>((const u32x4_t*)W, (u32x4_t*)P, n_chunks,
+                                                                      rows, cols));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
@@ -803,6 +854,8 @@ static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
     const int grid = persistent_grid() * C::MINB;
     if (g.b_fmt == LMOE_NVFP4)
         launch_grouped_fmt<C, LMOE_NVFP4>(g, grid, nN, s);
+    else if (g.b_fmt == LMOE_BF16_TILED)
+        launch_grouped_fmt<C, LMOE_BF16_TILED>(g, grid, nN, s);
     else
         launch_grouped_fmt<C, LMOE_BF16>(g, grid, nN, s);
     return hipGetLastError();

@@ -65,7 +65,7 @@ struct GroupedGemm {
     const int* a_row_map;
     int a_row_div;
     int n_rows;  // sorted rows in total (T * k): bound of a_row_map
-    int b_fmt;  // LMOE_F32 / LMOE_BF16 dense stack [E][N][K], or LMOE_NVFP4
+    int b_fmt;  // LMOE_F32 / LMOE_BF16 dense stack [E][N][K], LMOE_BF16_TILED, or LMOE_NVFP4
     const void* B;
     const uint8_t* B_codes;   // [E][N][K/2]
     const uint8_t* B_scales;  // [E][N][K/16]
@@ -93,6 +93,8 @@ void timer_mark_end(hipStream_t s);
 hipError_t launch_dense_gemm(const DenseGemm& g, int act_dtype, int T_hint, void* splitk_ws,
                              size_t splitk_bytes, hipStream_t s);
 hipError_t launch_grouped_gemm(const GroupedGemm& g, int act_dtype, hipStream_t s);
+// W [E][rows][cols] bf16 -> the LMOE_BF16_TILED image (rows, cols multiples of 64)
+hipError_t launch_pack_experts(const void* W, void* P, int64_t E, int rows, int cols, hipStream_t s);
 
 // Grouped-GEMM M-tile height for these sizes (the tile table is built for it).
 int grouped_bm(const lmoe_dims& d);

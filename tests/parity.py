@@ -129,12 +129,14 @@ def sample_tokens(T: int, n: int) -> np.ndarray:
     return np.unique(np.concatenate([np.linspace(0, T - 1, n).astype(np.int64), [0, T - 1]]))
 
 
-def run_and_check(cfg, inp, n_sample: int = 1 << 30, lazy_experts: bool = False, report=None):
+def run_and_check(cfg, inp, n_sample: int = 1 << 30, lazy_experts: bool = False, report=None, gpu_inp=None):
     """Runs the fused forward with every intermediate exposed and checks it
-    against the oracle.  Returns a dict of the measured errors."""
+    against the oracle.  gpu_inp (default inp) is what the GPU reads, e.g.
+    the same layer with packed expert weights; the oracle reads inp.
+    Returns a dict of the measured errors."""
     T = inp["x"].shape[0]
     dbg = debug_buffers(cfg, T)
-    out = B.forward(cfg, inp, debug=dbg)
+    out = B.forward(cfg, gpu_inp if gpu_inp is not None else inp, debug=dbg)
     torch.cuda.synchronize()
 
     h = host_inputs(inp, lazy_experts)

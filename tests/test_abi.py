@@ -144,3 +144,22 @@ def test_strerror_and_last_error():
     for code in range(-6, 1):
         assert L.lmoe_strerror(code)
     assert L.lmoe_last_hip_error() == 0
+
+
+def test_pack_error_paths():
+    L = B.lib()
+    far = FAKE + (1 << 30)  # disjoint placeholder
+    assert L.lmoe_pack_expert_weights(2, 100, 64, FAKE, far, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_pack_expert_weights(2, 64, 96, FAKE, far, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_pack_expert_weights(0, 64, 64, FAKE, far, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_pack_expert_weights(2, 64, 64, None, far, None) == B.LMOE_ERR_NULL
+    assert L.lmoe_pack_expert_weights(2, 64, 64, MIS, far, None) == B.LMOE_ERR_ALIGN
+    assert L.lmoe_pack_expert_weights(2, 64, 64, FAKE, FAKE + 4096, None) == B.LMOE_ERR_SHAPE  # overlap
+
+
+def test_tiled_experts_need_bf16_activations():
+    d = dims()
+    d.expert_dtype = B.LMOE_BF16_TILED
+    assert B.validate_dims(d) == B.LMOE_OK
+    d.act_dtype = B.LMOE_F32
+    assert B.validate_dims(d) == B.LMOE_ERR_DTYPE

@@ -167,6 +167,21 @@ def test_permutation_matches_oracle_on_both_paths(T, k, E):
     assert np.array_equal(p["inv"].cpu().numpy(), ri)
 
 
+@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "stream_ragged", "k100_E256", "E1_bf16"])
+def test_tiled_expert_weights(name):
+    # the packed layout holds the same values: outputs bit-identical to the
+    # row-major stacks, and the oracle (row-major weights) agrees
+    cfg = SMALL[name]
+    log(f"case tiled {name}")
+    inp = small_inputs(cfg)
+    ref = B.forward(cfg, inp).clone()
+    cfg_t, inp_t = B.pack_experts(cfg, inp)
+    out = B.forward(cfg_t, inp_t)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    P.run_and_check(cfg_t, inp, gpu_inp=inp_t, report=log)
+
+
 # ---- full-size workloads --------------------------------------------------
 
 @pytest.mark.timeout(900)
@@ -194,6 +209,23 @@ def test_decode_zipf_full_size():
     counts = dbg["counts"].cpu().numpy()
     log(f"experts touched {int((counts > 0).sum())}, expert 0 rows {counts[0]}")
     assert counts[0] == cfg.T  # the largest bias: every token picks expert 0
+
+
+@pytest.mark.timeout(900)
+def test_tiled_experts_full_size_match_row_major():
+    for name in ("decode_bf16_zipf", "prefill_bf16"):
+        cfg = CFG[name]
+        log(f"case tiled full size {cfg}")
+        inp = synth.make_inputs(cfg, 0, "cuda")
+        ref = B.forward(cfg, inp).clone()
+        cfg_t, inp_t = B.pack_experts(cfg, inp)
+        out = B.forward(cfg_t, inp_t)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), name
+        if name == "decode_bf16_zipf":
+            P.run_and_check(cfg_t, inp, lazy_experts=True, report=log, gpu_inp=inp_t)
+        del inp, inp_t, ref, out
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
