@@ -36,12 +36,12 @@ SMALL = {
                           experts="bf16"),
     "k1_bf16": TINY.with_(name="k1_bf16", T=128, d=256, l=64, E=8, k=1, f=128, act="bf16", experts="bf16"),
     "kE_bf16": TINY.with_(name="kE_bf16", T=64, d=256, l=64, E=5, k=5, f=64, act="bf16", experts="bf16"),
-    # few rows per expert: the weight-streaming expert kernel (16-row tiles),
-    # K rings of 4/2 steps (l=128, f=192) and of 16 steps (l=f=512)
-    "stream_ragged": TINY.with_(name="stream_ragged", T=37, d=512, l=128, E=32, k=5, f=192, f_s=64,
-                                act="bf16", experts="bf16"),
-    "stream_deepK": TINY.with_(name="stream_deepK", T=20, d=2048, l=512, E=16, k=4, f=512, f_s=0,
-                               act="bf16", experts="bf16"),
+    # few rows per expert (the 64-row, 4-stage expert tiles), short K (l=128,
+    # f=192) and deep K (l=f=512)
+    "few_rows_ragged": TINY.with_(name="few_rows_ragged", T=37, d=512, l=128, E=32, k=5, f=192, f_s=64,
+                                  act="bf16", experts="bf16"),
+    "few_rows_deepK": TINY.with_(name="few_rows_deepK", T=20, d=2048, l=512, E=16, k=4, f=512, f_s=0,
+                                 act="bf16", experts="bf16"),
     # top-k beyond one register slot per lane: k = 100 of E = 256, and E = 1024
     "k100_E256": TINY.with_(name="k100_E256", T=16, d=256, l=64, E=256, k=100, f=64, act="bf16",
                             experts="bf16"),
@@ -167,7 +167,7 @@ def test_permutation_matches_oracle_on_both_paths(T, k, E):
     assert np.array_equal(p["inv"].cpu().numpy(), ri)
 
 
-@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "stream_ragged", "k100_E256", "E1_bf16"])
+@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "k100_E256", "E1_bf16"])
 def test_tiled_expert_weights(name):
     # the packed layout holds the same values: outputs bit-identical to the
     # row-major stacks, and the oracle (row-major weights) agrees
