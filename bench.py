@@ -137,6 +137,15 @@ def decode(cfg, steps, torch, B, synth, layout="tiled"):
         times.append((a, b))
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+    # per-kernel durations, a separate pass with the same eviction between steps
+    n_k = min(steps, 20)
+    with B.KernelTimer(capacity=64 * n_k) as kt:
+        for _ in range(n_k):
+            flush.sum()
+            call()
+        torch.cuda.synchronize()
+    kernels = {n: dict(avg_us=round(1e3 * sum(v) / len(v), 2), launches_per_step=len(v) / n_k)
+               for n, v in kt.by_kernel().items()}
     touched = int((counts > 0).sum().item())
     l, f, d, E, T = cfg.l, cfg.f, cfg.d, cfg.E, cfg.T
     bytes_alg = touched * 2 * l * f * 2 + (2 * d * l + d * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
@@ -145,7 +154,7 @@ def decode(cfg, steps, torch, B, synth, layout="tiled"):
                          f"({layout if cfg.experts == 'bf16' else 'as stored'})", tokens_per_s=T / (ms * 1e-3),
                 ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
                 hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
-                "1 GiB buffer read between steps (cache eviction)" % steps)
+                "1 GiB buffer read between steps (cache eviction)" % steps, kernels=kernels)
 
 
 def secondary(name, steps, warmup, torch, B, synth, layout="tiled"):

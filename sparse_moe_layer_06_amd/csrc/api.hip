@@ -48,8 +48,15 @@ static int64_t max_tiles(const lmoe_dims& d) {
 
 struct Layout {
     size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
-        c, hs, splitk, splitk_bytes, total;
+        c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, total;
 };
+
+// Whether the few-rows expert GEMMs may take the split-K 64 x 256 tiles
+// (64-row expert tiles, outputs at least 1024 wide): they then need the
+// partial-sum buffer and one counter per work item.
+static bool expert_split_k(const lmoe_dims& d) {
+    return d.act_dtype == LMOE_BF16 && grouped_bm(d) == kSkBM && (d.f >= 1024 || d.l >= 1024);
+}
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -84,6 +91,12 @@ static Layout plan(const lmoe_dims& d) {
     const size_t widest = (size_t)((max(d.l + d.E + d.f_s, d.d) + 3) / 4 * 4);
     L.splitk_bytes = (d.act_dtype == LMOE_BF16 && d.T <= 64) ? 16 * (size_t)d.T * widest * 4 : 0;
     L.splitk = take(L.splitk_bytes);
+    if (expert_split_k(d)) {
+        const int64_t widest_n = d.f > d.l ? d.f : d.l;
+        L.sk_count_len = (size_t)(max_tiles(d) * ((widest_n + kSkBN - 1) / kSkBN));
+        L.sk_count = take(L.sk_count_len * 4);
+        L.sk_part = take(kSkPartialBytes);
+    }
     L.total = o;
     return L;
 }
@@ -141,6 +154,8 @@ static TileTable tile_table(const lmoe_dims& d, char* ws, const Layout& L) {
     tt.expert_ntiles = (const int*)(ws + L.ntiles);
     tt.max_tiles = (int)max_tiles(d);
     tt.bm = grouped_bm(d);
+    tt.sk_count = L.sk_count_len ? (int*)(ws + L.sk_count) : nullptr;
+    tt.sk_count_len = (int)L.sk_count_len;
     return tt;
 }
 
@@ -167,7 +182,7 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
 }
 
 static hipError_t run_experts(const lmoe_dims& d, const void* z, const int32_t* perm, const lmoe_experts* ex,
-                              void* H, void* Y, const TileTable& tt, hipStream_t s) {
+                              void* H, void* Y, const TileTable& tt, char* ws, const Layout& L, hipStream_t s) {
     GroupedGemm g1{};
     g1.N = (int)d.f;
     g1.K = (int)d.l;
@@ -185,6 +200,7 @@ static hipError_t run_experts(const lmoe_dims& d, const void* z, const int32_t* 
     g1.epi = EPI_RELU2;
     g1.C = H;
     g1.ldc = d.f;
+    g1.sk_part = L.sk_count_len ? (float*)(ws + L.sk_part) : nullptr;
     hipError_t e = launch_grouped_gemm(g1, d.act_dtype, s);
     if (e != hipSuccess) return e;
 
@@ -329,7 +345,7 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, 
         run_project_route(d, x, W_down, W_router, router_bias, shared, z, logits, idx, gate, hs, ws, L, s);
     if (e == hipSuccess)
         e = launch_permute(idx, d.T * d.k, (int)d.E, (int32_t*)(ws + L.hist), counts, offsets, perm, inv, &tt, s);
-    if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, ws + L.Y, tt, s);
+    if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, ws + L.Y, tt, ws, L, s);
     if (e == hipSuccess) e = run_combine_up(d, ws + L.Y, inv, gate, W_up, shared, hs, c, out, ws, L, s);
     return hip_status(e);
 }
@@ -374,7 +390,7 @@ int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const int32_t* offset
     const TileTable tt = tile_table(d, ws, L);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_build_tiles(offsets, (int)d.E, tt, s);
-    if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, Y, tt, s);
+    if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, Y, tt, ws, L, s);
     return hip_status(e);
 }
 

@@ -443,12 +443,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseGemm g, int spl
     const int m = (int)(i / q), n = (int)(i % q) * 4;
     if (m >= g.M || n >= g.N) return;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < splits; ++sp) {
-        const float4 p = *reinterpret_cast<const float4*>(partial + ((int64_t)sp * g.M + m) * ldp + n);
-        v[0] += p.x;
-        v[1] += p.y;
-        v[2] += p.z;
-        v[3] += p.w;
+    // eight splits' loads in flight at a time, added in split order
+    constexpr int kBatch = 8;
+    for (int sp0 = 0; sp0 < splits; sp0 += kBatch) {
+        float4 p[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            if (sp0 + b < splits)
+                p[b] = *reinterpret_cast<const float4*>(partial + ((int64_t)(sp0 + b) * g.M + m) * ldp + n);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+            if (sp0 + b < splits) {
+                v[0] += p[b].x;
+                v[1] += p[b].y;
+                v[2] += p[b].z;
+                v[3] += p[b].w;
+            }
     }
     if (n + 3 < g.N) {
         dense_store4(g, m, n, v);
@@ -509,9 +519,19 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float pw, float
 // A-row gather modes of the grouped GEMM.
 enum Gather : int { GATHER_NONE = 0, GATHER_SCALAR = 1, GATHER_LANE = 2 };
 
-template <class C, int BFMT, int GATHER>
+// Work items are (expert tile, N tile) pairs, W = tiles * nN of them.
+//   SK = false: whole items; XCD x takes the x-th eighth of the list and its
+//               blocks take every nbx-th item of it.
+//   SK = true:  if the last round is at most half full (T = W - R G tail
+//               items, R = W / G full rounds), R full rounds of whole items
+//               (spread over the XCDs as above), then each tail item split
+//               along K into P >= 2 parts, one per block; the last part to
+//               finish sums them (sk_finish).  A lone tail item would
+//               otherwise be streamed by one block while the rest idle.
+template <class C, int BFMT, int GATHER, bool SK = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGemm g, int nN) {
     __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
+    __shared__ int sk_last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -519,16 +539,52 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     const int nk = K / C::BK;
 
     const int W = *g.tt.tile_count * nN;
-    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, nbx = gridDim.x >> 3;
-    const int per = W >> 3, rem = W & 7;
-    const int first = x * per + min(x, rem);
-    const int end = first + per + (x < rem ? 1 : 0);
-    if (first + slot >= end) return;
-    const int n_items = (end - 1 - first - slot) / nbx + 1;
-    const int total = n_items * nk;
+    int w_first, stride, n_items, total;
+    // SK: full rounds, parts per tail item, this block's tail item and part
+    // K range [sk_kb, sk_ke) (sk_t < 0: no tail part; sk_R < 0: no split)
+    int sk_R = -1, sk_P = 1, sk_t = -1, sk_kb = 0, sk_ke = 0;
+    if constexpr (SK) {
+        const int G = gridDim.x, R = W / G, T = W - R * G;
+        if (T > 0) sk_P = max(1, min(min(G / T, kSkMaxParts), nk));
+        if (sk_P > 1) {
+            const int b = blockIdx.x;
+            sk_R = R;
+            if (b < T * sk_P) {
+                sk_t = R * G + b / sk_P;
+                const int p = b % sk_P;
+                sk_kb = p * nk / sk_P;
+                sk_ke = (p + 1) * nk / sk_P;
+            }
+            n_items = R + (sk_t >= 0 ? 1 : 0);
+            if (n_items == 0) return;
+            total = R * nk + (sk_ke - sk_kb);
+            // full rounds XCD by XCD as for whole items: XCD b % 8 takes the
+            // (b % 8)-th eighth of the first R G items
+            const int nbx = G >> 3;
+            w_first = (b & 7) * R * nbx + (b >> 3);
+            stride = nbx;
+        }
+    }
+    if (sk_R < 0) {  // whole items only
+        const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+        const int per = W >> 3, rem = W & 7;
+        const int first = x * per + min(x, rem);
+        const int end = first + per + (x < rem ? 1 : 0);
+        if (first + slot >= end) return;
+        n_items = (end - 1 - first - slot) / nbx + 1;
+        total = n_items * nk;
+        w_first = first + slot;
+        stride = nbx;
+    }
+    // first K step of item i (only a tail part starts inside its item)
+    auto item_kt0 = [&](int i) __attribute__((always_inline)) { return (SK && i == sk_R) ? sk_kb : 0; };
+    auto item_w = [&](int i) __attribute__((always_inline)) {
+        i = min(i, n_items - 1);
+        return __builtin_amdgcn_readfirstlane((SK && i == sk_R) ? sk_t : w_first + i * stride);
+    };
     // descriptor {expert, first sorted row, rows, n0} of this block's item i
     auto load_item = [&](int i) __attribute__((always_inline)) {
-        const int w = __builtin_amdgcn_readfirstlane(first + slot + min(i, n_items - 1) * nbx);
+        const int w = item_w(i);
         const i32x4_t t = sload4(g.tt.tiles + w / nN);
         return make_int4(t.x, t.y, t.z, (w % nN) * C::BN);
     };
@@ -553,7 +609,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     const uint8_t* s_ptr = nullptr;
     int4 fdesc = load_item(0);
     int4 fnext = load_item(1);
-    int f_item = 0, f_kt = 0;
+    int f_item = 0, f_kt = item_kt0(0);
     // A row of sorted row p for slot j.  GATHER_SCALAR (DMA slots): the
     // slot's RPI rows are read with one scalar load of the permutation
     // (clamped inside [0, n_rows)) and each lane picks its row.
@@ -621,8 +677,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     // issues the next K step of the fill item into stage (As, Bs)
     auto fill_next = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
         if (f_kt == nk) {  // next item: its descriptor was fetched one item ahead
-            f_kt = 0;
             ++f_item;
+            f_kt = item_kt0(f_item);
             fdesc = fnext;
             setup(fdesc);
             fnext = load_item(f_item + 1);
@@ -711,6 +767,90 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         });
     };
 
+    // Tail part: the block stores its partial sums (thread-fragment order,
+    // coalesced; rows past the item's end are skipped), then counts itself
+    // in; the last of the item's P blocks adds the partials in part order
+    // (its own from registers) and runs the epilogue.  Every block of an
+    // item takes the same additions in the same order, so the result does
+    // not depend on which one finishes last.
+    // The partials move through device-coherent (agent-scope) stores and
+    // loads, which bypass the per-XCD L2 copies; the stores have completed
+    // (vmcnt 0) before the block's arrival is counted.  Fences would write
+    // back and invalidate whole L2s instead.
+    auto sk_finish = [&](const int4& d, f32x16_t (&acc)[C::TM][C::TN]) __attribute__((always_inline)) {
+        constexpr int NF4 = C::TM * C::TN * 4;
+        const int rows = d.z, b0 = blockIdx.x - blockIdx.x % sk_P, me = blockIdx.x - b0;
+        // two 64-bit words (4 floats) per thread and fragment quad j
+        auto part_of = [&](int b) {
+            return reinterpret_cast<uint64_t*>(g.sk_part) + (int64_t)b * (NF4 * C::NT * 2);
+        };
+        auto row_ok = [&](int j) { return wm * C::WM + (j / 4 / C::TN) * 32 + (lane & 31) < rows; };
+        auto pack2 = [](float a, float b) {
+            return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+        };
+        uint64_t* mine = part_of(blockIdx.x);
+        static_for<NF4>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value, r = (j % 4) * 4;
+            const f32x16_t& a = acc[j / 4 / C::TN][(j / 4) % C::TN];
+            uint64_t* at = mine + ((int64_t)j * C::NT + tid) * 2;
+            if (row_ok(j)) {
+                __hip_atomic_store(at, pack2(a[r], a[r + 1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(at + 1, pack2(a[r + 2], a[r + 3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        });
+        __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+        __syncthreads();
+        if (tid == 0) {
+            const int before =
+                __hip_atomic_fetch_add(g.tt.sk_count + sk_t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sk_last = (before == sk_P - 1);
+        }
+        __syncthreads();
+        if (!sk_last) return;
+        // parts in order, one part's loads in flight at a time (few registers)
+        float sum[NF4][4];
+        for (int p = 0; p < sk_P; ++p) {
+            uint64_t v[NF4][2];
+            if (p != me) {
+                const uint64_t* src = part_of(b0 + p);
+                static_for<NF4>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    const uint64_t* at = src + ((int64_t)j * C::NT + tid) * 2;
+                    if (row_ok(j)) {
+                        v[j][0] = __hip_atomic_load(at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        v[j][1] = __hip_atomic_load(at + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                });
+            }
+            static_for<NF4>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value, r = (j % 4) * 4;
+                if (!row_ok(j)) return;
+                const f32x16_t& a = acc[j / 4 / C::TN][(j / 4) % C::TN];
+                float f[4];
+                if (p == me) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) f[t] = a[r + t];
+                } else {
+                    f[0] = __uint_as_float((uint32_t)v[j][0]);
+                    f[1] = __uint_as_float((uint32_t)(v[j][0] >> 32));
+                    f[2] = __uint_as_float((uint32_t)v[j][1]);
+                    f[3] = __uint_as_float((uint32_t)(v[j][1] >> 32));
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sum[j][t] = p == 0 ? f[t] : sum[j][t] + f[t];
+            });
+        }
+        static_for<NF4>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value, r = (j % 4) * 4;
+            if (!row_ok(j)) return;
+            f32x16_t& a = acc[j / 4 / C::TN][(j / 4) % C::TN];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a[r + t] = sum[j][t];
+        });
+        epilogue(d, acc);
+        if (tid == 0) __hip_atomic_store(g.tt.sk_count + sk_t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
     constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS, AOFF = C::BM * C::CPR;
     constexpr int PER_TILE = (C::DMA && B_DMA) ? SA::N + SB::N : 0;
     constexpr int MAXAHEAD = PER_TILE > 0 ? S - 2 : 0;
@@ -723,7 +863,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             land(ring + st * STG, ring + st * STG + AOFF);
         }
     }
-    int cur = 0, nxt = S - 1, m_kt = 0;
+    int cur = 0, nxt = S - 1, m_item = 0, m_kt = item_kt0(0), m_kt0 = m_kt;
     for (int q = 0; q < total; ++q) {
         wait_tiles_barrier<MAXAHEAD, PER_TILE>(min(MAXAHEAD, total - 1 - q));
         const bool more = q + S - 1 < total;
@@ -734,13 +874,24 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         if (more) land(ns, ns + AOFF);
         cur = (cur + 1 == S) ? 0 : cur + 1;
         nxt = (nxt + 1 == S) ? 0 : nxt + 1;
-        if (++m_kt == nk) {
-            m_kt = 0;
+        ++m_kt;
+        // a tail part is the block's last item and ends the loop; it is
+        // finished after the loop, which keeps the loop free of its stores,
+        // atomics and barriers (and of the waits the compiler adds for them)
+        if (SK && q == total - 1 && !(m_kt0 == 0 && m_kt == nk)) break;
+        if (m_kt == nk) {
             epilogue(mdesc, acc);
             zero_acc<C>(acc);
-            mdesc = fdesc;  // the fill side is already on the next item
+            // the fill side is on the next item already unless items are
+            // shorter than the prefetch distance
+            ++m_item;
+            m_kt = m_kt0 = item_kt0(m_item);
+            mdesc = nk >= S - 1 ? fdesc : load_item(m_item);
             fetch_scale(mdesc);
         }
+    }
+    if constexpr (SK) {
+        if (m_item < n_items && sk_t >= 0) sk_finish(mdesc, acc);
     }
 }
 
@@ -794,7 +945,7 @@ static int persistent_grid();
 static int splitk_factor(int tiles, int nk, int M, int ldp, size_t ws_bytes, int blocks_per_cu) {
     const int cus = persistent_grid();
     if (ws_bytes == 0 || tiles >= 2 * cus) return 1;
-    int splits = (blocks_per_cu * cus + tiles - 1) / tiles;
+    int splits = blocks_per_cu * cus / tiles;  // one round of blocks
     const int by_k = nk / 4 > 1 ? nk / 4 : 1;
     if (splits > by_k) splits = by_k;
     const size_t per = (size_t)M * ldp * sizeof(float);
@@ -834,30 +985,45 @@ static int persistent_grid() {
     return (cus + 7) / 8 * 8;
 }
 
-template <class C, int BFMT>
+template <class C, int BFMT, bool SK>
 static void launch_grouped_fmt(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
     constexpr int RPI = Slots<C, C::BM>::RPI;
     constexpr bool can_scalar = C::DMA && (RPI == 8 || RPI == 16);
     const char* name = BFMT == LMOE_NVFP4 ? "grouped_gemm_nvfp4" : "grouped_gemm";
     if (!g.a_row_map)
-        LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_NONE><<<grid, C::NT, 0, s>>>(g, nN));
+        LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_NONE, SK><<<grid, C::NT, 0, s>>>(g, nN));
     else if (can_scalar && g.n_rows >= RPI)
         LMOE_LAUNCH(name, s,
-                    grouped_gemm_kernel<C, BFMT, can_scalar ? GATHER_SCALAR : GATHER_LANE><<<grid, C::NT, 0, s>>>(g, nN));
+                    grouped_gemm_kernel<C, BFMT, can_scalar ? GATHER_SCALAR : GATHER_LANE, SK>
+                    <<<grid, C::NT, 0, s>>>(g, nN));
     else
-        LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_LANE><<<grid, C::NT, 0, s>>>(g, nN));
+        LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_LANE, SK><<<grid, C::NT, 0, s>>>(g, nN));
 }
 
+template <class C, bool SK>
+static void launch_grouped_any(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
+    if (g.b_fmt == LMOE_NVFP4)
+        launch_grouped_fmt<C, LMOE_NVFP4, SK>(g, grid, nN, s);
+    else if (g.b_fmt == LMOE_BF16_TILED)
+        launch_grouped_fmt<C, LMOE_BF16_TILED, SK>(g, grid, nN, s);
+    else
+        launch_grouped_fmt<C, LMOE_BF16, SK>(g, grid, nN, s);
+}
+
+// Split-K scheduling for the 64 x 256 few-rows tiles when the caller gave
+// the partial-sum buffer and enough counters; whole items otherwise.
 template <class C>
 static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
     const int nN = (g.N + C::BN - 1) / C::BN;
     const int grid = persistent_grid() * C::MINB;
-    if (g.b_fmt == LMOE_NVFP4)
-        launch_grouped_fmt<C, LMOE_NVFP4>(g, grid, nN, s);
-    else if (g.b_fmt == LMOE_BF16_TILED)
-        launch_grouped_fmt<C, LMOE_BF16_TILED>(g, grid, nN, s);
-    else
-        launch_grouped_fmt<C, LMOE_BF16>(g, grid, nN, s);
+    if constexpr (C::BM == kSkBM && C::BN == kSkBN) {
+        if (g.sk_part && g.tt.sk_count && grid <= kSkMaxBlocks &&
+            (int64_t)g.tt.max_tiles * nN <= (int64_t)g.tt.sk_count_len) {
+            launch_grouped_any<C, true>(g, grid, nN, s);
+            return hipGetLastError();
+        }
+    }
+    launch_grouped_any<C, false>(g, grid, nN, s);
     return hipGetLastError();
 }
 
@@ -880,10 +1046,13 @@ hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t sp
 
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to
 // 384) by 256 columns over 8 waves, each wave 96 x 64.  Few-row experts
-// (decode) stream their weights: 64x64 tiles, 4 LDS stages, two blocks per
-// CU, and the non-temporal hint on the weights, which each call reads once.
+// (decode) stream their weights with the non-temporal hint (each call reads
+// them once): 64x256 tiles, 3 LDS stages, for wide outputs (each activation
+// row fetched per K step then feeds 256 weight rows, not 64), else 64x64
+// tiles, 4 stages, two blocks per CU.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
     if (g.tt.bm == 192) return run_grouped<MfmaCfg<192, 256, 2, 4, true, 64, 2>>(g, s);
+    if (g.tt.bm == 64 && g.N >= 1024) return run_grouped<MfmaCfg<64, 256, 2, 4, true, 64, 3, 1, true>>(g, s);
     if (g.tt.bm == 64) return run_grouped<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, s);
     return hipErrorInvalidValue;
 }

@@ -51,7 +51,19 @@ struct TileTable {
     const int* expert_ntiles;
     int max_tiles;
     int bm;
+    // Arrival counters of the tail-split expert GEMMs, one per work item; the
+    // kernels that build the table zero them, and each GEMM leaves them zero.
+    int* sk_count;
+    int sk_count_len;
 };
+
+// Tail splitting of the few-rows expert GEMM: whole work items fill as many
+// full rounds of the blocks as they can; each item of the last, partial
+// round is split along K over up to kSkMaxParts blocks, and the block that
+// finishes last sums the parts in part order.  One partial-sum slot per block.
+constexpr int kSkBM = 64, kSkBN = 256;
+constexpr int kSkMaxBlocks = 512, kSkMaxParts = 4;
+constexpr size_t kSkPartialBytes = (size_t)kSkMaxBlocks * kSkBM * kSkBN * sizeof(float);
 
 // Per-expert GEMM over sorted rows: for every tile (expert e, rows p),
 // C[p][n] = epi( scale_e * sum_k A[arow(p)][k] * W_e[n][k] ), with
@@ -73,6 +85,7 @@ struct GroupedGemm {
     int epi;                  // EPI_RELU2 or EPI_STORE
     void* C;
     int64_t ldc;
+    float* sk_part;           // kSkPartialBytes of tail-split partial sums, or null (whole items only)
 };
 
 // ---- optional per-launch event timing (timing.hip) -----------------------

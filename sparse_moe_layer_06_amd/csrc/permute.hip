@@ -81,6 +81,7 @@ __device__ void write_tiles(int e, int E, int count, int offset, const TileTable
         const_cast<int*>(tt.expert_ntiles)[e] = nt;
     }
     if (threadIdx.x == 0) const_cast<int*>(tt.tile_count)[0] = total_tiles;
+    for (int i = threadIdx.x; i < tt.sk_count_len; i += blockDim.x) tt.sk_count[i] = 0;
     *tile_start_out = ts;
     *ntiles_out = nt;
 }

@@ -7,13 +7,21 @@
 // places routing in the latent stage.  The softmax-over-selected gate is
 // this library's specification.
 //
-// One wavefront per token.  Each lane holds S = ceil(E/64) logits as 64-bit
-// keys (order-preserving logit bits << 32 | ~expert id), so a plain max over
-// keys picks the larger logit and, on equal logits, the smaller id.  Each
-// lane sorts its keys once (descending), so its head is its largest; k
-// rounds then take the wave-wide max of the heads (DPP row shifts and row
-// broadcasts, no LDS round trips) and the winning lane drops its head.
-// Lane j % 64 keeps selection j in register slot j / 64.
+// One wavefront per token; each lane holds S = ceil(E/64) logits.
+//
+// k <= 64 (radix select): the k-th largest logit X is found bit by bit from
+// the top of the order-preserving 32-bit encoding (X is the largest value
+// with at least k logits >= X; each bit costs S ballots and popcounts).
+// The selection is every logit above X plus the lowest ids among those equal
+// to X.  The k selected (logit, id) keys are ranked against each other in
+// LDS, and lane j takes the key of rank j.
+//
+// k > 64 (repeated max): 64-bit keys (logit bits << 32 | ~expert id), so a
+// plain max over keys picks the larger logit and, on equal logits, the
+// smaller id.  Each lane sorts its keys once (descending), so its head is
+// its largest; k rounds then take the wave-wide max of the heads (DPP row
+// shifts and row broadcasts) and the winning lane drops its head.  Lane
+// j % 64 keeps selection j in register slot j / 64.
 #include "device_common.hpp"
 #include "lmoe_internal.hpp"
 
@@ -137,10 +145,96 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     }
 }
 
+// Gates of the k (<= 64) selections held by lanes 0..k-1, in rank order:
+// softmax with the rank-0 logit as the shift.
+__device__ __forceinline__ void write_gates(float v, int e, int lane, int64_t t, int k, int32_t* __restrict__ idx,
+                                            float* __restrict__ gate) {
+    const float vmax = __shfl(v, 0, kWave);
+    const float w = lane < k ? expf(v - vmax) : 0.f;
+    const float inv_sum = 1.0f / wave_sum(w);
+    if (lane < k) {
+        idx[t * k + lane] = e;
+        gate[t * k + lane] = w * inv_sum;
+    }
+}
+
+template <int S>
+__global__ __launch_bounds__(256) void topk_select_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                          int32_t* __restrict__ idx, float* __restrict__ gate) {
+    __shared__ uint64_t by_id[4][kWave], by_rank[4][kWave];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;  // whole wave exits together
+    const float* s = logits + (int64_t)t * E;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    uint32_t v[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        const int e = lane + i * kWave;
+        v[i] = (e < E) ? ordered_bits(s[e]) : 0u;  // 0 is below every encoded logit
+    }
+    auto count_ge = [&](uint32_t y) __attribute__((always_inline)) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < S; ++i) c += __popcll(__ballot(v[i] >= y));
+        return c;
+    };
+    uint32_t X = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t y = X | (1u << b);
+        if (count_ge(y) >= k) X = y;
+    }
+    // logits above X are all selected; ties at X go to the lowest ids
+    int need = k;
+#pragma unroll
+    for (int i = 0; i < S; ++i) need -= __popcll(__ballot(v[i] > X));
+    int base = 0;  // position of this slot's first selection in id order
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        const int e = lane + i * kWave;
+        const bool eq = e < E && v[i] == X;
+        const uint64_t m_eq = __ballot(eq);
+        const bool take = v[i] > X || (eq && __popcll(m_eq & lt_mask) < need);
+        need -= min(need, __popcll(m_eq));
+        const uint64_t m = __ballot(take);
+        if (take) by_id[wv][base + __popcll(m & lt_mask)] = ((uint64_t)v[i] << 32) | (uint32_t)(~(uint32_t)e);
+        base += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // rank = the number of selected keys above this one (keys are distinct)
+    if (lane < k) {
+        const uint64_t key = by_id[wv][lane];
+        int rank = 0;
+        for (int q = 0; q < k; ++q) rank += by_id[wv][q] > key;
+        by_rank[wv][rank] = key;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint64_t key = lane < k ? by_rank[wv][lane] : 0ull;
+    write_gates(unordered_value((uint32_t)(key >> 32)), (int)(~(uint32_t)key), lane, t, k, idx, gate);
+}
+
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* gate,
                                hipStream_t s) {
     if (E > kMaxE) return hipErrorInvalidValue;
     dim3 grid((T + 3) / 4);
+    if (k <= kWave) {
+        if (E <= 64)
+            LMOE_LAUNCH("topk_softmax", s, topk_select_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, idx, gate));
+        else if (E <= 128)
+            LMOE_LAUNCH("topk_softmax", s, topk_select_kernel<2><<<grid, 256, 0, s>>>(logits, T, E, k, idx, gate));
+        else if (E <= 256)
+            LMOE_LAUNCH("topk_softmax", s, topk_select_kernel<4><<<grid, 256, 0, s>>>(logits, T, E, k, idx, gate));
+        else if (E <= 512)
+            LMOE_LAUNCH("topk_softmax", s, topk_select_kernel<8><<<grid, 256, 0, s>>>(logits, T, E, k, idx, gate));
+        else
+            LMOE_LAUNCH("topk_softmax", s, topk_select_kernel<16><<<grid, 256, 0, s>>>(logits, T, E, k, idx, gate));
+        return hipGetLastError();
+    }
     if (E <= 64)
         LMOE_LAUNCH("topk_softmax", s, topk_softmax_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, idx, gate));
     else if (E <= 128)

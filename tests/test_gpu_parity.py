@@ -42,6 +42,12 @@ SMALL = {
                                   act="bf16", experts="bf16"),
     "few_rows_deepK": TINY.with_(name="few_rows_deepK", T=20, d=2048, l=512, E=16, k=4, f=512, f_s=0,
                                  act="bf16", experts="bf16"),
+    # few rows per expert and outputs >= 1024 wide (the 64x256 expert tiles),
+    # N = 1280 not a multiple of 256
+    "few_rows_wide": TINY.with_(name="few_rows_wide", T=24, d=4096, l=1024, E=32, k=4, f=1280, f_s=0,
+                                act="bf16", experts="bf16"),
+    "nvfp4_few_wide": TINY.with_(name="nvfp4_few_wide", T=16, d=4096, l=1024, E=16, k=2, f=1280, f_s=0,
+                                 act="bf16", experts="nvfp4"),
     # top-k beyond one register slot per lane: k = 100 of E = 256, and E = 1024
     "k100_E256": TINY.with_(name="k100_E256", T=16, d=256, l=64, E=256, k=100, f=64, act="bf16",
                             experts="bf16"),
@@ -109,7 +115,7 @@ def test_exact_logit_ties_break_to_lower_id():
 
 
 def test_staged_entry_points_compose_to_forward():
-    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged"):
+    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide"):
         cfg = SMALL[name]
         log(f"case staged {name}")
         inp = small_inputs(cfg)
@@ -123,8 +129,11 @@ def test_staged_entry_points_compose_to_forward():
         assert torch.equal(o["out"], fused), name
 
 
-def test_repeated_runs_are_bit_identical():
-    cfg = SMALL["bf16_deep"]
+@pytest.mark.parametrize("name", ["bf16_deep", "few_rows_wide"])
+def test_repeated_runs_are_bit_identical(name):
+    # few_rows_wide: expert GEMMs with split-K items, whose partial sums are
+    # added by whichever block finishes last
+    cfg = SMALL[name]
     inp = small_inputs(cfg)
     ws = B.alloc_workspace(cfg)
     a = B.forward(cfg, inp, workspace=ws).clone()
@@ -167,7 +176,8 @@ def test_permutation_matches_oracle_on_both_paths(T, k, E):
     assert np.array_equal(p["inv"].cpu().numpy(), ri)
 
 
-@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "k100_E256", "E1_bf16"])
+@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "few_rows_wide", "k100_E256",
+                                  "E1_bf16"])
 def test_tiled_expert_weights(name):
     # the packed layout holds the same values: outputs bit-identical to the
     # row-major stacks, and the oracle (row-major weights) agrees
