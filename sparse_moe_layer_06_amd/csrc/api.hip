@@ -46,6 +46,44 @@ static int64_t max_tiles(const lmoe_dims& d) {
     return (n + bm - 1) / bm + (d.E < n ? d.E : n);
 }
 
+// x [W_down; W_r; W_s1]^T -> z, logits (+ bias), hs (the shared expert's
+// hidden layer, only with f_s > 0).
+static DenseGemm gemm_in(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r, const float* bias,
+                         const void* W_s1, void* z, float* logits, void* hs) {
+    DenseGemm g{};
+    g.M = (int)d.T;
+    g.N = (int)(d.l + d.E + d.f_s);
+    g.nseg = 1;
+    g.A[0] = x;
+    g.lda[0] = d.d;
+    g.K[0] = (int)d.d;
+    g.ngroups = d.f_s > 0 ? 3 : 2;
+    g.g[0] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
+    g.g[1] = NGroup{(int)d.l, (int)(d.l + d.E), {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
+    if (d.f_s > 0) g.g[2] = NGroup{(int)(d.l + d.E), g.N, {W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
+    return g;
+}
+
+// [c | hs] [W_up | W_s2]^T -> out.
+static DenseGemm gemm_out(const lmoe_dims& d, const void* c, const void* hs, const void* W_up, const void* W_s2,
+                          void* out) {
+    DenseGemm g{};
+    g.M = (int)d.T;
+    g.N = (int)d.d;
+    g.nseg = d.f_s > 0 ? 2 : 1;
+    g.A[0] = c;
+    g.lda[0] = d.l;
+    g.K[0] = (int)d.l;
+    if (d.f_s > 0) {
+        g.A[1] = hs;
+        g.lda[1] = d.f_s;
+        g.K[1] = (int)d.f_s;
+    }
+    g.ngroups = 1;
+    g.g[0] = NGroup{0, (int)d.d, {W_up, d.f_s > 0 ? W_s2 : nullptr}, EPI_STORE, out, d.d, nullptr};
+    return g;
+}
+
 struct Layout {
     size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
         c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, total;
@@ -88,8 +126,16 @@ static Layout plan(const lmoe_dims& d) {
     L.c = take((size_t)d.T * d.l * es);
     L.hs = take((size_t)d.T * d.f_s * es);
     // fp32 split-K partials of the dense GEMMs of few-token (decode) calls
+    // and of the split last round of many-token ones
     const size_t widest = (size_t)((max(d.l + d.E + d.f_s, d.d) + 3) / 4 * 4);
-    L.splitk_bytes = (d.act_dtype == LMOE_BF16 && d.T <= 64) ? 16 * (size_t)d.T * widest * 4 : 0;
+    if (d.act_dtype == LMOE_BF16 && d.T <= 64) {
+        L.splitk_bytes = 16 * (size_t)d.T * widest * 4;
+    } else if (d.act_dtype == LMOE_BF16) {
+        const size_t a = dense_tail_split_bytes(gemm_in(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                        nullptr, nullptr));
+        const size_t b = dense_tail_split_bytes(gemm_out(d, nullptr, nullptr, nullptr, nullptr, nullptr));
+        L.splitk_bytes = a > b ? a : b;
+    }
     L.splitk = take(L.splitk_bytes);
     if (expert_split_k(d)) {
         const int64_t widest_n = d.f > d.l ? d.f : d.l;
@@ -165,17 +211,7 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
                                     const float* bias, const lmoe_shared* sh, void* z, float* logits,
                                     int32_t* idx, float* gate, void* hs, char* ws, const Layout& L,
                                     hipStream_t s) {
-    DenseGemm g{};
-    g.M = (int)d.T;
-    g.N = (int)(d.l + d.E + d.f_s);
-    g.nseg = 1;
-    g.A[0] = x;
-    g.lda[0] = d.d;
-    g.K[0] = (int)d.d;
-    g.ngroups = sh ? 3 : 2;
-    g.g[0] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
-    g.g[1] = NGroup{(int)d.l, (int)(d.l + d.E), {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
-    if (sh) g.g[2] = NGroup{(int)(d.l + d.E), g.N, {sh->W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
+    const DenseGemm g = gemm_in(d, x, W_down, W_r, bias, sh ? sh->W_s1 : nullptr, z, logits, hs);
     hipError_t e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
     if (e != hipSuccess) return e;
     return launch_topk_softmax(logits, (int)d.T, (int)d.E, (int)d.k, idx, gate, s);
@@ -226,20 +262,7 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
                                  char* ws, const Layout& L, hipStream_t s) {
     hipError_t e = launch_combine(Y, inv, gate, (int)d.T, (int)d.k, (int)d.l, d.act_dtype, c, s);
     if (e != hipSuccess) return e;
-    DenseGemm g{};
-    g.M = (int)d.T;
-    g.N = (int)d.d;
-    g.nseg = sh ? 2 : 1;
-    g.A[0] = c;
-    g.lda[0] = d.l;
-    g.K[0] = (int)d.l;
-    if (sh) {
-        g.A[1] = hs;
-        g.lda[1] = d.f_s;
-        g.K[1] = (int)d.f_s;
-    }
-    g.ngroups = 1;
-    g.g[0] = NGroup{0, (int)d.d, {W_up, sh ? sh->W_s2 : nullptr}, EPI_STORE, out, d.d, nullptr};
+    const DenseGemm g = gemm_out(d, c, hs, W_up, sh ? sh->W_s2 : nullptr, out);
     return launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
 }
 

@@ -27,6 +27,8 @@
 // the 8 XCDs, so block b is the (b/8)-th block of XCD b%8; each XCD is given
 // a contiguous range of the tile order, so tiles that share operands run
 // together under one L2.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "lmoe_internal.hpp"
 
@@ -1027,6 +1029,60 @@ static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Columns [n0, n1) of a dense GEMM as a GEMM of their own: groups clipped
+// to the range, their weight rows, outputs and biases offset to match.
+static DenseGemm sub_columns(const DenseGemm& g, int n0, int n1) {
+    DenseGemm h = g;
+    h.N = n1 - n0;
+    h.ngroups = 0;
+    for (int i = 0; i < g.ngroups; ++i) {
+        const NGroup& G = g.g[i];
+        const int b = G.n_begin > n0 ? G.n_begin : n0, e = G.n_end < n1 ? G.n_end : n1;
+        if (b >= e) continue;
+        const int skip = b - G.n_begin;  // columns of G before the range
+        NGroup H = G;
+        H.n_begin = b - n0;
+        H.n_end = e - n0;
+        for (int sg = 0; sg < g.nseg; ++sg)
+            if (G.B[sg]) H.B[sg] = (const uint16_t*)G.B[sg] + (int64_t)skip * g.K[sg];
+        H.C = G.epi == EPI_F32_BIAS ? (void*)((float*)G.C + skip) : (void*)((uint16_t*)G.C + skip);
+        if (G.bias) H.bias = G.bias + skip;
+        h.g[h.ngroups++] = H;
+    }
+    return h;
+}
+
+// Tail split of a many-tile dense GEMM: when the last round of 256 x 256
+// tiles over the CUs is at most half full and made of whole N-tile columns,
+// those columns run as a split-K GEMM of their own (one round of blocks, the
+// partials summed in split order), so the last round costs a fraction of a
+// tile instead of a whole one.  Returns the first tail column (N: no split)
+// and the partial-sum bytes the tail needs.
+static int dense_tail_split(const DenseGemm& g, int cus, size_t* bytes) {
+    constexpr int T = 256;
+    const int tiles_m = (g.M + T - 1) / T, tiles_n = (g.N + T - 1) / T;
+    const int tiles = tiles_m * tiles_n, rounds = tiles / cus, tail = tiles - rounds * cus;
+    *bytes = 0;
+    if (rounds < 1 || tail == 0 || tail > cus / 2 || tail % tiles_m != 0) return g.N;
+    const int n0 = (tiles_n - tail / tiles_m) * T;
+    for (int i = 0; i < g.ngroups; ++i) {  // the split must keep 8-column alignment of outputs
+        const NGroup& G = g.g[i];
+        if (n0 > G.n_begin && n0 < G.n_end && (n0 - G.n_begin) % 8 != 0) return g.N;
+    }
+    const int nk = g.K[0] / 64 + (g.nseg > 1 ? g.K[1] / 64 : 0);
+    const int splits = std::min(std::min(cus / tail, 4), std::max(1, nk / 4));
+    if (splits < 2) return g.N;
+    const size_t ldp = (size_t)((g.N - n0 + 3) / 4 * 4);
+    *bytes = (size_t)splits * g.M * ldp * sizeof(float);
+    return n0;
+}
+
+size_t dense_tail_split_bytes(const DenseGemm& g) {
+    size_t bytes = 0;
+    dense_tail_split(g, persistent_grid(), &bytes);
+    return bytes;
+}
+
 #ifndef LMOE_GEMM_VARIANTS
 // Dense: 256x256 tiles over 8 waves (2 per SIMD), each wave 64 x 128, the
 // fastest shape measured for the 8192-wide projections; 256x192 where that
@@ -1035,15 +1091,24 @@ static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
 hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s) {
     if (g.M <= 64)  // weight streaming: 64x64 tiles, 4 stages, 2 blocks per CU, split-K
         return run_dense<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, splitk_ws, splitk_bytes, s);
-    // 256-wide tiles unless 192-wide ones leave clearly fewer idle CUs: the
-    // cost of a shape is its rounds of tiles over the CUs times the tile width.
+    using C256 = MfmaCfg<256, 256, 4, 2, true, 64, 2>;
+    // The cost of a shape is its rounds of tiles over the CUs times the tile
+    // width (a split tail round costs about a quarter); 256-wide tiles
+    // unless 192-wide ones are clearly cheaper.
     const int cus = persistent_grid(), tiles_m = (g.M + 255) / 256;
-    const double r256 = (double)((tiles_m * ((g.N + 255) / 256) + cus - 1) / cus);
+    size_t tail_bytes = 0;
+    const int n_tail = dense_tail_split(g, cus, &tail_bytes);
+    const bool split_tail = n_tail < g.N && tail_bytes <= splitk_bytes;
+    const int full_rounds = tiles_m * ((g.N + 255) / 256) / cus;
+    const double r256 = split_tail ? full_rounds + 0.25
+                                   : (double)((tiles_m * ((g.N + 255) / 256) + cus - 1) / cus);
     const double r192 = (double)((tiles_m * ((g.N + 191) / 192) + cus - 1) / cus) * 0.75;
     if (r192 < 0.85 * r256) return run_dense<MfmaCfg<256, 192, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
-    return run_dense<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
+    if (!split_tail) return run_dense<C256>(g, nullptr, 0, s);
+    const hipError_t e = run_dense<C256>(sub_columns(g, 0, n_tail), nullptr, 0, s);
+    if (e != hipSuccess) return e;
+    return run_dense<C256>(sub_columns(g, n_tail, g.N), splitk_ws, splitk_bytes, s);
 }
-
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to
 // 384) by 256 columns over 8 waves, each wave 96 x 64.  Few-row experts
 // (decode) stream their weights with the non-temporal hint (each call reads

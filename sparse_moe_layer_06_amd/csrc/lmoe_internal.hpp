@@ -88,6 +88,10 @@ struct GroupedGemm {
     float* sk_part;           // kSkPartialBytes of tail-split partial sums, or null (whole items only)
 };
 
+// Partial-sum bytes the split last round of a many-token dense GEMM needs on
+// this device (0: no split).
+size_t dense_tail_split_bytes(const DenseGemm& g);
+
 // ---- optional per-launch event timing (timing.hip) -----------------------
 
 void timer_mark_begin(const char* name, hipStream_t s);
