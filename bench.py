@@ -148,23 +148,25 @@ def decode(cfg, steps, torch, B, synth, layout="tiled"):
                for n, v in kt.by_kernel().items()}
     touched = int((counts > 0).sum().item())
     l, f, d, E, T = cfg.l, cfg.f, cfg.d, cfg.E, cfg.T
-    bytes_alg = touched * 2 * l * f * 2 + (2 * d * l + d * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
+    r_in = l if cfg.router_latent else d  # router weights W_r [E][r_in]
+    bytes_alg = touched * 2 * l * f * 2 + (2 * d * l + r_in * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     return dict(workload=f"{cfg.name} T={T} d={d} l={l} E={E} k={cfg.k} f={f}, {cfg.experts} experts "
-                         f"({layout if cfg.experts == 'bf16' else 'as stored'})", tokens_per_s=T / (ms * 1e-3),
+                         f"({layout if cfg.experts == 'bf16' else 'as stored'}), router reads "
+                         f"{'z (latent)' if cfg.router_latent else 'x'}", tokens_per_s=T / (ms * 1e-3),
                 ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
                 hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
                 "1 GiB buffer read between steps (cache eviction)" % steps, kernels=kernels)
 
 
-def secondary(name, steps, warmup, torch, B, synth, layout="tiled"):
+def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     """The other MFMA-bound workloads (same metric, reported beside the headline)."""
-    cfg = synth.CONFIGS[name]
     inp, out, ms, _, kernels = prefill(cfg, steps, warmup, torch, B, synth, layout)
     gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
     g = kernels.get(gname)
     res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
-                        f"{cfg.experts} experts", ms_per_step=ms, tokens_per_s=cfg.T / (ms * 1e-3),
+                        f"{cfg.experts} experts, router reads {'z (latent)' if cfg.router_latent else 'x'}",
+               ms_per_step=ms, tokens_per_s=cfg.T / (ms * 1e-3),
                layer_tflops=cfg.flops / (ms * 1e-3) / 1e12, layer_mfma_frac=cfg.flops / (ms * 1e-3) / PEAK_BF16_FLOPS)
     if g:
         ach = 2.0 * cfg.T * cfg.k * cfg.l * cfg.f / (g["avg_ms"] * 1e-3)
@@ -214,7 +216,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the mid_bf16 and prefill_nvfp4 lines")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (NVFP4 and mid prefill, latent router)")
     ap.add_argument("--expert-layout", choices=("tiled", "rowmajor"), default="tiled",
                     help="bf16 expert weights as packed by lmoe_pack_expert_weights (default) or row-major")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -289,9 +292,15 @@ def main():
         result["decode"] = decode(synth.CONFIGS["decode_bf16_zipf"], args.decode_steps, torch, B, synth,
                                   args.expert_layout)
     if not args.no_extra:
-        result["other_workloads"] = {n: secondary(n, max(args.steps // 2, 3), args.warmup, torch, B, synth,
-                                                  args.expert_layout)
-                                     for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload}
+        C = synth.CONFIGS
+        extra = [C[n] for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload]
+        extra.append(C["prefill_bf16"].with_(name="prefill_bf16_latent_router", router_latent=True))
+        result["other_workloads"] = {c.name: secondary(c, max(args.steps // 2, 3), args.warmup, torch, B, synth,
+                                                       args.expert_layout) for c in extra}
+        if not args.no_decode:
+            result["other_workloads"]["decode_latent_router"] = decode(
+                C["decode_bf16_zipf"].with_(name="decode_latent_router", router_latent=True),
+                args.decode_steps, torch, B, synth, args.expert_layout)
     if not args.no_cpu:
         log("bench: cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens, synth)

@@ -8,7 +8,8 @@
  * paragraph):
  *
  *   z_t   = W_down x_t                      hidden d -> latent l = d/4
- *   s_t   = W_r x_t + b                     router logits over E experts (reads x in d)
+ *   s_t   = W_r x_t + b                     router logits over E experts (reads x in d),
+ *     or  W_r z_t + b                       with dims.router_latent (reads the latent z)
  *   I_t   = top-k of s_t, ordered (logit desc, expert id asc)
  *   g_t   = softmax over the k selected logits
  *   y_tj  = W2_e (max(0, W1_e z_t))^2       routed expert e = I_t[j], ReLU^2 FFN in l
@@ -21,8 +22,9 @@
  *     never allocates device memory itself: scratch comes from the caller's
  *     workspace (see lmoe_workspace_bytes).
  *   - Weights are stored out x in, row-major (fan-in contiguous):
- *       W_down [l][d], W_r [E][d], W1 [E][f][l], W2 [E][l][f], W_up [d][l],
- *       W_s1 [f_s][d], W_s2 [d][f_s].  x and out are [T][d] row-major.
+ *       W_down [l][d], W_r [E][d] ([E][l] with dims.router_latent),
+ *       W1 [E][f][l], W2 [E][l][f], W_up [d][l], W_s1 [f_s][d], W_s2 [d][f_s].
+ *       x and out are [T][d] row-major.
  *   - Activation dtype (dims.act_dtype) is the storage type of x, W_down,
  *     W_r, W_up, W_s1, W_s2, out and of the latent intermediates.  Every
  *     product accumulates in fp32.  Router logits and gates are fp32.
@@ -70,11 +72,17 @@ extern "C" {
  *   act_dtype LMOE_F32 with expert_dtype LMOE_F32, or
  *   act_dtype LMOE_BF16 with expert_dtype LMOE_BF16, LMOE_BF16_TILED or
  *   LMOE_NVFP4.
+ * router_latent (0 or 1, LMOE_ERR_SHAPE otherwise): 0 = the router reads x in
+ *   d, W_r [E][d] (the overview's paragraph after the section 2.2 table keeps
+ *   the gate in d); 1 = the router reads the latent z as stored (act dtype),
+ *   W_r [E][l] (overview section 2.2 step 2 and the Super blog, "Latent
+ *   MoE", place routing in the latent space).
  */
 typedef struct lmoe_dims {
     int64_t T, d, l, E, k, f, f_s;
     int32_t act_dtype;
     int32_t expert_dtype;
+    int32_t router_latent;
 } lmoe_dims;
 
 /*
@@ -206,7 +214,8 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down,
 /*
  * Steps 1-4 (overview section 2.2 step 1; Ultra release news, 512 experts
  * with top-22): z = x W_down^T [T][l] (act dtype), logits = x W_r^T + b
- * [T][E] fp32, topk_idx [T][k] int32 in (logit desc, id asc) order,
+ * [T][E] fp32 (z W_r^T + b with dims.router_latent, from the stored z),
+ * topk_idx [T][k] int32 in (logit desc, id asc) order,
  * topk_gate [T][k] fp32 = softmax of the selected logits.  If shared is
  * non-NULL also hs = (max(0, x W_s1^T))^2 [T][f_s] (act dtype), the first
  * half of the shared expert (it reads the same x).  hs may be NULL iff

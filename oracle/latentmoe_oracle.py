@@ -13,8 +13,11 @@ paragraph):
   1. z_t = W_down x_t, the token's hidden vector (width d) projected down to
      the latent width l = d/4                                (overview s2.2 step 1)
   2. s_t = W_r x_t + b, router logits over E experts; the router reads x in d
-     (the routing gate stays in d per the paragraph after the s2.2 table;
-     the pages also place routing in l -- see the note on readings)
+     (the routing gate stays in d per the paragraph after the s2.2 table).
+     The pages also place routing in the latent space (s2.2 step 2; Super
+     blog, "Latent MoE"): with W_r of width l the router reads the latent
+     z_t as the layer stores it (rounded to the activation format), which
+     the width of W_r selects
   3. I_t = the k largest logits, ordered by (logit desc, expert id asc);
      Ultra uses E = 512, k = 22                           (release news, architecture)
   4. g_t = softmax over the k selected logits (the gate form is this layer's
@@ -30,7 +33,8 @@ paragraph):
   expert, inv = perm^-1.
 
 Precision: all arithmetic in float64 on the exact values of the stored
-inputs.  The one place floating point decides an integer (the top-k) takes
+inputs; the one intermediate taken at its stored precision is the latent z
+a latent router reads (the layer stores z before the router reads it).  The one place floating point decides an integer (the top-k) takes
 the decision on float32 logits, the precision the layer stores its logits in;
 ties in float32 are broken by the lower expert id.
 
@@ -57,6 +61,28 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     IEEE-754 binary32 with the lower 16 mantissa bits zero."""
     u32 = bits.astype(np.uint32) << np.uint32(16)
     return u32.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(v) -> np.ndarray:
+    """float64 values rounded to the nearest bf16 value (ties to the even
+    mantissa), returned as float64.  bf16 keeps the binary32 exponent range
+    and 8 significant bits, so this drops the low 45 of the 52 stored
+    fraction bits of a float64 with round-to-nearest-even (normal numbers of
+    the binary32 range, the only ones the layer produces)."""
+    u = np.asarray(v, dtype=np.float64).view(np.uint64)
+    drop = np.uint64(45)
+    lsb = (u >> drop) & np.uint64(1)
+    u = u + (np.uint64((1 << 44) - 1) + lsb)
+    u = u & ~np.uint64((1 << 45) - 1)
+    return u.view(np.float64)
+
+
+def store_round(v, like) -> np.ndarray:
+    """float64 values rounded to the storage format of the array `like`
+    (bf16 bit patterns or float32), returned as float64."""
+    if np.asarray(like).dtype == np.uint16:
+        return round_to_bf16(v)
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
 def as_f64(a) -> np.ndarray:
@@ -190,9 +216,21 @@ def permutation(idx: np.ndarray, E: int):
             inv.astype(np.int32))
 
 
+def router_input(x: np.ndarray, inp: dict) -> np.ndarray:
+    """What the router reads for the rows x: x itself when W_r is [E][d], or
+    the latent z = W_down x as stored (rounded to x's format) when W_r is
+    [E][l]."""
+    width = np.asarray(inp["W_r"]).shape[1]
+    if width == np.asarray(x).shape[1]:
+        return x
+    if width != np.asarray(inp["W_down"]).shape[0]:
+        raise ValueError("W_r width is neither d nor l")
+    return store_round(down_project(x, inp["W_down"]), x)
+
+
 def route(inp: dict, k: int):
     """Steps 2-4 for every token: logits (float32), idx, gates (float64)."""
-    s = router_logits(inp["x"], inp["W_r"], inp.get("b_r"))
+    s = router_logits(router_input(inp["x"], inp), inp["W_r"], inp.get("b_r"))
     idx = select_topk(s, k)
     return s, idx, gate_weights(s, idx)
 
@@ -210,7 +248,7 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
         x = x[np.asarray(tokens)]
     experts = experts or ExpertWeights(inp)
     z = down_project(x, inp["W_down"])
-    s = router_logits(x, inp["W_r"], inp.get("b_r"))
+    s = router_logits(router_input(x, inp), inp["W_r"], inp.get("b_r"))
     idx = select_topk(s, k)
     g = gate_weights(s, idx)
     n, l = z.shape

@@ -47,20 +47,37 @@ static int64_t max_tiles(const lmoe_dims& d) {
 }
 
 // x [W_down; W_r; W_s1]^T -> z, logits (+ bias), hs (the shared expert's
-// hidden layer, only with f_s > 0).
+// hidden layer, only with f_s > 0).  With a latent router the logits are
+// left to gemm_router.
 static DenseGemm gemm_in(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r, const float* bias,
                          const void* W_s1, void* z, float* logits, void* hs) {
     DenseGemm g{};
+    const int E = d.router_latent ? 0 : (int)d.E;  // router columns in this GEMM
     g.M = (int)d.T;
-    g.N = (int)(d.l + d.E + d.f_s);
+    g.N = (int)(d.l + E + d.f_s);
     g.nseg = 1;
     g.A[0] = x;
     g.lda[0] = d.d;
     g.K[0] = (int)d.d;
-    g.ngroups = d.f_s > 0 ? 3 : 2;
-    g.g[0] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
-    g.g[1] = NGroup{(int)d.l, (int)(d.l + d.E), {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
-    if (d.f_s > 0) g.g[2] = NGroup{(int)(d.l + d.E), g.N, {W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
+    g.ngroups = 0;
+    g.g[g.ngroups++] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
+    if (E > 0) g.g[g.ngroups++] = NGroup{(int)d.l, (int)d.l + E, {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
+    if (d.f_s > 0)
+        g.g[g.ngroups++] = NGroup{(int)d.l + E, g.N, {W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
+    return g;
+}
+
+// Latent router: z W_r^T (+ bias) -> logits, from the stored z.
+static DenseGemm gemm_router(const lmoe_dims& d, const void* z, const void* W_r, const float* bias, float* logits) {
+    DenseGemm g{};
+    g.M = (int)d.T;
+    g.N = (int)d.E;
+    g.nseg = 1;
+    g.A[0] = z;
+    g.lda[0] = d.l;
+    g.K[0] = (int)d.l;
+    g.ngroups = 1;
+    g.g[0] = NGroup{0, (int)d.E, {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
     return g;
 }
 
@@ -134,7 +151,10 @@ static Layout plan(const lmoe_dims& d) {
         const size_t a = dense_tail_split_bytes(gemm_in(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                                         nullptr, nullptr));
         const size_t b = dense_tail_split_bytes(gemm_out(d, nullptr, nullptr, nullptr, nullptr, nullptr));
+        const size_t r = d.router_latent ? dense_tail_split_bytes(gemm_router(d, nullptr, nullptr, nullptr, nullptr))
+                                         : 0;
         L.splitk_bytes = a > b ? a : b;
+        if (r > L.splitk_bytes) L.splitk_bytes = r;
     }
     L.splitk = take(L.splitk_bytes);
     if (expert_split_k(d)) {
@@ -214,6 +234,11 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
     const DenseGemm g = gemm_in(d, x, W_down, W_r, bias, sh ? sh->W_s1 : nullptr, z, logits, hs);
     hipError_t e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
     if (e != hipSuccess) return e;
+    if (d.router_latent) {
+        e = launch_dense_gemm(gemm_router(d, z, W_r, bias, logits), d.act_dtype, (int)d.T, ws + L.splitk,
+                              L.splitk_bytes, s);
+        if (e != hipSuccess) return e;
+    }
     return launch_topk_softmax(logits, (int)d.T, (int)d.E, (int)d.k, idx, gate, s);
 }
 
@@ -279,6 +304,7 @@ int lmoe_validate_dims(const lmoe_dims* d) {
     if (d->l * 4 != d->d) return LMOE_ERR_SHAPE;
     if (d->E < 1 || d->E > 1024) return LMOE_ERR_SHAPE;
     if (d->k < 1 || d->k > d->E) return LMOE_ERR_SHAPE;
+    if (d->router_latent != 0 && d->router_latent != 1) return LMOE_ERR_SHAPE;
     if (d->f < 64 || d->f % 64 != 0 || d->f > 65536) return LMOE_ERR_SHAPE;
     if (d->f_s < 0 || d->f_s % 64 != 0 || d->f_s > 262144) return LMOE_ERR_SHAPE;
     if (d->T * d->k > (int64_t)1 << 30) return LMOE_ERR_SHAPE;

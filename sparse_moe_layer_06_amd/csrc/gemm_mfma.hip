@@ -1052,18 +1052,19 @@ static DenseGemm sub_columns(const DenseGemm& g, int n0, int n1) {
     return h;
 }
 
-// Tail split of a many-tile dense GEMM: when the last round of 256 x 256
+// Tail split of a many-row dense GEMM: when the last round of 256 x 256
 // tiles over the CUs is at most half full and made of whole N-tile columns,
 // those columns run as a split-K GEMM of their own (one round of blocks, the
 // partials summed in split order), so the last round costs a fraction of a
-// tile instead of a whole one.  Returns the first tail column (N: no split)
-// and the partial-sum bytes the tail needs.
+// tile instead of a whole one.  A GEMM with at most half a round of tiles is
+// split whole.  Returns the first tail column (N: no split) and the
+// partial-sum bytes the tail needs.
 static int dense_tail_split(const DenseGemm& g, int cus, size_t* bytes) {
     constexpr int T = 256;
     const int tiles_m = (g.M + T - 1) / T, tiles_n = (g.N + T - 1) / T;
     const int tiles = tiles_m * tiles_n, rounds = tiles / cus, tail = tiles - rounds * cus;
     *bytes = 0;
-    if (rounds < 1 || tail == 0 || tail > cus / 2 || tail % tiles_m != 0) return g.N;
+    if (tail == 0 || tail > cus / 2 || tail % tiles_m != 0) return g.N;
     const int n0 = (tiles_n - tail / tiles_m) * T;
     for (int i = 0; i < g.ngroups; ++i) {  // the split must keep 8-column alignment of outputs
         const NGroup& G = g.g[i];
@@ -1105,8 +1106,10 @@ hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t sp
     const double r192 = (double)((tiles_m * ((g.N + 191) / 192) + cus - 1) / cus) * 0.75;
     if (r192 < 0.85 * r256) return run_dense<MfmaCfg<256, 192, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
     if (!split_tail) return run_dense<C256>(g, nullptr, 0, s);
-    const hipError_t e = run_dense<C256>(sub_columns(g, 0, n_tail), nullptr, 0, s);
-    if (e != hipSuccess) return e;
+    if (n_tail > 0) {
+        const hipError_t e = run_dense<C256>(sub_columns(g, 0, n_tail), nullptr, 0, s);
+        if (e != hipSuccess) return e;
+    }
     return run_dense<C256>(sub_columns(g, n_tail, g.N), splitk_ws, splitk_bytes, s);
 }
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to

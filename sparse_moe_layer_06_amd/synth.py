@@ -10,9 +10,9 @@ Recipe (one stream per tensor, so every tensor is reproducible alone):
     with tensor_id: x=0, W_down=1, W_r=2, W1=3, W2=4, W_up=5, W_s1=6,
     W_s2=7, W1 block scales=8, W2 block scales=9.
   * x ~ N(0, 1); every weight ~ N(0, 1/fan_in) with fan_in the input width
-    of that matrix (d for W_down, W_r, W_s1; l for W1, W_up; f for W2;
-    f_s for W_s2).  Draws are fp32, then rounded to bf16 (round to nearest
-    even) for bf16 tensors.
+    of that matrix (d for W_down, W_r, W_s1; l for W1, W_up and a latent
+    router's W_r; f for W2; f_s for W_s2).  Draws are fp32, then rounded to
+    bf16 (round to nearest even) for bf16 tensors.
   * The skewed-routing workload adds a per-expert router bias
     b_e = 2 * log(1 / (e + 1)), stored in fp32.
   * NVFP4 expert weights: W ~ N(0, 1/fan_in) in fp32, a block scale
@@ -46,7 +46,8 @@ class LayerDims:
     expert intermediate width f, shared-expert intermediate width f_s
     (0 = no shared expert).  act is the activation/storage dtype ('f32' or
     'bf16'); experts is the routed-expert weight format ('f32', 'bf16' or
-    'nvfp4'); zipf_bias adds the skewed router bias.
+    'nvfp4'); zipf_bias adds the skewed router bias; router_latent makes the
+    router read the latent z (W_r [E][l]) instead of x (W_r [E][d]).
     """
     name: str
     T: int
@@ -59,6 +60,7 @@ class LayerDims:
     act: str
     experts: str
     zipf_bias: bool = False
+    router_latent: bool = False
 
     def with_(self, **kw) -> "LayerDims":
         return dataclasses.replace(self, **kw)
@@ -67,7 +69,8 @@ class LayerDims:
     def flops(self) -> float:
         """Algorithmic FLOPs of one forward: projections, router, experts, shared."""
         T, d, l, E, k, f, fs = self.T, self.d, self.l, self.E, self.k, self.f, self.f_s
-        return 2.0 * T * d * l + 2.0 * T * d * E + 4.0 * T * k * l * f + 2.0 * T * l * d + 4.0 * T * d * fs
+        router_in = l if self.router_latent else d
+        return 2.0 * T * d * l + 2.0 * T * router_in * E + 4.0 * T * k * l * f + 2.0 * T * l * d + 4.0 * T * d * fs
 
 
 # The five workloads.  Sizes follow the Ultra layer (d = 8192, 512 experts,
@@ -187,7 +190,8 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
     inp: Dict[str, Optional[torch.Tensor]] = {}
     inp["x"] = _normal((T, d), 1.0, _gen(dev, seed, "x"), dev, act)
     inp["W_down"] = _normal((l, d), 1.0 / math.sqrt(d), _gen(dev, seed, "W_down"), dev, act)
-    inp["W_r"] = _normal((E, d), 1.0 / math.sqrt(d), _gen(dev, seed, "W_r"), dev, act)
+    r_in = l if cfg.router_latent else d
+    inp["W_r"] = _normal((E, r_in), 1.0 / math.sqrt(r_in), _gen(dev, seed, "W_r"), dev, act)
     if cfg.zipf_bias:
         e = torch.arange(E, dtype=torch.float64)
         inp["b_r"] = (2.0 * torch.log(1.0 / (e + 1.0))).to(torch.float32).to(dev)

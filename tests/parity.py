@@ -1,6 +1,8 @@
 """Comparison protocol between the HIP path and the CPU oracle.
 
-* logits: max-norm relative error <= 1e-5 (both fp32; different summation).
+* logits: max-norm relative error <= 1e-5 (both fp32; different summation);
+  1e-3 for a latent router with bf16 activations, whose near-tie gap is 2e-3
+  and gate tolerance 2e-3 (see LOGIT_TOL_LATENT_BF16).
 * top-k: the GPU's ordered selection must equal the oracle's except at near
   ties (logits within 1e-3), where several answers are correct: a different
   set only where the oracle gap between the k-th and (k+1)-th logit is
@@ -9,7 +11,9 @@
 * permutation: bit-exact against the oracle when every ordered selection matched;
   otherwise checked as the unique stable counting sort of the GPU's own
   selection (counts, offsets, order within segments, inverse).
-* gates, z, c, out: compared on the tokens whose selection matched, with
+* gates: absolute error <= 1e-5 (2e-3 for a latent router with bf16
+  activations) on the tokens whose selection matched.
+* z, c, out: compared on the tokens whose selection matched, with
   max-norm relative error (max |gpu - ref| / max |ref|) against the
   tolerance of the activation format: 1e-5 fp32, 2e-2 bf16, 3e-2 NVFP4
   experts (the oracle decodes the same NVFP4 bytes).
@@ -25,6 +29,35 @@ from sparse_moe_layer_06_amd import synth
 
 GAP_TOL = 1e-3
 LOGIT_TOL = 1e-5
+# A latent router reads z as stored: the GPU rounds its fp32 z to bf16, the
+# oracle its float64 z, and the two roundings differ by one bf16 ulp where the
+# fp32 accumulation error crosses a rounding boundary (33 of 131072 elements
+# at the decode size, emulated on the CPU).  Each such element moves a logit
+# by |W_r| * ulp(z): at most 6.4e-4 absolute there, 1.6e-4 of the logits'
+# max-norm without the bias.  So the logits are held to 1e-3 (max-norm) and
+# the routing to exact sets beyond a 2e-3 gap (twice the largest move).  A
+# gate moves by g_j (ds_j - sum_i g_i ds_i), at most twice the largest logit
+# move: 2e-3.
+LOGIT_TOL_LATENT_BF16 = 1e-3
+GAP_TOL_LATENT_BF16 = 2e-3
+GATE_TOL = 1e-5
+GATE_TOL_LATENT_BF16 = 2e-3
+
+
+def latent_bf16(cfg) -> bool:
+    return bool(cfg.router_latent) and cfg.act == "bf16"
+
+
+def logit_tol(cfg) -> float:
+    return LOGIT_TOL_LATENT_BF16 if latent_bf16(cfg) else LOGIT_TOL
+
+
+def gap_tol(cfg) -> float:
+    return GAP_TOL_LATENT_BF16 if latent_bf16(cfg) else GAP_TOL
+
+
+def gate_tol(cfg) -> float:
+    return GATE_TOL_LATENT_BF16 if latent_bf16(cfg) else GATE_TOL
 
 
 def out_tol(cfg) -> float:
@@ -73,13 +106,13 @@ def debug_buffers(cfg, T, device="cuda"):
     )
 
 
-def check_topk(gpu_idx: np.ndarray, s: np.ndarray, ref_idx: np.ndarray, k: int):
+def check_topk(gpu_idx: np.ndarray, s: np.ndarray, ref_idx: np.ndarray, k: int, tol: float = GAP_TOL):
     """Returns (ordered_same, set_same) masks over tokens.
 
     A token whose GPU selection differs from the oracle's must sit at a near
-    tie: if the sets differ, the oracle gap at rank k is <= 1e-3 and the GPU
-    set is a valid top-k within 1e-3; if only the order differs, every pair
-    of consecutive GPU picks is descending in the oracle logits within 1e-3.
+    tie: if the sets differ, the oracle gap at rank k is <= tol and the GPU
+    set is a valid top-k within tol; if only the order differs, every pair
+    of consecutive GPU picks is descending in the oracle logits within tol.
     """
     T, E = s.shape
     ordered_same = np.all(gpu_idx == ref_idx, axis=1)
@@ -93,12 +126,12 @@ def check_topk(gpu_idx: np.ndarray, s: np.ndarray, ref_idx: np.ndarray, k: int):
         sel = gpu_idx[t]
         assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < E, f"token {t}: bad ids"
         v = s[t, sel].astype(np.float64)
-        assert np.all(v[:-1] >= v[1:] - GAP_TOL), f"token {t}: order not descending within tolerance"
+        assert np.all(v[:-1] >= v[1:] - tol), f"token {t}: order not descending within tolerance"
         if not set_same[t]:
-            assert gap[t] <= GAP_TOL, f"token {t}: selection differs at gap {gap[t]}"
+            assert gap[t] <= tol, f"token {t}: selection differs at gap {gap[t]}"
             mask = np.zeros(E, bool)
             mask[sel] = True
-            assert s[t, mask].min() >= s[t, ~mask].max() - GAP_TOL, f"token {t}: not a valid top-k"
+            assert s[t, mask].min() >= s[t, ~mask].max() - tol, f"token {t}: not a valid top-k"
     return ordered_same, set_same
 
 
@@ -143,10 +176,10 @@ def run_and_check(cfg, inp, n_sample: int = 1 << 30, lazy_experts: bool = False,
     s, ref_idx, ref_gate = O.route(h, cfg.k)
     gpu_s = dbg["logits"].cpu().numpy()
     errs = dict(logits=rel_err(gpu_s, s))
-    assert errs["logits"] <= LOGIT_TOL, errs
+    assert errs["logits"] <= logit_tol(cfg), errs
 
     gpu_idx = dbg["topk_idx"].cpu().numpy()
-    ordered_same, same = check_topk(gpu_idx, s, ref_idx, cfg.k)
+    ordered_same, same = check_topk(gpu_idx, s, ref_idx, cfg.k, gap_tol(cfg))
     errs["tie_reorders"] = int((~ordered_same & same).sum())
     errs["tie_substitutions"] = int((~same).sum())
     check_permutation(cfg, dbg, gpu_idx, ref_idx, bool(ordered_same.all()))
@@ -158,7 +191,7 @@ def run_and_check(cfg, inp, n_sample: int = 1 << 30, lazy_experts: bool = False,
     og = np.take_along_axis(gpu_gate, np.argsort(gpu_idx, axis=1), 1)
     orf = np.take_along_axis(ref_gate, np.argsort(ref_idx, axis=1), 1)
     errs["gate"] = float(np.max(np.abs(og[same] - orf[same]))) if same.any() else 0.0
-    assert errs["gate"] <= 1e-5, errs
+    assert errs["gate"] <= gate_tol(cfg), errs
 
     tokens = sample_tokens(T, n_sample)
     tokens = tokens[same[tokens]]

@@ -52,6 +52,12 @@ SMALL = {
     "k100_E256": TINY.with_(name="k100_E256", T=16, d=256, l=64, E=256, k=100, f=64, act="bf16",
                             experts="bf16"),
     "E1024": TINY.with_(name="E1024", T=32, d=256, l=64, E=1024, k=8, f=64, act="bf16", experts="bf16"),
+    # the router reading the stored latent z (W_r [E][l])
+    "latent_bf16": TINY.with_(name="latent_bf16", T=150, d=512, l=128, E=24, k=4, f=192, f_s=128,
+                              act="bf16", experts="bf16", router_latent=True),
+    "latent_f32": TINY.with_(name="latent_f32", T=70, E=12, k=3, f_s=64, router_latent=True),
+    "latent_nvfp4_zipf": TINY.with_(name="latent_nvfp4_zipf", T=40, d=256, l=64, E=32, k=5, f=128, f_s=0,
+                                    act="bf16", experts="nvfp4", zipf_bias=True, router_latent=True),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
@@ -115,7 +121,7 @@ def test_exact_logit_ties_break_to_lower_id():
 
 
 def test_staged_entry_points_compose_to_forward():
-    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide"):
+    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide", "latent_bf16"):
         cfg = SMALL[name]
         log(f"case staged {name}")
         inp = small_inputs(cfg)
@@ -236,6 +242,23 @@ def test_tiled_experts_full_size_match_row_major():
             P.run_and_check(cfg_t, inp, lazy_experts=True, report=log, gpu_inp=inp_t)
         del inp, inp_t, ref, out
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_decode_latent_router_full_size():
+    cfg = CFG["decode_bf16_zipf"].with_(name="decode_latent_router", router_latent=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_latent_router_sampled():
+    # many-token latent router: its own split-K GEMM (64 tiles of 256 x 256)
+    cfg = CFG["prefill_bf16"].with_(name="prefill_latent_router", T=2048, router_latent=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=8, lazy_experts=True, report=log)
 
 
 @pytest.mark.timeout(900)

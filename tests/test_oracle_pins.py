@@ -34,6 +34,8 @@ SMALL_BF16 = TINY.with_(name="small_bf16", T=48, d=128, l=32, E=12, k=3, f=64, f
 SMALL_NVFP4 = TINY.with_(name="small_nvfp4", T=40, d=128, l=32, E=8, k=2, f=64, f_s=0,
                          act="bf16", experts="nvfp4")
 SMALL_ZIPF = SMALL_BF16.with_(name="small_zipf", zipf_bias=True, f_s=0)
+SMALL_LATENT = SMALL_BF16.with_(name="small_latent", router_latent=True)
+TINY_LATENT = TINY.with_(name="tiny_latent", router_latent=True)
 
 
 # ---------------------------------------------------------------------------
@@ -197,7 +199,7 @@ def dense_bruteforce(inp, k):
     the top-k set and renormalised; one up-projection per expert."""
     x = O.as_f64(inp["x"])
     z = x @ O.as_f64(inp["W_down"]).T
-    s = O.router_logits(inp["x"], inp["W_r"], inp.get("b_r")).astype(np.float64)
+    s = O.router_logits(O.router_input(inp["x"], inp), inp["W_r"], inp.get("b_r")).astype(np.float64)
     E = s.shape[1]
     W_up = O.as_f64(inp["W_up"])
     ew = O.ExpertWeights(inp)
@@ -219,7 +221,7 @@ def dense_bruteforce(inp, k):
     return out
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_ZIPF,
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_ZIPF, SMALL_LATENT, TINY_LATENT,
                                  TINY.with_(k=1), TINY.with_(E=5, k=5)], ids=lambda c: f"{c.name}-E{c.E}k{c.k}")
 def test_sparse_equals_dense_bruteforce(cfg):
     inp = host_inputs(cfg)
@@ -390,3 +392,58 @@ def test_planted_tie_mistake_is_caught_by_rank_pin(monkeypatch):
     idx = O.select_topk(s, 2)
     rank = brute_force_topk_set(s[0], 2)
     assert not np.array_equal(idx[0], np.argsort(rank)[:2])
+
+
+# ---------------------------------------------------------------------------
+# Latent router (the pages' other reading: routing in the latent space)
+# ---------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch():
+    # float32 values over a wide exponent range, plus exact midpoints between
+    # neighbouring bf16 values (both parities of the lower neighbour)
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(1_000_000).astype(np.float32)
+    v *= np.exp2(rng.integers(-30, 30, v.size)).astype(np.float32)
+    lo = torch.from_numpy(v[:4096]).to(torch.bfloat16).to(torch.float32).numpy()
+    step = np.exp2(np.floor(np.log2(np.abs(lo))) - 7).astype(np.float32)
+    mid = (lo + np.sign(lo) * step / 2).astype(np.float32)  # exactly halfway
+    allv = np.concatenate([v, mid, -mid])
+    got = O.round_to_bf16(allv.astype(np.float64))
+    ref = torch.from_numpy(allv).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(O.round_to_bf16(got), got)  # idempotent on bf16 values
+
+
+def test_latent_router_reads_the_latent():
+    # Integer inputs keep z = W_down x exact in bf16, so the stored latent is
+    # z itself, and W_r z = (W_r W_down) x exactly: routing in l must equal
+    # routing in d with the folded weights.
+    rng = np.random.default_rng(3)
+    T, d, l, E = 20, 64, 16, 10
+    x = rng.integers(-2, 3, (T, d)).astype(np.float32)
+    W_down = rng.integers(-1, 2, (l, d)).astype(np.float32)
+    W_r = rng.integers(-3, 4, (E, l)).astype(np.float32) / 4
+    b = rng.standard_normal(E).astype(np.float32)
+    lat = {"x": x, "W_down": W_down, "W_r": W_r, "b_r": b}
+    folded = {"x": x, "W_down": W_down, "W_r": (W_r.astype(np.float64) @ W_down).astype(np.float32), "b_r": b}
+    s_lat, i_lat, g_lat = O.route(lat, 4)
+    s_d, i_d, g_d = O.route(folded, 4)
+    assert np.array_equal(s_lat, s_d) and np.array_equal(i_lat, i_d) and np.array_equal(g_lat, g_d)
+    # a W_r of neither width is rejected
+    with pytest.raises(ValueError):
+        O.route({"x": x, "W_down": W_down, "W_r": W_r[:, :7], "b_r": b}, 4)
+
+
+def test_latent_router_rounds_what_it_reads():
+    # bf16 activations: the router reads z rounded to bf16; with the folded
+    # weights in float64 the logits differ (rounding moved z), and with z
+    # rounded first they agree -- the router input is the stored latent.
+    cfg = SMALL_LATENT.with_(f_s=0)
+    inp = host_inputs(cfg)
+    z = O.down_project(inp["x"], inp["W_down"])
+    zr = O.router_input(inp["x"], inp)
+    assert np.array_equal(zr, O.round_to_bf16(z))
+    assert not np.array_equal(zr, z)
+    f32 = host_inputs(TINY_LATENT)
+    assert np.array_equal(O.router_input(f32["x"], f32),
+                          O.down_project(f32["x"], f32["W_down"]).astype(np.float32).astype(np.float64))
