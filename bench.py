@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LatentMoE fwd tokens/s + % MFMA peak (prefill) / % HBM BW (decode), d=8192"
 PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
+PEAK_FP8_FLOPS = 5.0e15    # MI355X dense fp8 MFMA
 PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_prefill_bf16_traffic.json")
 
@@ -165,13 +166,19 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
     g = kernels.get(gname)
     res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
-                        f"{cfg.experts} experts, router reads {'z (latent)' if cfg.router_latent else 'x'}",
+                        f"{cfg.experts} experts, router reads {'z (latent)' if cfg.router_latent else 'x'}"
+                        f"{', FP8 shared expert (E4M3 x E4M3 MFMA)' if cfg.shared_fp8 else ''}",
                ms_per_step=ms, tokens_per_s=cfg.T / (ms * 1e-3),
                layer_tflops=cfg.flops / (ms * 1e-3) / 1e12, layer_mfma_frac=cfg.flops / (ms * 1e-3) / PEAK_BF16_FLOPS)
     if g:
         ach = 2.0 * cfg.T * cfg.k * cfg.l * cfg.f / (g["avg_ms"] * 1e-3)
         res["grouped"] = dict(kernel=gname, avg_launch_ms=g["avg_ms"], achieved_tflops=ach / 1e12,
                               mfma_frac=ach / PEAK_BF16_FLOPS)
+    f8 = kernels.get("fp8_gemm")
+    if f8 and cfg.f_s > 0:  # the shared expert's two products, 2 T d f_s FLOPs each
+        ach = 2.0 * cfg.T * cfg.d * cfg.f_s / (f8["avg_ms"] * 1e-3)
+        res["fp8_gemm"] = dict(avg_launch_ms=f8["avg_ms"], launches_per_step=f8["launches_per_step"],
+                               achieved_tflops=ach / 1e12, mfma_frac_fp8=ach / PEAK_FP8_FLOPS)
     del inp, out
     torch.cuda.empty_cache()
     return res
@@ -295,6 +302,7 @@ def main():
         C = synth.CONFIGS
         extra = [C[n] for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload]
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_latent_router", router_latent=True))
+        extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_shared", shared_fp8=True))
         result["other_workloads"] = {c.name: secondary(c, max(args.steps // 2, 3), args.warmup, torch, B, synth,
                                                        args.expert_layout) for c in extra}
         if not args.no_decode:

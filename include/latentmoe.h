@@ -62,6 +62,7 @@ extern "C" {
 #define LMOE_BF16  1  /* bfloat16 */
 #define LMOE_NVFP4 2  /* routed-expert weights only, see lmoe_experts */
 #define LMOE_BF16_TILED 3  /* routed-expert bf16 weights in the tiled layout, see lmoe_pack_expert_weights */
+#define LMOE_FP8_E4M3 4    /* shared-expert weights only, see lmoe_shared */
 
 /*
  * Layer sizes.  Constraints (LMOE_ERR_SHAPE otherwise):
@@ -77,12 +78,17 @@ extern "C" {
  *   the gate in d); 1 = the router reads the latent z as stored (act dtype),
  *   W_r [E][l] (overview section 2.2 step 2 and the Super blog, "Latent
  *   MoE", place routing in the latent space).
+ * shared_dtype: the shared expert's weight format, the activation dtype or,
+ *   with bf16 activations, LMOE_FP8_E4M3 (the Ultra release news lists FP8
+ *   shared experts; see lmoe_shared; f_s must then be a multiple of 128).
+ *   LMOE_ERR_DTYPE otherwise; it is checked even when f_s == 0.
  */
 typedef struct lmoe_dims {
     int64_t T, d, l, E, k, f, f_s;
     int32_t act_dtype;
     int32_t expert_dtype;
     int32_t router_latent;
+    int32_t shared_dtype;
 } lmoe_dims;
 
 /*
@@ -115,10 +121,20 @@ typedef struct lmoe_experts {
 
 /* Shared expert in d (overview section 2.2, paragraph after the table):
  * W_s1 [f_s][d], W_s2 [d][f_s] in the activation dtype.  Pass NULL to the
- * entry points (and f_s = 0) for a layer without one. */
+ * entry points (and f_s = 0) for a layer without one.
+ * With dims.shared_dtype = LMOE_FP8_E4M3, W_s1 and W_s2 are E4M3 (FN) codes,
+ * one byte per weight, with one fp32 scale per output row: W_s1_scale [f_s],
+ * W_s2_scale [d] (weight = E4M3(code) * scale).  The shared expert's inputs
+ * are then quantised per token as lmoe_quantize_rows_fp8 does (x before the
+ * first matrix, the hidden layer hs before the second) and both products run
+ * as fp8 x fp8 MFMA GEMMs with fp32 accumulation; hs stays bf16 in between,
+ * and the second product is added to the bf16 up-projection output.  The
+ * scale fields are ignored for bf16 weights. */
 typedef struct lmoe_shared {
     const void* W_s1;
     const void* W_s2;
+    const float* W_s1_scale;
+    const float* W_s2_scale;
 } lmoe_shared;
 
 /*
@@ -192,6 +208,19 @@ int lmoe_timing_stop(lmoe_kernel_time* out, int capacity, int* count);
  */
 int lmoe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const void* W, void* packed,
                              void* stream);
+
+/*
+ * Per-row FP8 quantisation of a bf16 matrix src [rows][cols] (row-major):
+ * scales[r] = max_c |src[r][c]| / 448 in fp32 (1 for an all-zero row), and
+ * codes[r][c] = E4M3(src[r][c] / scales[r]), the fp32 quotient rounded to the
+ * nearest E4M3 (FN) value, ties to even.  This is how the fp8 shared expert
+ * quantises its inputs (one scale per token); callers may use it for FP8
+ * weights (one scale per output row).  codes [rows][cols] uint8, scales
+ * [rows] fp32.  rows >= 1, cols a positive multiple of 8 up to 2^20
+ * (LMOE_ERR_SHAPE); pointers 16-byte aligned.  Asynchronous on stream.
+ */
+int lmoe_quantize_rows_fp8(int64_t rows, int64_t cols, const void* src, uint8_t* codes, float* scales,
+                           void* stream);
 
 /* ---- the layer ------------------------------------------------------- */
 

@@ -27,7 +27,12 @@ paragraph):
   6. c_t = sum_j g_{t,j} y_{t,j}, then out_t = W_up c_t, back to width d
                                                             (overview s2.2 step 3)
   7. optional shared expert in d: out_t += W_s2 (max(0, W_s1 x_t))^2
-                                   (overview s2.2, paragraph after the table)
+                                   (overview s2.2, paragraph after the table).
+     With FP8 shared weights (the Ultra release news lists FP8 shared
+     experts): W_s1, W_s2 are E4M3 codes times one scale per output row, and
+     each of the shared expert's inputs (x_t, then its hidden layer as stored
+     in bf16) is quantised per token to E4M3 with scale max|v|/448 before
+     its product
   Integer side: counts[e] = #{(t, j): I_t[j] = e}, offsets = exclusive prefix
   sum of counts, perm = stable counting sort of the row-major (t, j) pairs by
   expert, inv = perm^-1.
@@ -116,6 +121,42 @@ def e4m3_value(byte) -> np.ndarray:
     mag = np.where(e == 0, np.exp2(-6.0) * (m / 8.0), np.exp2(e - 7.0) * (1.0 + m / 8.0))
     mag = np.where((e == 15) & (m == 7), np.nan, mag)
     return np.where(sign == 1, -mag, mag)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 (FN) code of each value, ties to the even mantissa:
+    normal numbers 2^(e-7) (1 + m/8), subnormals 2^-6 m/8.  Magnitudes must
+    stay below 464 (the midpoint above the largest finite value 448)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a >= 464.0) or not np.all(np.isfinite(v)):
+        raise ValueError("value outside the E4M3 range")
+    frac, p = np.frexp(a)                     # a = frac * 2^p, frac in [0.5, 1)
+    e = p.astype(np.int64) - 1                # a = (2 frac) * 2^e
+    m = np.rint((2.0 * frac - 1.0) * 8.0)     # mantissa steps, ties to even
+    carry = m == 8.0
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0.0, m)
+    field = e + 7
+    sub = field < 1                           # below 2^-6: steps of 2^-9
+    q = np.rint(a * 512.0)
+    field = np.where(sub, np.where(q == 8.0, 1, 0), field)
+    m = np.where(sub, np.where(q == 8.0, 0.0, q), m)
+    code = (field.astype(np.int64) << 3) | m.astype(np.int64)
+    code = np.where(a == 0.0, 0, code)
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_rows_fp8(v) -> tuple:
+    """Per-row E4M3 quantisation of float32-representable values [n][K]:
+    scale = max|row| / 448 and code = E4M3(v / scale), both quotients taken in
+    float32 (the precision the layer takes this decision in); scale 1 for an
+    all-zero row.  Returns (codes uint8 [n][K], scales float32 [n])."""
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(v32), axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (v32 / scale[:, None]).astype(np.float32)
+    return e4m3_encode(q.astype(np.float64)), scale
 
 
 def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, tensor_scale: float) -> np.ndarray:
@@ -259,6 +300,22 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
             c[t] += g[t, j] * expert_ffn(z[t], W1_e, W2_e)
     out = c @ as_f64(inp["W_up"]).T
     if inp.get("W_s1") is not None:
-        hs = np.maximum(as_f64(x) @ as_f64(inp["W_s1"]).T, 0.0) ** 2
-        out = out + hs @ as_f64(inp["W_s2"]).T
+        out = out + shared_expert(x, inp)
     return dict(z=z, logits=s, idx=idx, gate=g, c=c, out=out)
+
+
+def shared_expert(x: np.ndarray, inp: dict) -> np.ndarray:
+    """Step 7 for the rows x: W_s2 (max(0, W_s1 x))^2; with E4M3 weights
+    (uint8 codes, per-row scales) both products take per-token E4M3 inputs:
+    x, then the hidden layer as stored (bf16)."""
+    W1, W2 = np.asarray(inp["W_s1"]), np.asarray(inp["W_s2"])
+    if W1.dtype != np.uint8:
+        hs = np.maximum(as_f64(x) @ as_f64(W1).T, 0.0) ** 2
+        return hs @ as_f64(W2).T
+    s1 = np.asarray(inp["W_s1_scale"], dtype=np.float64)
+    s2 = np.asarray(inp["W_s2_scale"], dtype=np.float64)
+    qx, sx = quantize_rows_fp8(as_f64(x))
+    pre = (e4m3_value(qx) @ e4m3_value(W1).T) * sx.astype(np.float64)[:, None] * s1[None, :]
+    hs = round_to_bf16(np.maximum(pre, 0.0) ** 2)
+    qh, sh = quantize_rows_fp8(hs)
+    return (e4m3_value(qh) @ e4m3_value(W2).T) * sh.astype(np.float64)[:, None] * s2[None, :]

@@ -24,19 +24,22 @@ LMOE_ERR_ALIGN = -4
 LMOE_ERR_WORKSPACE = -5
 LMOE_ERR_HIP = -6
 
-LMOE_F32, LMOE_BF16, LMOE_NVFP4, LMOE_BF16_TILED = 0, 1, 2, 3
-DTYPE_CODE = {"f32": LMOE_F32, "bf16": LMOE_BF16, "nvfp4": LMOE_NVFP4, "bf16_tiled": LMOE_BF16_TILED}
+LMOE_F32, LMOE_BF16, LMOE_NVFP4, LMOE_BF16_TILED, LMOE_FP8_E4M3 = 0, 1, 2, 3, 4
+DTYPE_CODE = {"f32": LMOE_F32, "bf16": LMOE_BF16, "nvfp4": LMOE_NVFP4, "bf16_tiled": LMOE_BF16_TILED,
+              "fp8": LMOE_FP8_E4M3}
 
 EXPORTED = ["lmoe_workspace_bytes", "lmoe_validate_dims", "lmoe_strerror", "lmoe_last_hip_error",
             "latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
-            "lmoe_combine_up", "lmoe_timing_start", "lmoe_timing_stop", "lmoe_pack_expert_weights"]
+            "lmoe_combine_up", "lmoe_timing_start", "lmoe_timing_stop", "lmoe_pack_expert_weights",
+            "lmoe_quantize_rows_fp8"]
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("l", ctypes.c_int64),
                 ("E", ctypes.c_int64), ("k", ctypes.c_int64), ("f", ctypes.c_int64),
                 ("f_s", ctypes.c_int64), ("act_dtype", ctypes.c_int32),
-                ("expert_dtype", ctypes.c_int32), ("router_latent", ctypes.c_int32)]
+                ("expert_dtype", ctypes.c_int32), ("router_latent", ctypes.c_int32),
+                ("shared_dtype", ctypes.c_int32)]
 
 
 class Experts(ctypes.Structure):
@@ -45,7 +48,8 @@ class Experts(ctypes.Structure):
 
 
 class Shared(ctypes.Structure):
-    _fields_ = [("W_s1", ctypes.c_void_p), ("W_s2", ctypes.c_void_p)]
+    _fields_ = [("W_s1", ctypes.c_void_p), ("W_s2", ctypes.c_void_p), ("W_s1_scale", ctypes.c_void_p),
+                ("W_s2_scale", ctypes.c_void_p)]
 
 
 class Debug(ctypes.Structure):
@@ -98,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.lmoe_timing_stop.restype = ctypes.c_int
         L.lmoe_pack_expert_weights.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
         L.lmoe_pack_expert_weights.restype = ctypes.c_int
+        L.lmoe_quantize_rows_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, vp]
+        L.lmoe_quantize_rows_fp8.restype = ctypes.c_int
         for n in ("latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
                   "lmoe_combine_up"):
             getattr(L, n).restype = ctypes.c_int
@@ -119,7 +125,8 @@ def _check(status: int, what: str):
 
 def dims_of(cfg: LayerDims, T: Optional[int] = None) -> Dims:
     return Dims(T if T is not None else cfg.T, cfg.d, cfg.l, cfg.E, cfg.k, cfg.f, cfg.f_s,
-                DTYPE_CODE[cfg.act], DTYPE_CODE[cfg.experts], 1 if cfg.router_latent else 0)
+                DTYPE_CODE[cfg.act], DTYPE_CODE[cfg.experts], 1 if cfg.router_latent else 0,
+                DTYPE_CODE["fp8" if cfg.shared_fp8 else cfg.act])
 
 
 def _p(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -178,7 +185,20 @@ def pack_experts(cfg: LayerDims, inp, stream=None):
 def shared_struct(inp) -> Optional[Shared]:
     if inp.get("W_s1") is None:
         return None
-    return Shared(_p(inp["W_s1"]), _p(inp["W_s2"]))
+    return Shared(_p(inp["W_s1"]), _p(inp["W_s2"]), _p(inp.get("W_s1_scale")), _p(inp.get("W_s2_scale")))
+
+
+def quantize_rows_fp8(src: torch.Tensor, stream=None):
+    """(codes uint8 [rows][cols], scales fp32 [rows]) of a contiguous bf16
+    matrix, per row: scale = max|v| / 448, code = E4M3(v / scale)."""
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or not src.is_contiguous():
+        raise LatentMoEError(LMOE_ERR_DTYPE, "quantize_rows_fp8 needs a contiguous [rows][cols] bf16 matrix")
+    rows, cols = src.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=src.device)
+    _check(lib().lmoe_quantize_rows_fp8(rows, cols, _p(src), _p(codes), _p(scales), _stream(stream)),
+           "lmoe_quantize_rows_fp8")
+    return codes, scales
 
 
 def _byref_opt(s):

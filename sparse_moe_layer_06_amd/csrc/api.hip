@@ -46,15 +46,23 @@ static int64_t max_tiles(const lmoe_dims& d) {
     return (n + bm - 1) / bm + (d.E < n ? d.E : n);
 }
 
+// The shared expert with FP8 weights runs its two products as fp8 GEMMs of
+// their own; with weights in the activation dtype it rides in the dense
+// GEMMs (W_s1 as extra columns of the first, W_s2 as a second K segment of
+// the last).
+static bool shared_fp8(const lmoe_dims& d) { return d.f_s > 0 && d.shared_dtype == LMOE_FP8_E4M3; }
+static bool shared_dense(const lmoe_dims& d) { return d.f_s > 0 && d.shared_dtype != LMOE_FP8_E4M3; }
+
 // x [W_down; W_r; W_s1]^T -> z, logits (+ bias), hs (the shared expert's
-// hidden layer, only with f_s > 0).  With a latent router the logits are
-// left to gemm_router.
+// hidden layer, only with f_s > 0 in the activation dtype).  With a latent
+// router the logits are left to gemm_router.
 static DenseGemm gemm_in(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r, const float* bias,
                          const void* W_s1, void* z, float* logits, void* hs) {
     DenseGemm g{};
     const int E = d.router_latent ? 0 : (int)d.E;  // router columns in this GEMM
+    const int fs = shared_dense(d) ? (int)d.f_s : 0;
     g.M = (int)d.T;
-    g.N = (int)(d.l + E + d.f_s);
+    g.N = (int)d.l + E + fs;
     g.nseg = 1;
     g.A[0] = x;
     g.lda[0] = d.d;
@@ -62,8 +70,7 @@ static DenseGemm gemm_in(const lmoe_dims& d, const void* x, const void* W_down, 
     g.ngroups = 0;
     g.g[g.ngroups++] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
     if (E > 0) g.g[g.ngroups++] = NGroup{(int)d.l, (int)d.l + E, {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
-    if (d.f_s > 0)
-        g.g[g.ngroups++] = NGroup{(int)d.l + E, g.N, {W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
+    if (fs > 0) g.g[g.ngroups++] = NGroup{(int)d.l + E, g.N, {W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
     return g;
 }
 
@@ -85,25 +92,26 @@ static DenseGemm gemm_router(const lmoe_dims& d, const void* z, const void* W_r,
 static DenseGemm gemm_out(const lmoe_dims& d, const void* c, const void* hs, const void* W_up, const void* W_s2,
                           void* out) {
     DenseGemm g{};
+    const bool two = shared_dense(d);
     g.M = (int)d.T;
     g.N = (int)d.d;
-    g.nseg = d.f_s > 0 ? 2 : 1;
+    g.nseg = two ? 2 : 1;
     g.A[0] = c;
     g.lda[0] = d.l;
     g.K[0] = (int)d.l;
-    if (d.f_s > 0) {
+    if (two) {
         g.A[1] = hs;
         g.lda[1] = d.f_s;
         g.K[1] = (int)d.f_s;
     }
     g.ngroups = 1;
-    g.g[0] = NGroup{0, (int)d.d, {W_up, d.f_s > 0 ? W_s2 : nullptr}, EPI_STORE, out, d.d, nullptr};
+    g.g[0] = NGroup{0, (int)d.d, {W_up, two ? W_s2 : nullptr}, EPI_STORE, out, d.d, nullptr};
     return g;
 }
 
 struct Layout {
     size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
-        c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, total;
+        c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, q_x, s_x, q_h, s_h, total;
 };
 
 // Whether the few-rows expert GEMMs may take the split-K 64 x 256 tiles
@@ -157,6 +165,12 @@ static Layout plan(const lmoe_dims& d) {
         if (r > L.splitk_bytes) L.splitk_bytes = r;
     }
     L.splitk = take(L.splitk_bytes);
+    if (shared_fp8(d)) {  // E4M3 codes and per-token scales of x and hs
+        L.q_x = take((size_t)d.T * d.d);
+        L.s_x = take((size_t)d.T * 4);
+        L.q_h = take((size_t)d.T * d.f_s);
+        L.s_h = take((size_t)d.T * 4);
+    }
     if (expert_split_k(d)) {
         const int64_t widest_n = d.f > d.l ? d.f : d.l;
         L.sk_count_len = (size_t)(max_tiles(d) * ((widest_n + kSkBN - 1) / kSkBN));
@@ -202,6 +216,7 @@ static int check_experts(const lmoe_dims& d, const lmoe_experts* x) {
 
 static int check_shared(const lmoe_dims& d, const lmoe_shared* sh) {
     if ((sh != nullptr) != (d.f_s > 0)) return LMOE_ERR_SHAPE;
+    if (sh && shared_fp8(d)) return check_ptrs({sh->W_s1, sh->W_s2, sh->W_s1_scale, sh->W_s2_scale});
     if (sh) return check_ptrs({sh->W_s1, sh->W_s2});
     return LMOE_OK;
 }
@@ -237,6 +252,27 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
     if (d.router_latent) {
         e = launch_dense_gemm(gemm_router(d, z, W_r, bias, logits), d.act_dtype, (int)d.T, ws + L.splitk,
                               L.splitk_bytes, s);
+        if (e != hipSuccess) return e;
+    }
+    if (shared_fp8(d)) {  // hs = relu(s_x * (q_x W_s1^T) * s_w1)^2
+        uint8_t* qx = (uint8_t*)(ws + L.q_x);
+        float* sx = (float*)(ws + L.s_x);
+        e = launch_quantize_rows_fp8((const uint16_t*)x, d.T, (int)d.d, d.d, qx, sx, s);
+        if (e != hipSuccess) return e;
+        Fp8Gemm f{};
+        f.M = (int)d.T;
+        f.N = (int)d.f_s;
+        f.K = (int)d.d;
+        f.A = qx;
+        f.lda = d.d;
+        f.a_scale = sx;
+        f.B = (const uint8_t*)sh->W_s1;
+        f.ldb = d.d;
+        f.b_scale = sh->W_s1_scale;
+        f.epi = EPI_RELU2;
+        f.C = (uint16_t*)hs;
+        f.ldc = d.f_s;
+        e = launch_fp8_gemm(f, s);
         if (e != hipSuccess) return e;
     }
     return launch_topk_softmax(logits, (int)d.T, (int)d.E, (int)d.k, idx, gate, s);
@@ -288,7 +324,27 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
     hipError_t e = launch_combine(Y, inv, gate, (int)d.T, (int)d.k, (int)d.l, d.act_dtype, c, s);
     if (e != hipSuccess) return e;
     const DenseGemm g = gemm_out(d, c, hs, W_up, sh ? sh->W_s2 : nullptr, out);
-    return launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
+    e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
+    if (e != hipSuccess || !shared_fp8(d)) return e;
+    // out += s_h * (q_h W_s2^T) * s_w2, added to the bf16 up-projection
+    uint8_t* qh = (uint8_t*)(ws + L.q_h);
+    float* sh_scale = (float*)(ws + L.s_h);
+    e = launch_quantize_rows_fp8((const uint16_t*)hs, d.T, (int)d.f_s, d.f_s, qh, sh_scale, s);
+    if (e != hipSuccess) return e;
+    Fp8Gemm f{};
+    f.M = (int)d.T;
+    f.N = (int)d.d;
+    f.K = (int)d.f_s;
+    f.A = qh;
+    f.lda = d.f_s;
+    f.a_scale = sh_scale;
+    f.B = (const uint8_t*)sh->W_s2;
+    f.ldb = d.f_s;
+    f.b_scale = sh->W_s2_scale;
+    f.epi = EPI_ADD_BF16;
+    f.C = (uint16_t*)out;
+    f.ldc = d.d;
+    return launch_fp8_gemm(f, s);
 }
 
 }  // namespace lmoe
@@ -317,6 +373,9 @@ int lmoe_validate_dims(const lmoe_dims* d) {
     } else {
         return LMOE_ERR_DTYPE;
     }
+    if (d->shared_dtype != d->act_dtype && !(d->act_dtype == LMOE_BF16 && d->shared_dtype == LMOE_FP8_E4M3))
+        return LMOE_ERR_DTYPE;
+    if (d->shared_dtype == LMOE_FP8_E4M3 && d->f_s % 128 != 0) return LMOE_ERR_SHAPE;  // fp8 K step
     return LMOE_OK;
 }
 
@@ -348,6 +407,15 @@ int lmoe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const void* 
     const uintptr_t a = (uintptr_t)W, b = (uintptr_t)packed, n = (uintptr_t)(E * rows * cols * 2);
     if (a < b + n && b < a + n) return LMOE_ERR_SHAPE;  // overlapping buffers
     return hip_status(launch_pack_experts(W, packed, E, (int)rows, (int)cols, (hipStream_t)stream));
+}
+
+int lmoe_quantize_rows_fp8(int64_t rows, int64_t cols, const void* src, uint8_t* codes, float* scales,
+                           void* stream) {
+    if (rows < 1 || rows > ((int64_t)1 << 31) || cols < 8 || cols % 8 != 0 || cols > (1 << 20))
+        return LMOE_ERR_SHAPE;
+    LMOE_TRY(check_ptrs({src, codes, scales}));
+    return hip_status(launch_quantize_rows_fp8((const uint16_t*)src, rows, (int)cols, cols, codes, scales,
+                                               (hipStream_t)stream));
 }
 
 int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,

@@ -59,6 +59,15 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
+// 32x32x64 fp8 (E4M3 x E4M3) MFMA, fp32 accumulate: acc += A(32x64) * B(64x32).
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, each as 32
+// consecutive k values starting at 32 * (l / 32) (checked on the device).
+// The block-scale operands are unused (0 selects the unscaled form).
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16_t mfma32x32x64_fp8(const i32x8_t& a, const i32x8_t& b, f32x16_t acc) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
     return __builtin_bit_cast(bf16x8_t, v);
 }

@@ -109,7 +109,6 @@ __device__ __forceinline__ void dma16(const void* src, u32x4_t* dst) {
 // in flight (it cannot count those across loop iterations and would wait for
 // all of them).  Reads only; the pointer is made uniform explicitly.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
@@ -216,6 +215,46 @@ __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u
     });
 }
 
+// fp8 variant of mma_tile: the LDS tile holds K step 128 fp8 codes per row
+// (the same 8 chunks of 16 B as a K step of 64 bf16), multiplied in two
+// sub-steps of K 64; a lane's fragment is two adjacent chunks (32 codes).
+template <class C>
+__device__ __forceinline__ void mma_tile_fp8(const u32x4_t* __restrict__ As, const u32x4_t* __restrict__ Bs,
+                                             f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
+    constexpr int KS = 2, NM = C::TM * C::TN, NR = 2 * (C::TM + C::TN);
+    i32x8_t af[2][C::TM], bfr[2][C::TN];
+    auto frag = [&](const u32x4_t* T, int row, int ch) __attribute__((always_inline)) {
+        const u32x4_t lo = T[lds_idx<C>(row, ch)], hi = T[lds_idx<C>(row, ch + 1)];
+        return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto read = [&](int ks, int b) __attribute__((always_inline)) {
+        const int ch = ks * 4 + (lane >> 5) * 2;
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = frag(As, wm * C::WM + tm * 32 + (lane & 31), ch);
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) bfr[b][tn] = frag(Bs, wn * C::WN + tn * 32 + (lane & 31), ch);
+    };
+    read(0, 0);
+    static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(kc)::value, b = ks & 1;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks + 1 < KS) read(ks + 1, b ^ 1);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = mfma32x32x64_fp8(bfr[b][tn], af[b][tm], acc[tm][tn]);
+        if constexpr (ks + 1 < KS) {
+            static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value, r = (m + 1) * NR / NM - m * NR / NM;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS read
+            });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
 // K loop over nk tiles through a ring of C::STAGES LDS stages.
 //   fill(kt, As, Bs)  starts moving tile kt into a stage (DMA issue, and/or
 //                     global loads into registers);
@@ -224,7 +263,7 @@ __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u
 // STAGES - 1 tiles are in flight.  PER_TILE is the number of DMA
 // instructions per tile and wave; 0 means "wait for everything" (register
 // staged operands already wait in land).
-template <class C, int PER_TILE, class Fill, class Land>
+template <class C, int PER_TILE, bool F8 = false, class Fill, class Land>
 __device__ __forceinline__ void kloop(int nk, Fill&& fill, Land&& land, u32x4_t* ring,
                                       f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
     constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS, AOFF = C::BM * C::CPR;
@@ -243,7 +282,10 @@ __device__ __forceinline__ void kloop(int nk, Fill&& fill, Land&& land, u32x4_t*
         u32x4_t* ns = ring + nxt * STG;
         if (more) fill(kt + S - 1, ns, ns + AOFF);
         u32x4_t* cs = ring + cur * STG;
-        mma_tile<C>(cs, cs + AOFF, acc, wm, wn, lane);
+        if constexpr (F8)
+            mma_tile_fp8<C>(cs, cs + AOFF, acc, wm, wn, lane);
+        else
+            mma_tile<C>(cs, cs + AOFF, acc, wm, wn, lane);
         if (more) land(ns, ns + AOFF);
         cur = (cur + 1 == S) ? 0 : cur + 1;
         nxt = (nxt + 1 == S) ? 0 : nxt + 1;
@@ -898,6 +940,139 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 }
 
 // ---------------------------------------------------------------------------
+// FP8 dense GEMM (the shared expert with E4M3 weights and activations)
+// ---------------------------------------------------------------------------
+//
+// The LDS tile, DMA slots, swizzle and K loop are the bf16 GEMM's: a row's
+// K step is 128 codes = 128 bytes = 8 chunks of 16 B, as 64 bf16 values
+// are.  Each K step runs two 32x32x64 fp8 MFMAs per 32x32 block, twice the
+// K of the bf16 step for the same bytes and the same MFMA issue time.
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int tiles_m, int tiles_n, int group_m) {
+    static_assert(C::DMA && C::CPR == 8, "fp8 tiles: LDS-DMA, 128-byte K step");
+    __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+    const int w = xcd_work_index(blockIdx.x, tiles_m * tiles_n);
+    if (w < 0) return;
+    const int width = group_m * tiles_n;
+    const int first_m = (w / width) * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
+    const int m0 = (first_m + (w % width) % gsz) * C::BM;
+    const int n0 = ((w % width) / gsz) * C::BN;
+
+    using SA = Slots<C, C::BM>;
+    using SB = Slots<C, C::BN>;
+    const uint8_t* a_ptr[SA::N];
+    const uint8_t* b_ptr[SB::N];
+#pragma unroll
+    for (int j = 0; j < SA::N; ++j)
+        a_ptr[j] = g.A + (int64_t)min(m0 + SA::row(j, tid), g.M - 1) * g.lda + SA::lchunk(j, tid) * 16;
+#pragma unroll
+    for (int j = 0; j < SB::N; ++j)
+        b_ptr[j] = g.B + (int64_t)min(n0 + SB::row(j, tid), g.N - 1) * g.ldb + SB::lchunk(j, tid) * 16;
+
+    auto fill = [&](int kt, u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+        const int kk = kt * 128;
+#pragma unroll
+        for (int j = 0; j < SA::N; ++j)
+            if (SA::active(j, tid)) dma16(a_ptr[j] + kk, SA::dst(As, wave, j));
+#pragma unroll
+        for (int j = 0; j < SB::N; ++j)
+            if (SB::active(j, tid)) dma16<C::B_NT ? 2 : 0>(b_ptr[j] + kk, SB::dst(Bs, wave, j));
+    };
+    auto land = [](u32x4_t*, u32x4_t*) {};
+
+    f32x16_t acc[C::TM][C::TN];
+    zero_acc<C>(acc);
+    kloop<C, SA::N + SB::N, true>(g.K / 128, fill, land, ring, acc, wm, wn, lane);
+
+    static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
+        constexpr int tm = decltype(tmc)::value;
+        const int m = m0 + wm * C::WM + tm * 32 + (lane & 31);
+        if (m < g.M) {
+            const float sa = g.a_scale[m];
+            uint16_t* crow = g.C + (int64_t)m * g.ldc;
+            static_for<C::TN * 4>([&](auto tqc) __attribute__((always_inline)) {
+                constexpr int tn = decltype(tqc)::value / 4, q = decltype(tqc)::value % 4;
+                const int n = n0 + wn * C::WN + tn * 32 + q * 8 + (lane >> 5) * 4;
+                if (n < g.N) {  // N % 16 == 0: columns n..n+3 are all inside
+                    const float4 sb = *reinterpret_cast<const float4*>(g.b_scale + n);
+                    float v[4] = {acc[tm][tn][q * 4 + 0] * sa * sb.x, acc[tm][tn][q * 4 + 1] * sa * sb.y,
+                                  acc[tm][tn][q * 4 + 2] * sa * sb.z, acc[tm][tn][q * 4 + 3] * sa * sb.w};
+                    uint2* dst = reinterpret_cast<uint2*>(crow + n);
+                    if (g.epi == EPI_ADD_BF16) {
+                        const uint2 old = *dst;
+                        v[0] += bf16_to_f32((uint16_t)(old.x & 0xFFFFu));
+                        v[1] += bf16_to_f32((uint16_t)(old.x >> 16));
+                        v[2] += bf16_to_f32((uint16_t)(old.y & 0xFFFFu));
+                        v[3] += bf16_to_f32((uint16_t)(old.y >> 16));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.f) * fmaxf(v[i], 0.f);
+                    }
+                    uint2 o;
+                    o.x = pack_bf16x2(v[0], v[1]);
+                    o.y = pack_bf16x2(v[2], v[3]);
+                    *dst = o;
+                }
+            });
+        }
+    });
+}
+
+// One wave per row: the row's max |v| (a first pass), then the codes (a
+// second pass over the same 16-byte chunks, mostly cache hits).
+__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                                int cols, int64_t ld, uint8_t* __restrict__ codes,
+                                                                float* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;  // whole wave
+    const uint16_t* row = src + r * ld;
+    float amax = 0.f;
+    for (int c = lane * 8; c < cols; c += 512) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[i] & 0xFFFFu))));
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[i] >> 16))));
+        }
+    }
+    amax = wave_max(amax);
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    uint8_t* out = codes + r * (int64_t)cols;
+    for (int c = lane * 8; c < cols; c += 512) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c);
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float a = bf16_to_f32((uint16_t)(v[2 * h] & 0xFFFFu)) / scale;
+            const float b = bf16_to_f32((uint16_t)(v[2 * h] >> 16)) / scale;
+            const float cc = bf16_to_f32((uint16_t)(v[2 * h + 1] & 0xFFFFu)) / scale;
+            const float d = bf16_to_f32((uint16_t)(v[2 * h + 1] >> 16)) / scale;
+            int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(cc, d, p, true);
+            w[h] = (uint32_t)p;
+        }
+        *reinterpret_cast<uint2*>(out + c) = make_uint2(w[0], w[1]);
+    }
+    if (lane == 0) scales[r] = scale;
+}
+
+hipError_t launch_quantize_rows_fp8(const uint16_t* src, int64_t rows, int cols, int64_t ld, uint8_t* codes,
+                                    float* scales, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    const int64_t blocks = (rows + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    LMOE_LAUNCH("quantize_fp8", s,
+                quantize_rows_fp8_kernel<<<(unsigned)blocks, 256, 0, s>>>(src, rows, cols, ld, codes, scales));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Repacking of bf16 expert weights into the tiled layout
 // ---------------------------------------------------------------------------
 //
@@ -1112,6 +1287,21 @@ hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t sp
     }
     return run_dense<C256>(sub_columns(g, n_tail, g.N), splitk_ws, splitk_bytes, s);
 }
+// FP8 shared expert: 256x256 tiles (64x64 for decode-sized M), one tile per
+// block; N and K are the shared expert's (multiples of 64 and 128).
+template <class C>
+static hipError_t run_fp8(const Fp8Gemm& g, hipStream_t s) {
+    const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
+    LMOE_LAUNCH("fp8_gemm", s, fp8_gemm_kernel<C><<<tiles_m * tiles_n, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8));
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const Fp8Gemm& g, hipStream_t s) {
+    if (g.K % 128 != 0 || g.N % 16 != 0) return hipErrorInvalidValue;
+    if (g.M <= 64) return run_fp8<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, s);
+    return run_fp8<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, s);
+}
+
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to
 // 384) by 256 columns over 8 waves, each wave 96 x 64.  Few-row experts
 // (decode) stream their weights with the non-temporal hint (each call reads

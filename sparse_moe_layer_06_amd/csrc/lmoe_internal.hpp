@@ -14,6 +14,7 @@ enum Epi : int {
     EPI_STORE = 0,     // C = acc, stored in the activation dtype
     EPI_F32_BIAS = 1,  // C = acc (+ bias[col]), stored fp32
     EPI_RELU2 = 2,     // C = max(0, acc * scale)^2, activation dtype
+    EPI_ADD_BF16 = 3,  // C = C + acc * scale, bf16 in place (fp8 GEMM only)
 };
 
 // One contiguous range of output columns [n_begin, n_end) of a dense GEMM,
@@ -87,6 +88,30 @@ struct GroupedGemm {
     int64_t ldc;
     float* sk_part;           // kSkPartialBytes of tail-split partial sums, or null (whole items only)
 };
+
+// FP8 (E4M3 x E4M3) GEMM with per-row scales, fp32 accumulate:
+// C[m][n] = epi(a_scale[m] * b_scale[n] * sum_k A[m][k] * B[n][k]), epi
+// EPI_RELU2 (store bf16) or EPI_ADD_BF16.  K is a multiple of 128; N, lda,
+// ldb and ldc are multiples of 16.
+struct Fp8Gemm {
+    int M, N, K;
+    const uint8_t* A;
+    int64_t lda;
+    const float* a_scale;
+    const uint8_t* B;
+    int64_t ldb;
+    const float* b_scale;
+    int epi;
+    uint16_t* C;
+    int64_t ldc;
+};
+hipError_t launch_fp8_gemm(const Fp8Gemm& g, hipStream_t s);
+
+// Per-row FP8 quantisation of a bf16 matrix [rows][cols] (row stride ld):
+// scale = max |v| / 448 (1 for an all-zero row), code = E4M3(v / scale),
+// round to nearest even.  cols and ld are multiples of 8.
+hipError_t launch_quantize_rows_fp8(const uint16_t* src, int64_t rows, int cols, int64_t ld, uint8_t* codes,
+                                    float* scales, hipStream_t s);
 
 // Partial-sum bytes the split last round of a many-token dense GEMM needs on
 // this device (0: no split).

@@ -13,6 +13,8 @@ Recipe (one stream per tensor, so every tensor is reproducible alone):
     of that matrix (d for W_down, W_r, W_s1; l for W1, W_up and a latent
     router's W_r; f for W2; f_s for W_s2).  Draws are fp32, then rounded to
     bf16 (round to nearest even) for bf16 tensors.
+  * FP8 shared-expert weights (shared_fp8): the same fp32 draws, stored as
+    E4M3 codes with one fp32 scale per output row (max |row| / 448).
   * The skewed-routing workload adds a per-expert router bias
     b_e = 2 * log(1 / (e + 1)), stored in fp32.
   * NVFP4 expert weights: W ~ N(0, 1/fan_in) in fp32, a block scale
@@ -47,7 +49,9 @@ class LayerDims:
     (0 = no shared expert).  act is the activation/storage dtype ('f32' or
     'bf16'); experts is the routed-expert weight format ('f32', 'bf16' or
     'nvfp4'); zipf_bias adds the skewed router bias; router_latent makes the
-    router read the latent z (W_r [E][l]) instead of x (W_r [E][d]).
+    router read the latent z (W_r [E][l]) instead of x (W_r [E][d]);
+    shared_fp8 stores the shared expert's weights as E4M3 codes with one fp32
+    scale per output row.
     """
     name: str
     T: int
@@ -61,6 +65,7 @@ class LayerDims:
     experts: str
     zipf_bias: bool = False
     router_latent: bool = False
+    shared_fp8: bool = False
 
     def with_(self, **kw) -> "LayerDims":
         return dataclasses.replace(self, **kw)
@@ -200,13 +205,27 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
     inp.update(_expert_stack(cfg, "W1", seed, dev))
     inp.update(_expert_stack(cfg, "W2", seed, dev))
     inp["W_up"] = _normal((d, l), 1.0 / math.sqrt(l), _gen(dev, seed, "W_up"), dev, act)
-    if fs > 0:
+    if fs > 0 and cfg.shared_fp8:
+        for name, shape, fan_in in (("W_s1", (fs, d), d), ("W_s2", (d, fs), fs)):
+            W = _normal(shape, 1.0 / math.sqrt(fan_in), _gen(dev, seed, name), dev, torch.float32)
+            inp[name], inp[name + "_scale"] = _fp8_rows(W)
+    elif fs > 0:
         inp["W_s1"] = _normal((fs, d), 1.0 / math.sqrt(d), _gen(dev, seed, "W_s1"), dev, act)
         inp["W_s2"] = _normal((d, fs), 1.0 / math.sqrt(fs), _gen(dev, seed, "W_s2"), dev, act)
     else:
         inp["W_s1"] = None
         inp["W_s2"] = None
     return inp
+
+
+def _fp8_rows(W: torch.Tensor):
+    """fp32 W [rows][cols] -> (E4M3 codes as uint8, fp32 scale per row):
+    scale = max|row| / 448, code = E4M3(w / scale) by torch's float8_e4m3fn
+    cast (round to nearest even)."""
+    amax = W.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (W / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.contiguous()
 
 
 def host_view(t: Optional[torch.Tensor]):

@@ -65,6 +65,9 @@ def test_validate_accepts_every_workload():
     ("f_s", 32, B.LMOE_ERR_SHAPE),
     ("act_dtype", 7, B.LMOE_ERR_DTYPE),
     ("expert_dtype", B.LMOE_F32, B.LMOE_ERR_DTYPE),  # fp32 experts with bf16 activations
+    ("shared_dtype", 7, B.LMOE_ERR_DTYPE),
+    ("shared_dtype", B.LMOE_F32, B.LMOE_ERR_DTYPE),  # fp32 shared weights with bf16 activations
+    ("router_latent", 2, B.LMOE_ERR_SHAPE),
 ])
 def test_validate_rejects(field, value, code):
     d = dims()
@@ -163,3 +166,30 @@ def test_tiled_experts_need_bf16_activations():
     assert B.validate_dims(d) == B.LMOE_OK
     d.act_dtype = B.LMOE_F32
     assert B.validate_dims(d) == B.LMOE_ERR_DTYPE
+
+
+def test_fp8_shared_rules():
+    d = dims()  # bf16 activations, f_s = 4096
+    d.shared_dtype = B.LMOE_FP8_E4M3
+    assert B.validate_dims(d) == B.LMOE_OK
+    d.f_s = 4096 + 64  # the fp8 K step is 128
+    assert B.validate_dims(d) == B.LMOE_ERR_SHAPE
+    f = B.dims_of(synth.CONFIGS["tiny_f32"])
+    f.shared_dtype = B.LMOE_FP8_E4M3  # fp8 shared weights need bf16 activations
+    assert B.validate_dims(f) == B.LMOE_ERR_DTYPE
+    # the per-row scales are required with fp8 weights
+    d = dims()
+    d.shared_dtype = B.LMOE_FP8_E4M3
+    assert _forward(d, shared=B.Shared(FAKE, FAKE, None, FAKE)) == B.LMOE_ERR_NULL
+    assert _forward(d, shared=B.Shared(FAKE, FAKE, FAKE, MIS)) == B.LMOE_ERR_ALIGN
+    assert _forward(d, shared=B.Shared(FAKE, FAKE, FAKE, FAKE)) == B.LMOE_ERR_WORKSPACE
+    assert B.lib().lmoe_workspace_bytes(ctypes.byref(d)) > B.lib().lmoe_workspace_bytes(ctypes.byref(dims()))
+
+
+def test_quantize_rows_error_paths():
+    L = B.lib()
+    assert L.lmoe_quantize_rows_fp8(0, 64, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_quantize_rows_fp8(4, 60, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_quantize_rows_fp8(4, 1 << 21, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_quantize_rows_fp8(4, 64, None, FAKE, FAKE, None) == B.LMOE_ERR_NULL
+    assert L.lmoe_quantize_rows_fp8(4, 64, FAKE, FAKE, MIS, None) == B.LMOE_ERR_ALIGN

@@ -58,6 +58,11 @@ SMALL = {
     "latent_f32": TINY.with_(name="latent_f32", T=70, E=12, k=3, f_s=64, router_latent=True),
     "latent_nvfp4_zipf": TINY.with_(name="latent_nvfp4_zipf", T=40, d=256, l=64, E=32, k=5, f=128, f_s=0,
                                     act="bf16", experts="nvfp4", zipf_bias=True, router_latent=True),
+    # FP8 shared expert (E4M3 weights, per-token E4M3 inputs, fp8 MFMA GEMMs)
+    "fp8_shared": TINY.with_(name="fp8_shared", T=150, d=512, l=128, E=16, k=3, f=192, f_s=256,
+                             act="bf16", experts="bf16", shared_fp8=True),
+    "fp8_shared_few": TINY.with_(name="fp8_shared_few", T=5, d=1024, l=256, E=8, k=2, f=128, f_s=384,
+                                 act="bf16", experts="nvfp4", shared_fp8=True, router_latent=True),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
@@ -121,7 +126,7 @@ def test_exact_logit_ties_break_to_lower_id():
 
 
 def test_staged_entry_points_compose_to_forward():
-    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide", "latent_bf16"):
+    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide", "latent_bf16", "fp8_shared"):
         cfg = SMALL[name]
         log(f"case staged {name}")
         inp = small_inputs(cfg)
@@ -198,6 +203,20 @@ def test_tiled_expert_weights(name):
     P.run_and_check(cfg_t, inp, gpu_inp=inp_t, report=log)
 
 
+def test_quantize_rows_fp8_matches_oracle():
+    # rows of very different magnitudes, an all-zero row, and a ragged width
+    g = torch.Generator().manual_seed(5)
+    v = torch.randn(37, 1000, generator=g) * torch.exp2(torch.randint(-20, 20, (37, 1), generator=g).float())
+    v[4] = 0.0
+    v[6, :500] *= 1e-4  # values near the E4M3 subnormal range of that row
+    src = v.to(torch.bfloat16)
+    codes, scales = B.quantize_rows_fp8(src.cuda())
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_rows_fp8(O.as_f64(synth.host_view(src)))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
 # ---- full-size workloads --------------------------------------------------
 
 @pytest.mark.timeout(900)
@@ -259,6 +278,22 @@ def test_prefill_latent_router_sampled():
     log(f"case {cfg}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     P.run_and_check(cfg, inp, n_sample=8, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_mid_fp8_shared_full_size():
+    cfg = CFG["mid_bf16"].with_(name="mid_fp8_shared", shared_fp8=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=48, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_fp8_shared_sampled():
+    cfg = CFG["prefill_bf16"].with_(name="prefill_fp8_shared", shared_fp8=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=12, lazy_experts=True, report=log)
 
 
 @pytest.mark.timeout(900)

@@ -35,6 +35,7 @@ SMALL_NVFP4 = TINY.with_(name="small_nvfp4", T=40, d=128, l=32, E=8, k=2, f=64, 
                          act="bf16", experts="nvfp4")
 SMALL_ZIPF = SMALL_BF16.with_(name="small_zipf", zipf_bias=True, f_s=0)
 SMALL_LATENT = SMALL_BF16.with_(name="small_latent", router_latent=True)
+SMALL_FP8 = SMALL_BF16.with_(name="small_fp8_shared", f_s=128, shared_fp8=True)
 TINY_LATENT = TINY.with_(name="tiny_latent", router_latent=True)
 
 
@@ -215,13 +216,12 @@ def dense_bruteforce(inp, k):
             W1, W2 = ew(e)
             h = np.maximum(W1 @ z[t], 0) ** 2
             out[t] += p[e] * (W_up @ (W2 @ h))
-    if inp.get("W_s1") is not None:
-        hs = np.maximum(x @ O.as_f64(inp["W_s1"]).T, 0) ** 2
-        out += hs @ O.as_f64(inp["W_s2"]).T
+    if inp.get("W_s1") is not None:  # pinned on its own (test_shared_expert_*)
+        out += O.shared_expert(inp["x"], inp)
     return out
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_ZIPF, SMALL_LATENT, TINY_LATENT,
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_ZIPF, SMALL_LATENT, TINY_LATENT, SMALL_FP8,
                                  TINY.with_(k=1), TINY.with_(E=5, k=5)], ids=lambda c: f"{c.name}-E{c.E}k{c.k}")
 def test_sparse_equals_dense_bruteforce(cfg):
     inp = host_inputs(cfg)
@@ -447,3 +447,75 @@ def test_latent_router_rounds_what_it_reads():
     f32 = host_inputs(TINY_LATENT)
     assert np.array_equal(O.router_input(f32["x"], f32),
                           O.down_project(f32["x"], f32["W_down"]).astype(np.float32).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# FP8 shared expert (E4M3 weights and per-token E4M3 inputs)
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3(v):
+    return torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encoding_matches_torch():
+    rng = np.random.default_rng(11)
+    v = (rng.standard_normal(300_000) * np.exp2(rng.integers(-14, 9, 300_000))).astype(np.float32)
+    v = v[np.abs(v) < 448]
+    grid = O.e4m3_value(np.arange(256))
+    pos = np.unique(grid[np.isfinite(grid) & (grid >= 0)])
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)  # exact ties, subnormal ones included
+    allv = np.concatenate([v, mids, -mids, pos.astype(np.float32), [0.0, -0.0, 448.0, 460.0, -460.0]])
+    assert np.array_equal(O.e4m3_encode(allv.astype(np.float64)), _torch_e4m3(allv))
+    with pytest.raises(ValueError):
+        O.e4m3_encode(np.array([464.0]))
+
+
+def test_row_quantisation_invariants():
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal((40, 96)) * np.exp2(rng.integers(-10, 10, (40, 1)))
+    v = O.round_to_bf16(v)
+    v[3] = 0.0
+    codes, scale = O.quantize_rows_fp8(v)
+    assert scale.dtype == np.float32 and scale[3] == 1.0 and not codes[3].any()
+    # the largest magnitude of each row lands on +-448
+    rows = [r for r in range(40) if r != 3]
+    big = np.argmax(np.abs(v[rows]), axis=1)
+    assert np.all(np.abs(O.e4m3_value(codes[rows, big])) == 448.0)
+    # library route: torch's float8 cast of the float32 quotients
+    q = (v.astype(np.float32) / scale[:, None]).astype(np.float32)
+    assert np.array_equal(codes, _torch_e4m3(q))
+    # error bound: within half an E4M3 step of the value (plus the quotient's rounding)
+    deq = O.e4m3_value(codes) * scale.astype(np.float64)[:, None]
+    mag = np.maximum(np.abs(q.astype(np.float64)), 2.0 ** -6)
+    step = np.exp2(np.floor(np.log2(mag)) - 3) * scale.astype(np.float64)[:, None]
+    assert np.all(np.abs(deq - v) <= 0.5 * step * (1 + 1e-6) + 1e-300)
+
+
+def test_shared_expert_fp8_against_torch_casts():
+    # the fp8 shared expert re-derived with torch's float8 casts in both
+    # directions (codes from fp32 quotients, values from codes) and torch's
+    # bf16 cast of the stored hidden layer
+    cfg = SMALL_FP8
+    inp = host_inputs(cfg)
+    f8 = torch.float8_e4m3fn
+
+    def quant(v64):
+        v = torch.from_numpy(v64).to(torch.float32)
+        amax = v.abs().amax(dim=1)
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        return (v / sc[:, None]).to(f8).to(torch.float64), sc.to(torch.float64)
+
+    def weights(name):
+        return (torch.from_numpy(inp[name]).view(f8).to(torch.float64)
+                * torch.from_numpy(inp[name + "_scale"]).to(torch.float64)[:, None])
+
+    qx, sx = quant(O.as_f64(inp["x"]))
+    hs = torch.relu((qx * sx[:, None]) @ weights("W_s1").T).square()
+    hs = hs.to(torch.bfloat16).to(torch.float64)
+    qh, sh = quant(hs.numpy())
+    ref = (qh * sh[:, None]) @ weights("W_s2").T
+    got = O.shared_expert(inp["x"], inp)
+    assert rel_err(got, ref.numpy()) <= 1e-12
+    # and the whole layer with W_up zeroed is the shared expert alone
+    inp["W_up"] = np.zeros_like(inp["W_up"])
+    assert rel_err(O.forward(inp, cfg.k)["out"], ref.numpy()) <= 1e-12
