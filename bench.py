@@ -150,11 +150,13 @@ def decode(cfg, steps, torch, B, synth, layout="tiled"):
     touched = int((counts > 0).sum().item())
     l, f, d, E, T = cfg.l, cfg.f, cfg.d, cfg.E, cfg.T
     r_in = l if cfg.router_latent else d  # router weights W_r [E][r_in]
-    bytes_alg = touched * 2 * l * f * 2 + (2 * d * l + r_in * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
+    proj = 0 if cfg.standard_moe else 2 * d * l  # W_down and W_up
+    bytes_alg = touched * 2 * l * f * 2 + (proj + r_in * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     return dict(workload=f"{cfg.name} T={T} d={d} l={l} E={E} k={cfg.k} f={f}, {cfg.experts} experts "
                          f"({layout if cfg.experts == 'bf16' else 'as stored'}), router reads "
-                         f"{'z (latent)' if cfg.router_latent else 'x'}", tokens_per_s=T / (ms * 1e-3),
+                         f"{'z (latent)' if cfg.router_latent else 'x'}"
+                         f"{', standard MoE (experts in d)' if cfg.standard_moe else ''}", tokens_per_s=T / (ms * 1e-3),
                 ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
                 hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
                 "1 GiB buffer read between steps (cache eviction)" % steps, kernels=kernels)
@@ -167,7 +169,8 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     g = kernels.get(gname)
     res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
                         f"{cfg.experts} experts, router reads {'z (latent)' if cfg.router_latent else 'x'}"
-                        f"{', FP8 shared expert (E4M3 x E4M3 MFMA)' if cfg.shared_fp8 else ''}",
+                        f"{', FP8 shared expert (E4M3 x E4M3 MFMA)' if cfg.shared_fp8 else ''}"
+                        f"{', standard MoE (experts in d, no latent projections)' if cfg.standard_moe else ''}",
                ms_per_step=ms, tokens_per_s=cfg.T / (ms * 1e-3),
                layer_tflops=cfg.flops / (ms * 1e-3) / 1e12, layer_mfma_frac=cfg.flops / (ms * 1e-3) / PEAK_BF16_FLOPS)
     if g:
@@ -303,11 +306,18 @@ def main():
         extra = [C[n] for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload]
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_latent_router", router_latent=True))
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_shared", shared_fp8=True))
+        # the standard MoE the overview compares against: 128 experts of d, top-6
+        extra.append(C["prefill_bf16"].with_(name="prefill_standard_moe", l=C["prefill_bf16"].d, E=128, k=6,
+                                             standard_moe=True))
         result["other_workloads"] = {c.name: secondary(c, max(args.steps // 2, 3), args.warmup, torch, B, synth,
                                                        args.expert_layout) for c in extra}
         if not args.no_decode:
             result["other_workloads"]["decode_latent_router"] = decode(
                 C["decode_bf16_zipf"].with_(name="decode_latent_router", router_latent=True),
+                args.decode_steps, torch, B, synth, args.expert_layout)
+            result["other_workloads"]["decode_standard_moe"] = decode(
+                C["decode_bf16_zipf"].with_(name="decode_standard_moe", l=C["decode_bf16_zipf"].d, E=128, k=6,
+                                            standard_moe=True),
                 args.decode_steps, torch, B, synth, args.expert_layout)
     if not args.no_cpu:
         log("bench: cpu baseline (oracle)")

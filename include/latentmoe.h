@@ -82,6 +82,12 @@ extern "C" {
  *   with bf16 activations, LMOE_FP8_E4M3 (the Ultra release news lists FP8
  *   shared experts; see lmoe_shared; f_s must then be a multiple of 128).
  *   LMOE_ERR_DTYPE otherwise; it is checked even when f_s == 0.
+ * standard_moe (0 or 1): 1 runs the same kernels as a standard MoE layer,
+ *   the comparison point of the overview's section 2.2 table (128 experts,
+ *   top-6, experts in the hidden width): no down- or up-projection, l == d
+ *   (instead of d/4), routed experts W1 [E][f][d], W2 [E][d][f], z = x and
+ *   out = c (+ shared expert); router_latent must be 0.  W_down and W_up are
+ *   then ignored and may be NULL.  LMOE_ERR_SHAPE when violated.
  */
 typedef struct lmoe_dims {
     int64_t T, d, l, E, k, f, f_s;
@@ -89,6 +95,7 @@ typedef struct lmoe_dims {
     int32_t expert_dtype;
     int32_t router_latent;
     int32_t shared_dtype;
+    int32_t standard_moe;
 } lmoe_dims;
 
 /*
@@ -242,8 +249,9 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down,
 
 /*
  * Steps 1-4 (overview section 2.2 step 1; Ultra release news, 512 experts
- * with top-22): z = x W_down^T [T][l] (act dtype), logits = x W_r^T + b
- * [T][E] fp32 (z W_r^T + b with dims.router_latent, from the stored z),
+ * with top-22): z = x W_down^T [T][l] (act dtype; not written with
+ * dims.standard_moe, where z is x itself and may be NULL), logits = x W_r^T
+ * + b [T][E] fp32 (z W_r^T + b with dims.router_latent, from the stored z),
  * topk_idx [T][k] int32 in (logit desc, id asc) order,
  * topk_gate [T][k] fp32 = softmax of the selected logits.  If shared is
  * non-NULL also hs = (max(0, x W_s1^T))^2 [T][f_s] (act dtype), the first
@@ -279,7 +287,8 @@ int lmoe_experts_ffn(const lmoe_dims* dims, const void* z, const int32_t* offset
 /*
  * Combine and up-projection (overview section 2.2 step 3): c_t = sum over
  * j = 0..k-1, in that order, of topk_gate[t][j] * Y[inv[t*k + j]] in fp32 (no
- * atomics; deterministic), out = c W_up^T [+ hs W_s2^T if shared].
+ * atomics; deterministic), out = c W_up^T [+ hs W_s2^T if shared]; with
+ * dims.standard_moe, out = c [+ hs W_s2^T] and W_up may be NULL.
  * c [T][l] may be NULL (then it lives in the workspace).
  */
 int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv,

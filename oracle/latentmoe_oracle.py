@@ -33,6 +33,9 @@ paragraph):
      each of the shared expert's inputs (x_t, then its hidden layer as stored
      in bf16) is quantised per token to E4M3 with scale max|v|/448 before
      its product
+  Without W_down and W_up the same steps describe the standard MoE layer the
+  overview compares against (section 2.2 table: 128 experts, top-6, experts
+  in the hidden width): z_t = x_t and out_t = c_t (+ shared expert).
   Integer side: counts[e] = #{(t, j): I_t[j] = e}, offsets = exclusive prefix
   sum of counts, perm = stable counting sort of the row-major (t, j) pairs by
   expert, inv = perm^-1.
@@ -288,7 +291,8 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
     if tokens is not None:
         x = x[np.asarray(tokens)]
     experts = experts or ExpertWeights(inp)
-    z = down_project(x, inp["W_down"])
+    # a standard MoE (no W_down / W_up, experts in d) routes and computes on x
+    z = down_project(x, inp["W_down"]) if inp.get("W_down") is not None else as_f64(x)
     s = router_logits(router_input(x, inp), inp["W_r"], inp.get("b_r"))
     idx = select_topk(s, k)
     g = gate_weights(s, idx)
@@ -298,7 +302,7 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
         for j in range(k):
             W1_e, W2_e = experts(idx[t, j])
             c[t] += g[t, j] * expert_ffn(z[t], W1_e, W2_e)
-    out = c @ as_f64(inp["W_up"]).T
+    out = c @ as_f64(inp["W_up"]).T if inp.get("W_up") is not None else c.copy()
     if inp.get("W_s1") is not None:
         out = out + shared_expert(x, inp)
     return dict(z=z, logits=s, idx=idx, gate=g, c=c, out=out)

@@ -39,7 +39,7 @@ class Dims(ctypes.Structure):
                 ("E", ctypes.c_int64), ("k", ctypes.c_int64), ("f", ctypes.c_int64),
                 ("f_s", ctypes.c_int64), ("act_dtype", ctypes.c_int32),
                 ("expert_dtype", ctypes.c_int32), ("router_latent", ctypes.c_int32),
-                ("shared_dtype", ctypes.c_int32)]
+                ("shared_dtype", ctypes.c_int32), ("standard_moe", ctypes.c_int32)]
 
 
 class Experts(ctypes.Structure):
@@ -126,7 +126,7 @@ def _check(status: int, what: str):
 def dims_of(cfg: LayerDims, T: Optional[int] = None) -> Dims:
     return Dims(T if T is not None else cfg.T, cfg.d, cfg.l, cfg.E, cfg.k, cfg.f, cfg.f_s,
                 DTYPE_CODE[cfg.act], DTYPE_CODE[cfg.experts], 1 if cfg.router_latent else 0,
-                DTYPE_CODE["fp8" if cfg.shared_fp8 else cfg.act])
+                DTYPE_CODE["fp8" if cfg.shared_fp8 else cfg.act], 1 if cfg.standard_moe else 0)
 
 
 def _p(t: Optional[torch.Tensor]) -> Optional[int]:

@@ -59,18 +59,19 @@ static bool shared_dense(const lmoe_dims& d) { return d.f_s > 0 && d.shared_dtyp
 static DenseGemm gemm_in(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r, const float* bias,
                          const void* W_s1, void* z, float* logits, void* hs) {
     DenseGemm g{};
-    const int E = d.router_latent ? 0 : (int)d.E;  // router columns in this GEMM
+    const int L = d.standard_moe ? 0 : (int)d.l;        // latent columns (none: z is x)
+    const int E = d.router_latent ? 0 : (int)d.E;       // router columns in this GEMM
     const int fs = shared_dense(d) ? (int)d.f_s : 0;
     g.M = (int)d.T;
-    g.N = (int)d.l + E + fs;
+    g.N = L + E + fs;
     g.nseg = 1;
     g.A[0] = x;
     g.lda[0] = d.d;
     g.K[0] = (int)d.d;
     g.ngroups = 0;
-    g.g[g.ngroups++] = NGroup{0, (int)d.l, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
-    if (E > 0) g.g[g.ngroups++] = NGroup{(int)d.l, (int)d.l + E, {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
-    if (fs > 0) g.g[g.ngroups++] = NGroup{(int)d.l + E, g.N, {W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
+    if (L > 0) g.g[g.ngroups++] = NGroup{0, L, {W_down, nullptr}, EPI_STORE, z, d.l, nullptr};
+    if (E > 0) g.g[g.ngroups++] = NGroup{L, L + E, {W_r, nullptr}, EPI_F32_BIAS, logits, d.E, bias};
+    if (fs > 0) g.g[g.ngroups++] = NGroup{L + E, g.N, {W_s1, nullptr}, EPI_RELU2, hs, d.f_s, nullptr};
     return g;
 }
 
@@ -88,10 +89,22 @@ static DenseGemm gemm_router(const lmoe_dims& d, const void* z, const void* W_r,
     return g;
 }
 
-// [c | hs] [W_up | W_s2]^T -> out.
+// [c | hs] [W_up | W_s2]^T -> out.  Standard MoE: out (holding c already)
+// += hs W_s2^T.
 static DenseGemm gemm_out(const lmoe_dims& d, const void* c, const void* hs, const void* W_up, const void* W_s2,
                           void* out) {
     DenseGemm g{};
+    if (d.standard_moe) {
+        g.M = (int)d.T;
+        g.N = (int)d.d;
+        g.nseg = 1;
+        g.A[0] = hs;
+        g.lda[0] = d.f_s;
+        g.K[0] = (int)d.f_s;
+        g.ngroups = 1;
+        g.g[0] = NGroup{0, (int)d.d, {W_s2, nullptr}, EPI_ADD, out, d.d, nullptr};
+        return g;
+    }
     const bool two = shared_dense(d);
     g.M = (int)d.T;
     g.N = (int)d.d;
@@ -133,7 +146,7 @@ static Layout plan(const lmoe_dims& d) {
         o = align256(o + bytes);
         return at;
     };
-    L.z = take((size_t)d.T * d.l * es);
+    L.z = take(d.standard_moe ? 0 : (size_t)d.T * d.l * es);
     L.logits = take((size_t)d.T * d.E * 4);
     L.idx = take(n * 4);
     L.gate = take(n * 4);
@@ -148,7 +161,7 @@ static Layout plan(const lmoe_dims& d) {
     L.ntiles = take((size_t)d.E * 4);
     L.H = take(n * d.f * es);
     L.Y = take(n * d.l * es);
-    L.c = take((size_t)d.T * d.l * es);
+    L.c = take(d.standard_moe ? 0 : (size_t)d.T * d.l * es);
     L.hs = take((size_t)d.T * d.f_s * es);
     // fp32 split-K partials of the dense GEMMs of few-token (decode) calls
     // and of the split last round of many-token ones
@@ -158,7 +171,9 @@ static Layout plan(const lmoe_dims& d) {
     } else if (d.act_dtype == LMOE_BF16) {
         const size_t a = dense_tail_split_bytes(gemm_in(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                                         nullptr, nullptr));
-        const size_t b = dense_tail_split_bytes(gemm_out(d, nullptr, nullptr, nullptr, nullptr, nullptr));
+        const size_t b = (!d.standard_moe || shared_dense(d))
+                             ? dense_tail_split_bytes(gemm_out(d, nullptr, nullptr, nullptr, nullptr, nullptr))
+                             : 0;
         const size_t r = d.router_latent ? dense_tail_split_bytes(gemm_router(d, nullptr, nullptr, nullptr, nullptr))
                                          : 0;
         L.splitk_bytes = a > b ? a : b;
@@ -318,13 +333,23 @@ static hipError_t run_experts(const lmoe_dims& d, const void* z, const int32_t* 
     return launch_grouped_gemm(g2, d.act_dtype, s);
 }
 
+// c_opt: the caller's c, or NULL.  A standard MoE combines straight into
+// out (then copied to c_opt if given) and adds the shared expert there.
 static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_t* inv, const float* gate,
-                                 const void* W_up, const lmoe_shared* sh, const void* hs, void* c, void* out,
+                                 const void* W_up, const lmoe_shared* sh, const void* hs, void* c_opt, void* out,
                                  char* ws, const Layout& L, hipStream_t s) {
+    void* c = d.standard_moe ? out : (c_opt ? c_opt : ws + L.c);
     hipError_t e = launch_combine(Y, inv, gate, (int)d.T, (int)d.k, (int)d.l, d.act_dtype, c, s);
     if (e != hipSuccess) return e;
-    const DenseGemm g = gemm_out(d, c, hs, W_up, sh ? sh->W_s2 : nullptr, out);
-    e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
+    if (d.standard_moe && c_opt) {
+        const size_t es = d.act_dtype == LMOE_BF16 ? 2 : 4;
+        e = hipMemcpyAsync(c_opt, out, (size_t)d.T * d.l * es, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return e;
+    }
+    if (!d.standard_moe || shared_dense(d)) {
+        const DenseGemm g = gemm_out(d, c, hs, W_up, sh ? sh->W_s2 : nullptr, out);
+        e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
+    }
     if (e != hipSuccess || !shared_fp8(d)) return e;
     // out += s_h * (q_h W_s2^T) * s_w2, added to the bf16 up-projection
     uint8_t* qh = (uint8_t*)(ws + L.q_h);
@@ -341,7 +366,7 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
     f.B = (const uint8_t*)sh->W_s2;
     f.ldb = d.f_s;
     f.b_scale = sh->W_s2_scale;
-    f.epi = EPI_ADD_BF16;
+    f.epi = EPI_ADD;
     f.C = (uint16_t*)out;
     f.ldc = d.d;
     return launch_fp8_gemm(f, s);
@@ -357,7 +382,8 @@ int lmoe_validate_dims(const lmoe_dims* d) {
     if (!d) return LMOE_ERR_NULL;
     if (d->T < 1 || d->T > (1 << 24)) return LMOE_ERR_SHAPE;
     if (d->d < 256 || d->d % 256 != 0 || d->d > 65536) return LMOE_ERR_SHAPE;
-    if (d->l * 4 != d->d) return LMOE_ERR_SHAPE;
+    if (d->standard_moe != 0 && d->standard_moe != 1) return LMOE_ERR_SHAPE;
+    if (d->standard_moe ? (d->l != d->d || d->router_latent != 0) : d->l * 4 != d->d) return LMOE_ERR_SHAPE;
     if (d->E < 1 || d->E > 1024) return LMOE_ERR_SHAPE;
     if (d->k < 1 || d->k > d->E) return LMOE_ERR_SHAPE;
     if (d->router_latent != 0 && d->router_latent != 1) return LMOE_ERR_SHAPE;
@@ -425,7 +451,8 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, 
     LMOE_TRY(lmoe_validate_dims(dims));
     const lmoe_dims& d = *dims;
     if (k != d.k) return LMOE_ERR_SHAPE;
-    LMOE_TRY(check_ptrs({x, W_down, W_router, W_up, out}));
+    LMOE_TRY(check_ptrs({x, W_router, out}));
+    if (!d.standard_moe) LMOE_TRY(check_ptrs({W_down, W_up}));
     LMOE_TRY(check_optional(router_bias));
     LMOE_TRY(check_experts(d, experts));
     LMOE_TRY(check_shared(d, shared));
@@ -446,7 +473,7 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, 
     char* ws = (char*)workspace;
     const Layout L = plan(d);
     hipStream_t s = (hipStream_t)stream;
-    void* z = dv.z ? dv.z : ws + L.z;
+    const void* z = d.standard_moe ? x : (dv.z ? dv.z : ws + L.z);
     float* logits = dv.logits ? dv.logits : (float*)(ws + L.logits);
     int32_t* idx = dv.topk_idx ? dv.topk_idx : (int32_t*)(ws + L.idx);
     float* gate = dv.topk_gate ? dv.topk_gate : (float*)(ws + L.gate);
@@ -454,16 +481,15 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, 
     int32_t* offsets = dv.offsets ? dv.offsets : (int32_t*)(ws + L.offsets);
     int32_t* perm = dv.perm ? dv.perm : (int32_t*)(ws + L.perm);
     int32_t* inv = dv.inv ? dv.inv : (int32_t*)(ws + L.inv);
-    void* c = dv.c ? dv.c : ws + L.c;
     void* hs = ws + L.hs;
     const TileTable tt = tile_table(d, ws, L);
 
-    hipError_t e =
-        run_project_route(d, x, W_down, W_router, router_bias, shared, z, logits, idx, gate, hs, ws, L, s);
+    hipError_t e = run_project_route(d, x, W_down, W_router, router_bias, shared, (void*)z, logits, idx, gate, hs,
+                                     ws, L, s);
     if (e == hipSuccess)
         e = launch_permute(idx, d.T * d.k, (int)d.E, (int32_t*)(ws + L.hist), counts, offsets, perm, inv, &tt, s);
     if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, ws + L.Y, tt, ws, L, s);
-    if (e == hipSuccess) e = run_combine_up(d, ws + L.Y, inv, gate, W_up, shared, hs, c, out, ws, L, s);
+    if (e == hipSuccess) e = run_combine_up(d, ws + L.Y, inv, gate, W_up, shared, hs, dv.c, out, ws, L, s);
     return hip_status(e);
 }
 
@@ -473,7 +499,8 @@ int lmoe_project_route(const lmoe_dims* dims, const void* x, const void* W_down,
                        void* stream) {
     LMOE_TRY(lmoe_validate_dims(dims));
     const lmoe_dims& d = *dims;
-    LMOE_TRY(check_ptrs({x, W_down, W_router, z, logits, topk_idx, topk_gate}));
+    LMOE_TRY(check_ptrs({x, W_router, logits, topk_idx, topk_gate}));
+    if (!d.standard_moe) LMOE_TRY(check_ptrs({W_down, z}));  // a standard MoE has no z of its own
     LMOE_TRY(check_optional(router_bias));
     LMOE_TRY(check_shared(d, shared));
     if (shared) LMOE_TRY(check_ptrs({hs}));
@@ -516,15 +543,15 @@ int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv, co
                     size_t workspace_bytes, void* stream) {
     LMOE_TRY(lmoe_validate_dims(dims));
     const lmoe_dims& d = *dims;
-    LMOE_TRY(check_ptrs({Y, inv, topk_gate, W_up, out}));
+    LMOE_TRY(check_ptrs({Y, inv, topk_gate, out}));
+    if (!d.standard_moe) LMOE_TRY(check_ptrs({W_up}));
     LMOE_TRY(check_shared(d, shared));
     if (shared) LMOE_TRY(check_ptrs({hs}));
     LMOE_TRY(check_optional(c));
     LMOE_TRY(check_workspace(d, workspace, workspace_bytes));
     char* ws = (char*)workspace;
     const Layout L = plan(d);
-    return hip_status(run_combine_up(d, Y, inv, topk_gate, W_up, shared, hs, c ? c : ws + L.c, out, ws, L,
-                                     (hipStream_t)stream));
+    return hip_status(run_combine_up(d, Y, inv, topk_gate, W_up, shared, hs, c, out, ws, L, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void dense_fma_kernel(DenseGemm g) {
                 v = fmaxf(v, 0.f);
                 v *= v;
             }
-            ((float*)G.C)[(int64_t)m * G.ldc + nc] = v;
+            float* c = (float*)G.C + (int64_t)m * G.ldc + nc;
+            *c = G.epi == EPI_ADD ? *c + v : v;
         }
     }
 }

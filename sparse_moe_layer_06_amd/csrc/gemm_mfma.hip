@@ -336,6 +336,9 @@ __device__ __forceinline__ void dense_store1(const DenseGemm& g, int m, int n, f
     const int64_t off = (int64_t)m * G.ldc + nc;
     if (G.epi == EPI_F32_BIAS) {
         ((float*)G.C)[off] = v + (G.bias ? G.bias[nc] : 0.f);
+    } else if (G.epi == EPI_ADD) {
+        uint16_t* c = (uint16_t*)G.C + off;
+        *c = f32_to_bf16_rne(bf16_to_f32(*c) + v);
     } else {
         ((uint16_t*)G.C)[off] = f32_to_bf16_rne(apply_epi(G.epi, v));
     }
@@ -357,6 +360,13 @@ __device__ __forceinline__ void dense_store4(const DenseGemm& g, int m, int n, c
                 o.w += b.w;
             }
             *reinterpret_cast<float4*>((float*)G.C + off) = o;
+        } else if (G.epi == EPI_ADD) {
+            uint2* c = reinterpret_cast<uint2*>((uint16_t*)G.C + off);
+            const uint2 old = *c;
+            uint2 o;
+            o.x = pack_bf16x2(bf16_to_f32((uint16_t)(old.x & 0xFFFFu)) + v[0], bf16_to_f32((uint16_t)(old.x >> 16)) + v[1]);
+            o.y = pack_bf16x2(bf16_to_f32((uint16_t)(old.y & 0xFFFFu)) + v[2], bf16_to_f32((uint16_t)(old.y >> 16)) + v[3]);
+            *c = o;
         } else {
             uint2 o;
             o.x = pack_bf16x2(apply_epi(G.epi, v[0]), apply_epi(G.epi, v[1]));
@@ -1003,7 +1013,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
                     float v[4] = {acc[tm][tn][q * 4 + 0] * sa * sb.x, acc[tm][tn][q * 4 + 1] * sa * sb.y,
                                   acc[tm][tn][q * 4 + 2] * sa * sb.z, acc[tm][tn][q * 4 + 3] * sa * sb.w};
                     uint2* dst = reinterpret_cast<uint2*>(crow + n);
-                    if (g.epi == EPI_ADD_BF16) {
+                    if (g.epi == EPI_ADD) {
                         const uint2 old = *dst;
                         v[0] += bf16_to_f32((uint16_t)(old.x & 0xFFFFu));
                         v[1] += bf16_to_f32((uint16_t)(old.x >> 16));

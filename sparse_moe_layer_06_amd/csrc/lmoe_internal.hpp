@@ -14,7 +14,7 @@ enum Epi : int {
     EPI_STORE = 0,     // C = acc, stored in the activation dtype
     EPI_F32_BIAS = 1,  // C = acc (+ bias[col]), stored fp32
     EPI_RELU2 = 2,     // C = max(0, acc * scale)^2, activation dtype
-    EPI_ADD_BF16 = 3,  // C = C + acc * scale, bf16 in place (fp8 GEMM only)
+    EPI_ADD = 3,       // C = C + acc (times the fp8 scales), in place, activation dtype
 };
 
 // One contiguous range of output columns [n_begin, n_end) of a dense GEMM,
@@ -91,7 +91,7 @@ struct GroupedGemm {
 
 // FP8 (E4M3 x E4M3) GEMM with per-row scales, fp32 accumulate:
 // C[m][n] = epi(a_scale[m] * b_scale[n] * sum_k A[m][k] * B[n][k]), epi
-// EPI_RELU2 (store bf16) or EPI_ADD_BF16.  K is a multiple of 128; N, lda,
+// EPI_RELU2 (store bf16) or EPI_ADD.  K is a multiple of 128; N, lda,
 // ldb and ldc are multiples of 16.
 struct Fp8Gemm {
     int M, N, K;

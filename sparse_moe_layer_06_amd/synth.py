@@ -51,7 +51,8 @@ class LayerDims:
     'nvfp4'); zipf_bias adds the skewed router bias; router_latent makes the
     router read the latent z (W_r [E][l]) instead of x (W_r [E][d]);
     shared_fp8 stores the shared expert's weights as E4M3 codes with one fp32
-    scale per output row.
+    scale per output row; standard_moe is the comparison layer without the
+    latent projections (l = d, no W_down / W_up).
     """
     name: str
     T: int
@@ -66,6 +67,7 @@ class LayerDims:
     zipf_bias: bool = False
     router_latent: bool = False
     shared_fp8: bool = False
+    standard_moe: bool = False
 
     def with_(self, **kw) -> "LayerDims":
         return dataclasses.replace(self, **kw)
@@ -75,7 +77,8 @@ class LayerDims:
         """Algorithmic FLOPs of one forward: projections, router, experts, shared."""
         T, d, l, E, k, f, fs = self.T, self.d, self.l, self.E, self.k, self.f, self.f_s
         router_in = l if self.router_latent else d
-        return 2.0 * T * d * l + 2.0 * T * router_in * E + 4.0 * T * k * l * f + 2.0 * T * l * d + 4.0 * T * d * fs
+        proj = 0.0 if self.standard_moe else 4.0 * T * d * l  # down- and up-projection
+        return proj + 2.0 * T * router_in * E + 4.0 * T * k * l * f + 4.0 * T * d * fs
 
 
 # The five workloads.  Sizes follow the Ultra layer (d = 8192, 512 experts,
@@ -194,7 +197,8 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
     T, d, l, E, f, fs = cfg.T, cfg.d, cfg.l, cfg.E, cfg.f, cfg.f_s
     inp: Dict[str, Optional[torch.Tensor]] = {}
     inp["x"] = _normal((T, d), 1.0, _gen(dev, seed, "x"), dev, act)
-    inp["W_down"] = _normal((l, d), 1.0 / math.sqrt(d), _gen(dev, seed, "W_down"), dev, act)
+    inp["W_down"] = (None if cfg.standard_moe
+                     else _normal((l, d), 1.0 / math.sqrt(d), _gen(dev, seed, "W_down"), dev, act))
     r_in = l if cfg.router_latent else d
     inp["W_r"] = _normal((E, r_in), 1.0 / math.sqrt(r_in), _gen(dev, seed, "W_r"), dev, act)
     if cfg.zipf_bias:
@@ -204,7 +208,8 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
         inp["b_r"] = None
     inp.update(_expert_stack(cfg, "W1", seed, dev))
     inp.update(_expert_stack(cfg, "W2", seed, dev))
-    inp["W_up"] = _normal((d, l), 1.0 / math.sqrt(l), _gen(dev, seed, "W_up"), dev, act)
+    inp["W_up"] = (None if cfg.standard_moe
+                   else _normal((d, l), 1.0 / math.sqrt(l), _gen(dev, seed, "W_up"), dev, act))
     if fs > 0 and cfg.shared_fp8:
         for name, shape, fan_in in (("W_s1", (fs, d), d), ("W_s2", (d, fs), fs)):
             W = _normal(shape, 1.0 / math.sqrt(fan_in), _gen(dev, seed, name), dev, torch.float32)

@@ -63,6 +63,13 @@ SMALL = {
                              act="bf16", experts="bf16", shared_fp8=True),
     "fp8_shared_few": TINY.with_(name="fp8_shared_few", T=5, d=1024, l=256, E=8, k=2, f=128, f_s=384,
                                  act="bf16", experts="nvfp4", shared_fp8=True, router_latent=True),
+    # the standard MoE comparison layer (no latent projections, experts in d)
+    "standard_bf16": TINY.with_(name="standard_bf16", T=150, d=256, l=256, E=16, k=3, f=128, f_s=128,
+                                act="bf16", experts="bf16", standard_moe=True),
+    "standard_f32": TINY.with_(name="standard_f32", T=40, l=256, E=8, k=2, f_s=64, standard_moe=True),
+    "standard_fp8_zipf": TINY.with_(name="standard_fp8_zipf", T=24, d=512, l=512, E=32, k=6, f=256, f_s=256,
+                                    act="bf16", experts="bf16", shared_fp8=True, zipf_bias=True,
+                                    standard_moe=True),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
@@ -126,7 +133,8 @@ def test_exact_logit_ties_break_to_lower_id():
 
 
 def test_staged_entry_points_compose_to_forward():
-    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide", "latent_bf16", "fp8_shared"):
+    for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide", "latent_bf16", "fp8_shared",
+                 "standard_bf16"):
         cfg = SMALL[name]
         log(f"case staged {name}")
         inp = small_inputs(cfg)
@@ -134,7 +142,8 @@ def test_staged_entry_points_compose_to_forward():
         fused = B.forward(cfg, inp, workspace=ws)
         r = B.project_route(cfg, inp, ws)
         p = B.permute(cfg, r["idx"], ws)
-        Y = B.experts_ffn(cfg, inp, r["z"], p["offsets"], p["perm"], ws)
+        z = inp["x"] if cfg.standard_moe else r["z"]  # a standard MoE computes on x
+        Y = B.experts_ffn(cfg, inp, z, p["offsets"], p["perm"], ws)
         o = B.combine_up(cfg, inp, Y, p["inv"], r["gate"], r["hs"], ws, cfg.T)
         torch.cuda.synchronize()
         assert torch.equal(o["out"], fused), name
@@ -294,6 +303,15 @@ def test_prefill_fp8_shared_sampled():
     log(f"case {cfg}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     P.run_and_check(cfg, inp, n_sample=12, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_decode_standard_moe_full_size():
+    # the comparison layer at decode: 128 experts of d -> 2048 -> d, top-6
+    cfg = CFG["decode_bf16_zipf"].with_(name="decode_standard_moe", l=8192, E=128, k=6, standard_moe=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=6, lazy_experts=True, report=log)
 
 
 @pytest.mark.timeout(900)

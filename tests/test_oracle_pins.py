@@ -36,6 +36,7 @@ SMALL_NVFP4 = TINY.with_(name="small_nvfp4", T=40, d=128, l=32, E=8, k=2, f=64, 
 SMALL_ZIPF = SMALL_BF16.with_(name="small_zipf", zipf_bias=True, f_s=0)
 SMALL_LATENT = SMALL_BF16.with_(name="small_latent", router_latent=True)
 SMALL_FP8 = SMALL_BF16.with_(name="small_fp8_shared", f_s=128, shared_fp8=True)
+SMALL_STANDARD = SMALL_BF16.with_(name="small_standard", l=128, E=8, k=2, standard_moe=True)
 TINY_LATENT = TINY.with_(name="tiny_latent", router_latent=True)
 
 
@@ -199,12 +200,12 @@ def dense_bruteforce(inp, k):
     """Every expert on every token, weighted by the full-E softmax masked to
     the top-k set and renormalised; one up-projection per expert."""
     x = O.as_f64(inp["x"])
-    z = x @ O.as_f64(inp["W_down"]).T
+    z = x @ O.as_f64(inp["W_down"]).T if inp.get("W_down") is not None else x
     s = O.router_logits(O.router_input(inp["x"], inp), inp["W_r"], inp.get("b_r")).astype(np.float64)
     E = s.shape[1]
-    W_up = O.as_f64(inp["W_up"])
+    W_up = O.as_f64(inp["W_up"]) if inp.get("W_up") is not None else None
     ew = O.ExpertWeights(inp)
-    out = np.zeros((x.shape[0], W_up.shape[0]))
+    out = np.zeros((x.shape[0], x.shape[1]))
     for t in range(x.shape[0]):
         rank = brute_force_topk_set(s[t].astype(np.float32), k)
         mask = (rank < k).astype(np.float64)
@@ -215,13 +216,14 @@ def dense_bruteforce(inp, k):
                 continue
             W1, W2 = ew(e)
             h = np.maximum(W1 @ z[t], 0) ** 2
-            out[t] += p[e] * (W_up @ (W2 @ h))
+            out[t] += p[e] * (W_up @ (W2 @ h) if W_up is not None else W2 @ h)
     if inp.get("W_s1") is not None:  # pinned on its own (test_shared_expert_*)
         out += O.shared_expert(inp["x"], inp)
     return out
 
 
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_ZIPF, SMALL_LATENT, TINY_LATENT, SMALL_FP8,
+                                 SMALL_STANDARD,
                                  TINY.with_(k=1), TINY.with_(E=5, k=5)], ids=lambda c: f"{c.name}-E{c.E}k{c.k}")
 def test_sparse_equals_dense_bruteforce(cfg):
     inp = host_inputs(cfg)
@@ -519,3 +521,19 @@ def test_shared_expert_fp8_against_torch_casts():
     # and the whole layer with W_up zeroed is the shared expert alone
     inp["W_up"] = np.zeros_like(inp["W_up"])
     assert rel_err(O.forward(inp, cfg.k)["out"], ref.numpy()) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Standard MoE (the overview's comparison layer: no latent projections)
+# ---------------------------------------------------------------------------
+
+def test_standard_moe_is_latent_layer_with_identity_projections():
+    # z = x and out = c are the latent layer with W_down = W_up = I (d x d),
+    # exactly, in float64
+    inp = host_inputs(SMALL_STANDARD)
+    std = O.forward(inp, SMALL_STANDARD.k)
+    d = inp["x"].shape[1]
+    eye = dict(inp, W_down=np.eye(d), W_up=np.eye(d))
+    lat = O.forward(eye, SMALL_STANDARD.k)
+    assert np.array_equal(std["idx"], lat["idx"])
+    assert np.array_equal(std["out"], lat["out"]) and np.array_equal(std["z"], O.as_f64(inp["x"]))
