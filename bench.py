@@ -89,18 +89,46 @@ def prepared(cfg, inp, layout, B):
     return cfg, inp
 
 
-def prefill(cfg, steps, warmup, torch, B, synth, layout="tiled"):
+def captured(make_call, torch):
+    """One forward recorded into a HIP graph on torch's capture stream.  The
+    library allocates nothing and enqueues only kernels, so a replay is the
+    same launches without the host-side work of the call."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        make_call()()
+    torch.cuda.synchronize()
+    return g
+
+
+def graph_matches(g, out, torch):
+    """Replay once and compare with what the eager call left in `out`."""
+    ref = out.clone()
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    return bool(torch.equal(out, ref))
+
+
+def prefill(cfg, steps, warmup, torch, B, synth, layout="tiled", graph=False):
     log(f"bench: generating inputs {cfg.name}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
     ws = B.alloc_workspace(cfg)
-    call = B.Call(*prepared(cfg, inp, layout, B), out, ws)
+    pcfg, pinp = prepared(cfg, inp, layout, B)
+    call = B.Call(pcfg, pinp, out, ws)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     log(f"bench: timing {steps} steps")
     ms, wall = time_steps(call, steps, torch)
     log(f"bench: {ms:.3f} ms/step")
+    if graph:  # the same step replayed from a HIP graph (reported, not the headline)
+        g = captured(lambda: B.Call(pcfg, pinp, out, ws), torch)
+        same = graph_matches(g, out, torch)
+        gms, _ = time_steps(g.replay, steps, torch)
+        graph = dict(ms_per_step=gms, matches_eager=same)
+        log(f"bench: {gms:.3f} ms/step replayed from a HIP graph")
+        del g
 
     # Per-kernel durations over the same number of steps (separate pass, so the
     # headline timing has no extra events between launches).
@@ -111,16 +139,17 @@ def prefill(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     per = kt.by_kernel()
     kernels = {n: dict(avg_ms=sum(v) / len(v), launches_per_step=len(v) / steps,
                        ms_per_step=sum(v) / steps) for n, v in per.items()}
-    return inp, out, ms, wall, kernels
+    return inp, out, ms, wall, kernels, graph
 
 
-def decode(cfg, steps, torch, B, synth, layout="tiled"):
+def decode(cfg, steps, torch, B, synth, layout="tiled", graph=False):
     log(f"bench: generating inputs {cfg.name}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
     ws = B.alloc_workspace(cfg)
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    call = B.Call(*prepared(cfg, inp, layout, B), out, ws, debug=dict(counts=counts))
+    pcfg, pinp = prepared(cfg, inp, layout, B)
+    call = B.Call(pcfg, pinp, out, ws, debug=dict(counts=counts))
     # Reading 1 GiB between steps evicts L2 and the 256 MB Infinity Cache; a read
     # leaves only clean lines, so the timed step pays no write-back of flush data.
     flush = torch.ones(1 << 29, dtype=torch.float16, device="cuda")
@@ -138,6 +167,21 @@ def decode(cfg, steps, torch, B, synth, layout="tiled"):
         times.append((a, b))
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in times)[len(times) // 2]
+    if graph:  # the same step replayed from a HIP graph, same eviction between steps
+        g = captured(lambda: B.Call(pcfg, pinp, out, ws), torch)
+        same = graph_matches(g, out, torch)
+        gtimes = []
+        for _ in range(steps):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            g.replay()
+            b.record(s)
+            gtimes.append((a, b))
+        torch.cuda.synchronize()
+        graph = dict(ms_per_step=sorted(a.elapsed_time(b) for a, b in gtimes)[len(gtimes) // 2],
+                     matches_eager=same)
+        del g
     # per-kernel durations, a separate pass with the same eviction between steps
     n_k = min(steps, 20)
     with B.KernelTimer(capacity=64 * n_k) as kt:
@@ -159,12 +203,13 @@ def decode(cfg, steps, torch, B, synth, layout="tiled"):
                          f"{', standard MoE (experts in d)' if cfg.standard_moe else ''}", tokens_per_s=T / (ms * 1e-3),
                 ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
                 hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
-                "1 GiB buffer read between steps (cache eviction)" % steps, kernels=kernels)
+                "1 GiB buffer read between steps (cache eviction)" % steps, kernels=kernels,
+                **({"hipgraph": graph} if graph else {}))
 
 
 def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     """The other MFMA-bound workloads (same metric, reported beside the headline)."""
-    inp, out, ms, _, kernels = prefill(cfg, steps, warmup, torch, B, synth, layout)
+    inp, out, ms, _, kernels, _ = prefill(cfg, steps, warmup, torch, B, synth, layout)
     gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
     g = kernels.get(gname)
     res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
@@ -257,7 +302,8 @@ def main():
 
     B.lib()
     cfg = synth.CONFIGS[args.workload]
-    inp, out, ms, wall, kernels = prefill(cfg, args.steps, args.warmup, torch, B, synth, args.expert_layout)
+    inp, out, ms, wall, kernels, graph = prefill(cfg, args.steps, args.warmup, torch, B, synth,
+                                                 args.expert_layout, graph=True)
     tokens_per_s = cfg.T / (ms * 1e-3)
     layer_tflops = cfg.flops / (ms * 1e-3) / 1e12
 
@@ -297,10 +343,12 @@ def main():
         "wall_s_timed": wall,
         "roofline": roofline,
         "kernels": kernels,
+        # the graded figure is the eager one above; this is the same step replayed from a HIP graph
+        "hipgraph": graph,
     }
     if not args.no_decode:
         result["decode"] = decode(synth.CONFIGS["decode_bf16_zipf"], args.decode_steps, torch, B, synth,
-                                  args.expert_layout)
+                                  args.expert_layout, graph=True)
     if not args.no_extra:
         C = synth.CONFIGS
         extra = [C[n] for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload]
