@@ -33,6 +33,11 @@ paragraph):
      each of the shared expert's inputs (x_t, then its hidden layer as stored
      in bf16) is quantised per token to E4M3 with scale max|v|/448 before
      its product
+  FP8 projections (the Ultra model card, "Model design", keeps the latent
+  projections out of NVFP4, in BF16 or MXFP8; here the 8-bit option takes
+  the shared expert's scheme, not MX blocks): W_down and W_up as E4M3 codes
+  times one scale per output row, each input quantised per token like the
+  shared expert's (x before W_down; c as stored in bf16 before W_up).
   Without W_down and W_up the same steps describe the standard MoE layer the
   overview compares against (section 2.2 table: 128 experts, top-6, experts
   in the hidden width): z_t = x_t and out_t = c_t (+ shared expert).
@@ -215,6 +220,26 @@ def down_project(x: np.ndarray, W_down: np.ndarray) -> np.ndarray:
     return as_f64(x) @ as_f64(W_down).T
 
 
+def fp8_product(v: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """v W^T for E4M3 weights W = codes times one scale per output row, with
+    the rows of v quantised per row to E4M3 first (quantize_rows_fp8): the
+    product of the decoded codes, times the row scale of v and the column
+    scale of W."""
+    qv, sv = quantize_rows_fp8(as_f64(v))
+    sw = np.asarray(scales, dtype=np.float64)
+    return (e4m3_value(qv) @ e4m3_value(codes).T) * sv.astype(np.float64)[:, None] * sw[None, :]
+
+
+def project(v: np.ndarray, inp: dict, name: str) -> np.ndarray:
+    """v W^T for the projection weight inp[name] (W_down or W_up) in its
+    stored format: bf16 / fp32 values, or E4M3 codes (uint8) with per-row
+    scales under name + '_scale'."""
+    W = np.asarray(inp[name])
+    if W.dtype == np.uint8:
+        return fp8_product(v, W, inp[name + "_scale"])
+    return as_f64(v) @ as_f64(W).T
+
+
 def router_logits(x: np.ndarray, W_r: np.ndarray, b_r=None) -> np.ndarray:
     """Step 2: s_t = W_r x_t (+ b) in float64, returned as float32 (the
     precision in which the top-k decision is taken)."""
@@ -269,7 +294,7 @@ def router_input(x: np.ndarray, inp: dict) -> np.ndarray:
         return x
     if width != np.asarray(inp["W_down"]).shape[0]:
         raise ValueError("W_r width is neither d nor l")
-    return store_round(down_project(x, inp["W_down"]), x)
+    return store_round(project(x, inp, "W_down"), x)
 
 
 def route(inp: dict, k: int):
@@ -292,7 +317,7 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
         x = x[np.asarray(tokens)]
     experts = experts or ExpertWeights(inp)
     # a standard MoE (no W_down / W_up, experts in d) routes and computes on x
-    z = down_project(x, inp["W_down"]) if inp.get("W_down") is not None else as_f64(x)
+    z = project(x, inp, "W_down") if inp.get("W_down") is not None else as_f64(x)
     s = router_logits(router_input(x, inp), inp["W_r"], inp.get("b_r"))
     idx = select_topk(s, k)
     g = gate_weights(s, idx)
@@ -302,7 +327,12 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
         for j in range(k):
             W1_e, W2_e = experts(idx[t, j])
             c[t] += g[t, j] * expert_ffn(z[t], W1_e, W2_e)
-    out = c @ as_f64(inp["W_up"]).T if inp.get("W_up") is not None else c.copy()
+    if inp.get("W_up") is None:
+        out = c.copy()
+    elif np.asarray(inp["W_up"]).dtype == np.uint8:  # E4M3 W_up reads c as stored
+        out = project(store_round(c, x), inp, "W_up")
+    else:
+        out = project(c, inp, "W_up")
     if inp.get("W_s1") is not None:
         out = out + shared_expert(x, inp)
     return dict(z=z, logits=s, idx=idx, gate=g, c=c, out=out)
@@ -316,10 +346,5 @@ def shared_expert(x: np.ndarray, inp: dict) -> np.ndarray:
     if W1.dtype != np.uint8:
         hs = np.maximum(as_f64(x) @ as_f64(W1).T, 0.0) ** 2
         return hs @ as_f64(W2).T
-    s1 = np.asarray(inp["W_s1_scale"], dtype=np.float64)
-    s2 = np.asarray(inp["W_s2_scale"], dtype=np.float64)
-    qx, sx = quantize_rows_fp8(as_f64(x))
-    pre = (e4m3_value(qx) @ e4m3_value(W1).T) * sx.astype(np.float64)[:, None] * s1[None, :]
-    hs = round_to_bf16(np.maximum(pre, 0.0) ** 2)
-    qh, sh = quantize_rows_fp8(hs)
-    return (e4m3_value(qh) @ e4m3_value(W2).T) * sh.astype(np.float64)[:, None] * s2[None, :]
+    hs = round_to_bf16(np.maximum(fp8_product(x, W1, inp["W_s1_scale"]), 0.0) ** 2)
+    return fp8_product(hs, W2, inp["W_s2_scale"])

@@ -13,8 +13,9 @@ Recipe (one stream per tensor, so every tensor is reproducible alone):
     of that matrix (d for W_down, W_r, W_s1; l for W1, W_up and a latent
     router's W_r; f for W2; f_s for W_s2).  Draws are fp32, then rounded to
     bf16 (round to nearest even) for bf16 tensors.
-  * FP8 shared-expert weights (shared_fp8): the same fp32 draws, stored as
-    E4M3 codes with one fp32 scale per output row (max |row| / 448).
+  * FP8 shared-expert weights (shared_fp8) and FP8 projection weights
+    (proj_fp8, W_down and W_up): the same fp32 draws, stored as E4M3 codes
+    with one fp32 scale per output row (max |row| / 448).
   * The skewed-routing workload adds a per-expert router bias
     b_e = 2 * log(1 / (e + 1)), stored in fp32.
   * NVFP4 expert weights: W ~ N(0, 1/fan_in) in fp32, a block scale
@@ -52,7 +53,8 @@ class LayerDims:
     router read the latent z (W_r [E][l]) instead of x (W_r [E][d]);
     shared_fp8 stores the shared expert's weights as E4M3 codes with one fp32
     scale per output row; standard_moe is the comparison layer without the
-    latent projections (l = d, no W_down / W_up).
+    latent projections (l = d, no W_down / W_up); proj_fp8 stores W_down and
+    W_up that way too.
     """
     name: str
     T: int
@@ -68,6 +70,7 @@ class LayerDims:
     router_latent: bool = False
     shared_fp8: bool = False
     standard_moe: bool = False
+    proj_fp8: bool = False
 
     def with_(self, **kw) -> "LayerDims":
         return dataclasses.replace(self, **kw)
@@ -198,7 +201,7 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
     inp: Dict[str, Optional[torch.Tensor]] = {}
     inp["x"] = _normal((T, d), 1.0, _gen(dev, seed, "x"), dev, act)
     inp["W_down"] = (None if cfg.standard_moe
-                     else _normal((l, d), 1.0 / math.sqrt(d), _gen(dev, seed, "W_down"), dev, act))
+                     else _proj_weight(cfg, (l, d), d, _gen(dev, seed, "W_down"), dev, act, inp, "W_down"))
     r_in = l if cfg.router_latent else d
     inp["W_r"] = _normal((E, r_in), 1.0 / math.sqrt(r_in), _gen(dev, seed, "W_r"), dev, act)
     if cfg.zipf_bias:
@@ -209,7 +212,7 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
     inp.update(_expert_stack(cfg, "W1", seed, dev))
     inp.update(_expert_stack(cfg, "W2", seed, dev))
     inp["W_up"] = (None if cfg.standard_moe
-                   else _normal((d, l), 1.0 / math.sqrt(l), _gen(dev, seed, "W_up"), dev, act))
+                   else _proj_weight(cfg, (d, l), l, _gen(dev, seed, "W_up"), dev, act, inp, "W_up"))
     if fs > 0 and cfg.shared_fp8:
         for name, shape, fan_in in (("W_s1", (fs, d), d), ("W_s2", (d, fs), fs)):
             W = _normal(shape, 1.0 / math.sqrt(fan_in), _gen(dev, seed, name), dev, torch.float32)
@@ -221,6 +224,15 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
         inp["W_s1"] = None
         inp["W_s2"] = None
     return inp
+
+
+def _proj_weight(cfg: LayerDims, shape, fan_in: int, gen, dev, act, inp, name: str):
+    """A projection weight in the activation dtype, or as E4M3 codes (its
+    per-row scales stored under name + '_scale') with proj_fp8."""
+    if not cfg.proj_fp8:
+        return _normal(shape, 1.0 / math.sqrt(fan_in), gen, dev, act)
+    codes, inp[name + "_scale"] = _fp8_rows(_normal(shape, 1.0 / math.sqrt(fan_in), gen, dev, torch.float32))
+    return codes
 
 
 def _fp8_rows(W: torch.Tensor):

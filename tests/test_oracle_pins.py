@@ -38,6 +38,7 @@ SMALL_LATENT = SMALL_BF16.with_(name="small_latent", router_latent=True)
 SMALL_FP8 = SMALL_BF16.with_(name="small_fp8_shared", f_s=128, shared_fp8=True)
 SMALL_STANDARD = SMALL_BF16.with_(name="small_standard", l=128, E=8, k=2, standard_moe=True)
 TINY_LATENT = TINY.with_(name="tiny_latent", router_latent=True)
+SMALL_FP8_PROJ = SMALL_BF16.with_(name="small_fp8_proj", proj_fp8=True)
 
 
 # ---------------------------------------------------------------------------
@@ -537,3 +538,52 @@ def test_standard_moe_is_latent_layer_with_identity_projections():
     lat = O.forward(eye, SMALL_STANDARD.k)
     assert np.array_equal(std["idx"], lat["idx"])
     assert np.array_equal(std["out"], lat["out"]) and np.array_equal(std["z"], O.as_f64(inp["x"]))
+
+
+# ---------------------------------------------------------------------------
+# FP8 down- and up-projections
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("latent", [False, True], ids=["router_in_d", "router_in_l"])
+def test_fp8_projections_against_torch_casts(latent):
+    # the layer with E4M3 W_down / W_up re-derived with torch's float8 and
+    # bf16 casts: z from the per-token codes of x, the routed part by the
+    # dense brute force (every expert, masked softmax), and out from the
+    # per-token codes of c as stored in bf16
+    cfg = SMALL_FP8_PROJ.with_(router_latent=latent)
+    inp = host_inputs(cfg)
+    f8 = torch.float8_e4m3fn
+
+    def quant(v64):
+        v = torch.from_numpy(np.asarray(v64, dtype=np.float64)).to(torch.float32)
+        amax = v.abs().amax(dim=1)
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        return (v / sc[:, None]).to(f8).to(torch.float64) * sc.to(torch.float64)[:, None]
+
+    def weights(name):
+        return (torch.from_numpy(inp[name]).view(f8).to(torch.float64)
+                * torch.from_numpy(inp[name + "_scale"]).to(torch.float64)[:, None])
+
+    def bf16(v):
+        return torch.as_tensor(v).to(torch.bfloat16).to(torch.float64)
+
+    x = torch.from_numpy(O.as_f64(inp["x"]))
+    z = quant(x.numpy()) @ weights("W_down").T
+    r_in = bf16(z) if latent else x  # a latent router reads z as stored
+    s = (r_in @ torch.from_numpy(O.as_f64(inp["W_r"])).T).to(torch.float32).numpy()
+    ew = O.ExpertWeights(inp)
+    c = np.zeros((x.shape[0], z.shape[1]))
+    for t in range(x.shape[0]):
+        rank = brute_force_topk_set(s[t], cfg.k)
+        p = np.exp(s[t].astype(np.float64) - s[t].max()) * (rank < cfg.k)
+        p /= p.sum()
+        for e in np.nonzero(p)[0]:
+            W1, W2 = ew(e)
+            c[t] += p[e] * (W2 @ (np.maximum(W1 @ z[t].numpy(), 0) ** 2))
+    out = quant(bf16(c).numpy()) @ weights("W_up").T
+    Ws1, Ws2 = (torch.from_numpy(O.as_f64(inp[n])) for n in ("W_s1", "W_s2"))
+    out = out + torch.relu(x @ Ws1.T).square() @ Ws2.T
+    got = O.forward(inp, cfg.k)
+    assert rel_err(got["z"], z.numpy()) <= 1e-12
+    assert rel_err(got["c"], c) <= 1e-12
+    assert rel_err(got["out"], out.numpy()) <= 1e-12
