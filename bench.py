@@ -194,13 +194,16 @@ def decode(cfg, steps, torch, B, synth, layout="tiled", graph=False):
     touched = int((counts > 0).sum().item())
     l, f, d, E, T = cfg.l, cfg.f, cfg.d, cfg.E, cfg.T
     r_in = l if cfg.router_latent else d  # router weights W_r [E][r_in]
-    proj = 0 if cfg.standard_moe else 2 * d * l  # W_down and W_up
-    bytes_alg = touched * 2 * l * f * 2 + (proj + r_in * E) * 2 + 2 * T * d * 2 + (E * 4 if cfg.zipf_bias else 0)
+    # W_down and W_up: bf16, or E4M3 codes plus one fp32 scale per row
+    proj = 0 if cfg.standard_moe else (2 * d * l + 4 * (l + d) if cfg.proj_fp8 else 2 * d * l * 2)
+    bytes_alg = (touched * 2 * l * f * 2 + proj + r_in * E * 2 + 2 * T * d * 2
+                 + (E * 4 if cfg.zipf_bias else 0))
     gbs = bytes_alg / (ms * 1e-3) / 1e9
     return dict(workload=f"{cfg.name} T={T} d={d} l={l} E={E} k={cfg.k} f={f}, {cfg.experts} experts "
                          f"({layout if cfg.experts == 'bf16' else 'as stored'}), router reads "
                          f"{'z (latent)' if cfg.router_latent else 'x'}"
-                         f"{', standard MoE (experts in d)' if cfg.standard_moe else ''}", tokens_per_s=T / (ms * 1e-3),
+                         f"{', standard MoE (experts in d)' if cfg.standard_moe else ''}"
+                         f"{', FP8 projections' if cfg.proj_fp8 else ''}", tokens_per_s=T / (ms * 1e-3),
                 ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
                 hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
                 "1 GiB buffer read between steps (cache eviction)" % steps, kernels=kernels,
@@ -215,6 +218,7 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
                         f"{cfg.experts} experts, router reads {'z (latent)' if cfg.router_latent else 'x'}"
                         f"{', FP8 shared expert (E4M3 x E4M3 MFMA)' if cfg.shared_fp8 else ''}"
+                        f"{', FP8 down- and up-projections' if cfg.proj_fp8 else ''}"
                         f"{', standard MoE (experts in d, no latent projections)' if cfg.standard_moe else ''}",
                ms_per_step=ms, tokens_per_s=cfg.T / (ms * 1e-3),
                layer_tflops=cfg.flops / (ms * 1e-3) / 1e12, layer_mfma_frac=cfg.flops / (ms * 1e-3) / PEAK_BF16_FLOPS)
@@ -223,8 +227,12 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
         res["grouped"] = dict(kernel=gname, avg_launch_ms=g["avg_ms"], achieved_tflops=ach / 1e12,
                               mfma_frac=ach / PEAK_BF16_FLOPS)
     f8 = kernels.get("fp8_gemm")
-    if f8 and cfg.f_s > 0:  # the shared expert's two products, 2 T d f_s FLOPs each
-        ach = 2.0 * cfg.T * cfg.d * cfg.f_s / (f8["avg_ms"] * 1e-3)
+    # the fp8 products: the shared expert's two (2 T d f_s FLOPs each) and
+    # the two projections (2 T d l each)
+    f8_flops = (4.0 * cfg.T * cfg.d * cfg.f_s if cfg.shared_fp8 else 0.0) + \
+        (4.0 * cfg.T * cfg.d * cfg.l if cfg.proj_fp8 else 0.0)
+    if f8 and f8_flops > 0:
+        ach = f8_flops / (f8["ms_per_step"] * 1e-3)
         res["fp8_gemm"] = dict(avg_launch_ms=f8["avg_ms"], launches_per_step=f8["launches_per_step"],
                                achieved_tflops=ach / 1e12, mfma_frac_fp8=ach / PEAK_FP8_FLOPS)
     del inp, out
@@ -354,6 +362,7 @@ def main():
         extra = [C[n] for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload]
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_latent_router", router_latent=True))
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_shared", shared_fp8=True))
+        extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_proj_shared", shared_fp8=True, proj_fp8=True))
         # the standard MoE the overview compares against: 128 experts of d, top-6
         extra.append(C["prefill_bf16"].with_(name="prefill_standard_moe", l=C["prefill_bf16"].d, E=128, k=6,
                                              standard_moe=True))
@@ -362,6 +371,9 @@ def main():
         if not args.no_decode:
             result["other_workloads"]["decode_latent_router"] = decode(
                 C["decode_bf16_zipf"].with_(name="decode_latent_router", router_latent=True),
+                args.decode_steps, torch, B, synth, args.expert_layout)
+            result["other_workloads"]["decode_fp8_proj"] = decode(
+                C["decode_bf16_zipf"].with_(name="decode_fp8_proj", proj_fp8=True),
                 args.decode_steps, torch, B, synth, args.expert_layout)
             result["other_workloads"]["decode_standard_moe"] = decode(
                 C["decode_bf16_zipf"].with_(name="decode_standard_moe", l=C["decode_bf16_zipf"].d, E=128, k=6,

@@ -62,7 +62,7 @@ extern "C" {
 #define LMOE_BF16  1  /* bfloat16 */
 #define LMOE_NVFP4 2  /* routed-expert weights only, see lmoe_experts */
 #define LMOE_BF16_TILED 3  /* routed-expert bf16 weights in the tiled layout, see lmoe_pack_expert_weights */
-#define LMOE_FP8_E4M3 4    /* shared-expert weights only, see lmoe_shared */
+#define LMOE_FP8_E4M3 4    /* shared-expert and projection weights, see lmoe_shared, lmoe_fp8_matrix */
 
 /*
  * Layer sizes.  Constraints (LMOE_ERR_SHAPE otherwise):
@@ -88,6 +88,15 @@ extern "C" {
  *   (instead of d/4), routed experts W1 [E][f][d], W2 [E][d][f], z = x and
  *   out = c (+ shared expert); router_latent must be 0.  W_down and W_up are
  *   then ignored and may be NULL.  LMOE_ERR_SHAPE when violated.
+ * proj_dtype: the down- and up-projection weight format, the activation
+ *   dtype or, with bf16 activations and standard_moe = 0, LMOE_FP8_E4M3
+ *   (LMOE_ERR_DTYPE otherwise): then the W_down and W_up arguments each
+ *   point to an lmoe_fp8_matrix, l must be a multiple of 128
+ *   (LMOE_ERR_SHAPE), and each projection quantises its input per token as
+ *   lmoe_quantize_rows_fp8 does (x before W_down; the combined latent c, as
+ *   stored in bf16, before W_up) and runs as an fp8 x fp8 MFMA GEMM with
+ *   fp32 accumulation; z and out stay bf16.  The router and the expert FFNs
+ *   are unchanged.
  */
 typedef struct lmoe_dims {
     int64_t T, d, l, E, k, f, f_s;
@@ -96,7 +105,20 @@ typedef struct lmoe_dims {
     int32_t router_latent;
     int32_t shared_dtype;
     int32_t standard_moe;
+    int32_t proj_dtype;
 } lmoe_dims;
+
+/*
+ * An E4M3 weight matrix [rows][cols] with one scale per output row (weight
+ * = E4M3(code) * scale): codes [rows][cols] uint8 and scales [rows] fp32,
+ * both device memory, 16-byte aligned.  The struct itself is host memory,
+ * read during the call.  Used for W_down [l][d] and W_up [d][l] with
+ * dims.proj_dtype = LMOE_FP8_E4M3.
+ */
+typedef struct lmoe_fp8_matrix {
+    const uint8_t* codes;
+    const float* scales;
+} lmoe_fp8_matrix;
 
 /*
  * Routed-expert weights.  Dense formats (F32/BF16) use W1 [E][f][l] and
@@ -234,7 +256,8 @@ int lmoe_quantize_rows_fp8(int64_t rows, int64_t cols, const void* src, uint8_t*
 /*
  * The whole forward: out [T][d] = LatentMoE(x).  router_bias [E] fp32 may be
  * NULL (no bias); shared may be NULL (then dims.f_s must be 0); dbg may be
- * NULL.  workspace must hold lmoe_workspace_bytes(dims) bytes.  The result
+ * NULL.  W_down and W_up are device arrays in the activation dtype, or
+ * host pointers to lmoe_fp8_matrix with dims.proj_dtype = LMOE_FP8_E4M3.  workspace must hold lmoe_workspace_bytes(dims) bytes.  The result
  * equals running lmoe_project_route, lmoe_permute, lmoe_experts_ffn and
  * lmoe_combine_up in that order.
  */

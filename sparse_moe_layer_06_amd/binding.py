@@ -39,7 +39,13 @@ class Dims(ctypes.Structure):
                 ("E", ctypes.c_int64), ("k", ctypes.c_int64), ("f", ctypes.c_int64),
                 ("f_s", ctypes.c_int64), ("act_dtype", ctypes.c_int32),
                 ("expert_dtype", ctypes.c_int32), ("router_latent", ctypes.c_int32),
-                ("shared_dtype", ctypes.c_int32), ("standard_moe", ctypes.c_int32)]
+                ("shared_dtype", ctypes.c_int32), ("standard_moe", ctypes.c_int32),
+                ("proj_dtype", ctypes.c_int32)]
+
+
+class Fp8Matrix(ctypes.Structure):
+    """lmoe_fp8_matrix: E4M3 codes [rows][cols] and fp32 scales [rows] (device)."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 class Experts(ctypes.Structure):
@@ -126,7 +132,21 @@ def _check(status: int, what: str):
 def dims_of(cfg: LayerDims, T: Optional[int] = None) -> Dims:
     return Dims(T if T is not None else cfg.T, cfg.d, cfg.l, cfg.E, cfg.k, cfg.f, cfg.f_s,
                 DTYPE_CODE[cfg.act], DTYPE_CODE[cfg.experts], 1 if cfg.router_latent else 0,
-                DTYPE_CODE["fp8" if cfg.shared_fp8 else cfg.act], 1 if cfg.standard_moe else 0)
+                DTYPE_CODE["fp8" if cfg.shared_fp8 else cfg.act], 1 if cfg.standard_moe else 0,
+                DTYPE_CODE["fp8" if cfg.proj_fp8 else cfg.act])
+
+
+class _Proj:
+    """The W_down / W_up argument: the tensor's address, or with FP8
+    projections a pointer to an lmoe_fp8_matrix (kept alive here)."""
+
+    def __init__(self, cfg: LayerDims, inp, name: str):
+        self.m = None
+        if cfg.proj_fp8:
+            self.m = Fp8Matrix(_p(inp[name]), _p(inp[name + "_scale"]))
+            self.arg = ctypes.cast(ctypes.pointer(self.m), ctypes.c_void_p)
+        else:
+            self.arg = _p(inp.get(name))
 
 
 def _p(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -222,8 +242,9 @@ class Call:
         self.dbg = None
         if debug:
             self.dbg = Debug(**{n: _p(debug.get(n)) for n, _ in Debug._fields_})
-        self.args = (ctypes.byref(self.dims), _p(inp["x"]), _p(inp["W_down"]), _p(inp["W_r"]),
-                     _p(inp.get("b_r")), ctypes.byref(self.ex), _p(inp["W_up"]), _byref_opt(self.sh),
+        self.wd, self.wu = _Proj(cfg, inp, "W_down"), _Proj(cfg, inp, "W_up")
+        self.args = (ctypes.byref(self.dims), _p(inp["x"]), self.wd.arg, _p(inp["W_r"]),
+                     _p(inp.get("b_r")), ctypes.byref(self.ex), self.wu.arg, _byref_opt(self.sh),
                      cfg.k, _p(out), _p(workspace), workspace.numel(), _byref_opt(self.dbg),
                      _stream(stream))
         self._keep = (inp, out, workspace, debug)
@@ -283,7 +304,8 @@ def project_route(cfg: LayerDims, inp, workspace, stream=None):
     sh = shared_struct(inp)
     hs = torch.empty((T, cfg.f_s), dtype=dt, device=dev) if sh is not None else None
     d = dims_of(cfg, T)
-    _check(lib().lmoe_project_route(ctypes.byref(d), _p(x), _p(inp["W_down"]), _p(inp["W_r"]),
+    wd = _Proj(cfg, inp, "W_down")
+    _check(lib().lmoe_project_route(ctypes.byref(d), _p(x), wd.arg, _p(inp["W_r"]),
                                     _p(inp.get("b_r")), _byref_opt(sh), _p(z), _p(logits), _p(idx),
                                     _p(gate), _p(hs), _p(workspace), workspace.numel(),
                                     _stream(stream)), "lmoe_project_route")
@@ -321,7 +343,8 @@ def combine_up(cfg: LayerDims, inp, Y, inv, gate, hs, workspace, T: int, stream=
     out = torch.empty((T, cfg.d), dtype=dt, device=dev)
     sh = shared_struct(inp)
     d = dims_of(cfg, T)
-    _check(lib().lmoe_combine_up(ctypes.byref(d), _p(Y), _p(inv), _p(gate), _p(inp["W_up"]), _byref_opt(sh),
+    wu = _Proj(cfg, inp, "W_up")
+    _check(lib().lmoe_combine_up(ctypes.byref(d), _p(Y), _p(inv), _p(gate), wu.arg, _byref_opt(sh),
                                  _p(hs), _p(c), _p(out), _p(workspace), workspace.numel(),
                                  _stream(stream)), "lmoe_combine_up")
     return dict(c=c, out=out)

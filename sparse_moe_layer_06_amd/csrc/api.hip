@@ -11,6 +11,8 @@
 //   5. grouped GEMM  Y = H W2_e^T
 //   6. combine       c_t = sum_j gate_tj Y[inv(t, j)]
 //   7. dense GEMM    out = [c | hs] [W_up | W_s2]^T
+// With FP8 weights the shared expert's products and the projections run as
+// fp8 GEMMs of their own, each after a per-token quantisation of its input.
 #include <string.h>
 
 #include "lmoe_internal.hpp"
@@ -52,14 +54,20 @@ static int64_t max_tiles(const lmoe_dims& d) {
 // the last).
 static bool shared_fp8(const lmoe_dims& d) { return d.f_s > 0 && d.shared_dtype == LMOE_FP8_E4M3; }
 static bool shared_dense(const lmoe_dims& d) { return d.f_s > 0 && d.shared_dtype != LMOE_FP8_E4M3; }
+// FP8 down- and up-projections: fp8 GEMMs of their own, like the shared expert's.
+static bool proj_fp8(const lmoe_dims& d) { return d.proj_dtype == LMOE_FP8_E4M3; }
+// Whether the last dense GEMM only adds the shared expert to an out that
+// already holds the routed result (standard MoE, or an fp8 up-projection).
+static bool out_add_only(const lmoe_dims& d) { return d.standard_moe || proj_fp8(d); }
 
 // x [W_down; W_r; W_s1]^T -> z, logits (+ bias), hs (the shared expert's
 // hidden layer, only with f_s > 0 in the activation dtype).  With a latent
-// router the logits are left to gemm_router.
+// router the logits are left to gemm_router; with FP8 projections z is left
+// to the fp8 GEMM.  N may be 0 (nothing left for this GEMM).
 static DenseGemm gemm_in(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r, const float* bias,
                          const void* W_s1, void* z, float* logits, void* hs) {
     DenseGemm g{};
-    const int L = d.standard_moe ? 0 : (int)d.l;        // latent columns (none: z is x)
+    const int L = (d.standard_moe || proj_fp8(d)) ? 0 : (int)d.l;  // latent columns here
     const int E = d.router_latent ? 0 : (int)d.E;       // router columns in this GEMM
     const int fs = shared_dense(d) ? (int)d.f_s : 0;
     g.M = (int)d.T;
@@ -89,12 +97,12 @@ static DenseGemm gemm_router(const lmoe_dims& d, const void* z, const void* W_r,
     return g;
 }
 
-// [c | hs] [W_up | W_s2]^T -> out.  Standard MoE: out (holding c already)
-// += hs W_s2^T.
+// [c | hs] [W_up | W_s2]^T -> out.  Standard MoE or FP8 up-projection: out
+// (holding the routed result already) += hs W_s2^T.
 static DenseGemm gemm_out(const lmoe_dims& d, const void* c, const void* hs, const void* W_up, const void* W_s2,
                           void* out) {
     DenseGemm g{};
-    if (d.standard_moe) {
+    if (out_add_only(d)) {
         g.M = (int)d.T;
         g.N = (int)d.d;
         g.nseg = 1;
@@ -124,7 +132,7 @@ static DenseGemm gemm_out(const lmoe_dims& d, const void* c, const void* hs, con
 
 struct Layout {
     size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
-        c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, q_x, s_x, q_h, s_h, total;
+        c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, q_x, s_x, q_h, s_h, q_c, s_c, total;
 };
 
 // Whether the few-rows expert GEMMs may take the split-K 64 x 256 tiles
@@ -169,9 +177,9 @@ static Layout plan(const lmoe_dims& d) {
     if (d.act_dtype == LMOE_BF16 && d.T <= 64) {
         L.splitk_bytes = 16 * (size_t)d.T * widest * 4;
     } else if (d.act_dtype == LMOE_BF16) {
-        const size_t a = dense_tail_split_bytes(gemm_in(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                                        nullptr, nullptr));
-        const size_t b = (!d.standard_moe || shared_dense(d))
+        const DenseGemm gi = gemm_in(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+        const size_t a = gi.N > 0 ? dense_tail_split_bytes(gi) : 0;
+        const size_t b = (!out_add_only(d) || shared_dense(d))
                              ? dense_tail_split_bytes(gemm_out(d, nullptr, nullptr, nullptr, nullptr, nullptr))
                              : 0;
         const size_t r = d.router_latent ? dense_tail_split_bytes(gemm_router(d, nullptr, nullptr, nullptr, nullptr))
@@ -180,11 +188,17 @@ static Layout plan(const lmoe_dims& d) {
         if (r > L.splitk_bytes) L.splitk_bytes = r;
     }
     L.splitk = take(L.splitk_bytes);
-    if (shared_fp8(d)) {  // E4M3 codes and per-token scales of x and hs
+    if (shared_fp8(d) || proj_fp8(d)) {  // E4M3 codes and per-token scales of x
         L.q_x = take((size_t)d.T * d.d);
         L.s_x = take((size_t)d.T * 4);
+    }
+    if (shared_fp8(d)) {  // ... of hs
         L.q_h = take((size_t)d.T * d.f_s);
         L.s_h = take((size_t)d.T * 4);
+    }
+    if (proj_fp8(d)) {  // ... of c
+        L.q_c = take((size_t)d.T * d.l);
+        L.s_c = take((size_t)d.T * 4);
     }
     if (expert_split_k(d)) {
         const int64_t widest_n = d.f > d.l ? d.f : d.l;
@@ -229,6 +243,15 @@ static int check_experts(const lmoe_dims& d, const lmoe_experts* x) {
     return check_ptrs({x->W1, x->W2});
 }
 
+// W_down or W_up as passed: a device array, or with FP8 projections a host
+// lmoe_fp8_matrix naming the codes and the per-row scales.
+static int check_proj(const lmoe_dims& d, const void* W) {
+    if (!proj_fp8(d)) return check_ptrs({W});
+    if (!W) return LMOE_ERR_NULL;
+    const lmoe_fp8_matrix* m = (const lmoe_fp8_matrix*)W;
+    return check_ptrs({m->codes, m->scales});
+}
+
 static int check_shared(const lmoe_dims& d, const lmoe_shared* sh) {
     if ((sh != nullptr) != (d.f_s > 0)) return LMOE_ERR_SHAPE;
     if (sh && shared_fp8(d)) return check_ptrs({sh->W_s1, sh->W_s2, sh->W_s1_scale, sh->W_s2_scale});
@@ -262,18 +285,28 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
                                     int32_t* idx, float* gate, void* hs, char* ws, const Layout& L,
                                     hipStream_t s) {
     const DenseGemm g = gemm_in(d, x, W_down, W_r, bias, sh ? sh->W_s1 : nullptr, z, logits, hs);
-    hipError_t e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
+    hipError_t e = hipSuccess;
+    if (g.N > 0) e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
     if (e != hipSuccess) return e;
+    uint8_t* qx = (uint8_t*)(ws + L.q_x);
+    float* sx = (float*)(ws + L.s_x);
+    if (shared_fp8(d) || proj_fp8(d)) {
+        e = launch_quantize_rows_fp8((const uint16_t*)x, d.T, (int)d.d, d.d, qx, sx, s);
+        if (e != hipSuccess) return e;
+    }
+    if (proj_fp8(d)) {  // z = s_x * (q_x W_down^T) * s_down
+        const lmoe_fp8_matrix* W = (const lmoe_fp8_matrix*)W_down;
+        e = launch_fp8_gemm(Fp8Gemm{(int)d.T, (int)d.l, (int)d.d, qx, d.d, sx, W->codes, d.d, W->scales, EPI_STORE,
+                                    (uint16_t*)z, d.l},
+                            ws + L.splitk, L.splitk_bytes, s);
+        if (e != hipSuccess) return e;
+    }
     if (d.router_latent) {
         e = launch_dense_gemm(gemm_router(d, z, W_r, bias, logits), d.act_dtype, (int)d.T, ws + L.splitk,
                               L.splitk_bytes, s);
         if (e != hipSuccess) return e;
     }
     if (shared_fp8(d)) {  // hs = relu(s_x * (q_x W_s1^T) * s_w1)^2
-        uint8_t* qx = (uint8_t*)(ws + L.q_x);
-        float* sx = (float*)(ws + L.s_x);
-        e = launch_quantize_rows_fp8((const uint16_t*)x, d.T, (int)d.d, d.d, qx, sx, s);
-        if (e != hipSuccess) return e;
         Fp8Gemm f{};
         f.M = (int)d.T;
         f.N = (int)d.f_s;
@@ -287,7 +320,7 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
         f.epi = EPI_RELU2;
         f.C = (uint16_t*)hs;
         f.ldc = d.f_s;
-        e = launch_fp8_gemm(f, s);
+        e = launch_fp8_gemm(f, ws + L.splitk, L.splitk_bytes, s);
         if (e != hipSuccess) return e;
     }
     return launch_topk_softmax(logits, (int)d.T, (int)d.E, (int)d.k, idx, gate, s);
@@ -346,7 +379,18 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
         e = hipMemcpyAsync(c_opt, out, (size_t)d.T * d.l * es, hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return e;
     }
-    if (!d.standard_moe || shared_dense(d)) {
+    if (proj_fp8(d)) {  // out = s_c * (q_c W_up^T) * s_up, from c as stored
+        uint8_t* qc = (uint8_t*)(ws + L.q_c);
+        float* sc = (float*)(ws + L.s_c);
+        e = launch_quantize_rows_fp8((const uint16_t*)c, d.T, (int)d.l, d.l, qc, sc, s);
+        if (e != hipSuccess) return e;
+        const lmoe_fp8_matrix* W = (const lmoe_fp8_matrix*)W_up;
+        e = launch_fp8_gemm(Fp8Gemm{(int)d.T, (int)d.d, (int)d.l, qc, d.l, sc, W->codes, d.l, W->scales, EPI_STORE,
+                                    (uint16_t*)out, d.d},
+                            ws + L.splitk, L.splitk_bytes, s);
+        if (e != hipSuccess) return e;
+    }
+    if (!out_add_only(d) || shared_dense(d)) {
         const DenseGemm g = gemm_out(d, c, hs, W_up, sh ? sh->W_s2 : nullptr, out);
         e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
     }
@@ -369,7 +413,7 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
     f.epi = EPI_ADD;
     f.C = (uint16_t*)out;
     f.ldc = d.d;
-    return launch_fp8_gemm(f, s);
+    return launch_fp8_gemm(f, ws + L.splitk, L.splitk_bytes, s);
 }
 
 }  // namespace lmoe
@@ -402,6 +446,10 @@ int lmoe_validate_dims(const lmoe_dims* d) {
     if (d->shared_dtype != d->act_dtype && !(d->act_dtype == LMOE_BF16 && d->shared_dtype == LMOE_FP8_E4M3))
         return LMOE_ERR_DTYPE;
     if (d->shared_dtype == LMOE_FP8_E4M3 && d->f_s % 128 != 0) return LMOE_ERR_SHAPE;  // fp8 K step
+    if (d->proj_dtype != d->act_dtype &&
+        !(d->act_dtype == LMOE_BF16 && d->proj_dtype == LMOE_FP8_E4M3 && d->standard_moe == 0))
+        return LMOE_ERR_DTYPE;
+    if (d->proj_dtype == LMOE_FP8_E4M3 && d->l % 128 != 0) return LMOE_ERR_SHAPE;  // fp8 K step of W_up
     return LMOE_OK;
 }
 
@@ -452,7 +500,10 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, 
     const lmoe_dims& d = *dims;
     if (k != d.k) return LMOE_ERR_SHAPE;
     LMOE_TRY(check_ptrs({x, W_router, out}));
-    if (!d.standard_moe) LMOE_TRY(check_ptrs({W_down, W_up}));
+    if (!d.standard_moe) {
+        LMOE_TRY(check_proj(d, W_down));
+        LMOE_TRY(check_proj(d, W_up));
+    }
     LMOE_TRY(check_optional(router_bias));
     LMOE_TRY(check_experts(d, experts));
     LMOE_TRY(check_shared(d, shared));
@@ -500,7 +551,10 @@ int lmoe_project_route(const lmoe_dims* dims, const void* x, const void* W_down,
     LMOE_TRY(lmoe_validate_dims(dims));
     const lmoe_dims& d = *dims;
     LMOE_TRY(check_ptrs({x, W_router, logits, topk_idx, topk_gate}));
-    if (!d.standard_moe) LMOE_TRY(check_ptrs({W_down, z}));  // a standard MoE has no z of its own
+    if (!d.standard_moe) {  // a standard MoE has no z of its own
+        LMOE_TRY(check_ptrs({z}));
+        LMOE_TRY(check_proj(d, W_down));
+    }
     LMOE_TRY(check_optional(router_bias));
     LMOE_TRY(check_shared(d, shared));
     if (shared) LMOE_TRY(check_ptrs({hs}));
@@ -544,7 +598,7 @@ int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv, co
     LMOE_TRY(lmoe_validate_dims(dims));
     const lmoe_dims& d = *dims;
     LMOE_TRY(check_ptrs({Y, inv, topk_gate, out}));
-    if (!d.standard_moe) LMOE_TRY(check_ptrs({W_up}));
+    if (!d.standard_moe) LMOE_TRY(check_proj(d, W_up));
     LMOE_TRY(check_shared(d, shared));
     if (shared) LMOE_TRY(check_ptrs({hs}));
     LMOE_TRY(check_optional(c));

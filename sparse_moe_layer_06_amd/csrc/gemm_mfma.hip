@@ -957,16 +957,24 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 // K step is 128 codes = 128 bytes = 8 chunks of 16 B, as 64 bf16 values
 // are.  Each K step runs two 32x32x64 fp8 MFMAs per 32x32 block, twice the
 // K of the bf16 step for the same bytes and the same MFMA issue time.
+// With splits > 1 (few-row calls) block (tile, split) takes the K steps
+// [split * nk / splits, (split + 1) * nk / splits) and stores its scaled
+// fp32 partial tile to partial[split][M][ldp]; splitk_reduce_kernel adds the
+// splits in order and applies the epilogue.
 template <class C>
-__global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int tiles_m, int tiles_n, int group_m) {
+__global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int tiles_m, int tiles_n, int group_m,
+                                                                  int splits, float* partial, int ldp) {
     static_assert(C::DMA && C::CPR == 8, "fp8 tiles: LDS-DMA, 128-byte K step");
     __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
-    const int w = xcd_work_index(blockIdx.x, tiles_m * tiles_n);
-    if (w < 0) return;
+    const int ws_ = xcd_work_index(blockIdx.x, tiles_m * tiles_n * splits);
+    if (ws_ < 0) return;
+    const int split = ws_ % splits, w = ws_ / splits;
+    const int nk = g.K / 128;
+    const int kb = split * nk / splits, ke = (split + 1) * nk / splits;
     const int width = group_m * tiles_n;
     const int first_m = (w / width) * group_m;
     const int gsz = min(tiles_m - first_m, group_m);
@@ -985,7 +993,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
         b_ptr[j] = g.B + (int64_t)min(n0 + SB::row(j, tid), g.N - 1) * g.ldb + SB::lchunk(j, tid) * 16;
 
     auto fill = [&](int kt, u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
-        const int kk = kt * 128;
+        const int kk = (kb + kt) * 128;
 #pragma unroll
         for (int j = 0; j < SA::N; ++j)
             if (SA::active(j, tid)) dma16(a_ptr[j] + kk, SA::dst(As, wave, j));
@@ -997,7 +1005,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
 
     f32x16_t acc[C::TM][C::TN];
     zero_acc<C>(acc);
-    kloop<C, SA::N + SB::N, true>(g.K / 128, fill, land, ring, acc, wm, wn, lane);
+    kloop<C, SA::N + SB::N, true>(ke - kb, fill, land, ring, acc, wm, wn, lane);
 
     static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
         constexpr int tm = decltype(tmc)::value;
@@ -1012,6 +1020,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
                     const float4 sb = *reinterpret_cast<const float4*>(g.b_scale + n);
                     float v[4] = {acc[tm][tn][q * 4 + 0] * sa * sb.x, acc[tm][tn][q * 4 + 1] * sa * sb.y,
                                   acc[tm][tn][q * 4 + 2] * sa * sb.z, acc[tm][tn][q * 4 + 3] * sa * sb.w};
+                    if (partial) {  // ldp is a multiple of 4: one aligned float4
+                        *reinterpret_cast<float4*>(partial + ((int64_t)split * g.M + m) * ldp + n) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                        return;
+                    }
                     uint2* dst = reinterpret_cast<uint2*>(crow + n);
                     if (g.epi == EPI_ADD) {
                         const uint2 old = *dst;
@@ -1019,7 +1032,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
                         v[1] += bf16_to_f32((uint16_t)(old.x >> 16));
                         v[2] += bf16_to_f32((uint16_t)(old.y & 0xFFFFu));
                         v[3] += bf16_to_f32((uint16_t)(old.y >> 16));
-                    } else {
+                    } else if (g.epi == EPI_RELU2) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.f) * fmaxf(v[i], 0.f);
                     }
@@ -1300,16 +1313,33 @@ hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t sp
 // FP8 shared expert: 256x256 tiles (64x64 for decode-sized M), one tile per
 // block; N and K are the shared expert's (multiples of 64 and 128).
 template <class C>
-static hipError_t run_fp8(const Fp8Gemm& g, hipStream_t s) {
+static hipError_t run_fp8(const Fp8Gemm& g, void* ws, size_t ws_bytes, hipStream_t s) {
     const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
-    LMOE_LAUNCH("fp8_gemm", s, fp8_gemm_kernel<C><<<tiles_m * tiles_n, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8));
+    const int ldp = (g.N + 3) / 4 * 4;
+    const int splits = splitk_factor(tiles_m * tiles_n, g.K / 128, g.M, ldp, ws_bytes, C::MINB);
+    float* partial = splits > 1 ? (float*)ws : nullptr;
+    LMOE_LAUNCH("fp8_gemm", s,
+                fp8_gemm_kernel<C><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
+                                                                               partial, ldp));
+    if (splits > 1) {  // the reduction's epilogue: one column group writing g.C
+        DenseGemm r{};
+        r.M = g.M;
+        r.N = g.N;
+        r.ngroups = 1;
+        r.g[0] = NGroup{0, g.N, {nullptr, nullptr}, g.epi, g.C, g.ldc, nullptr};
+        const int64_t threads = (int64_t)g.M * (ldp / 4);
+        LMOE_LAUNCH("splitk_reduce", s,
+                    splitk_reduce_kernel<<<(int)((threads + 255) / 256), 256, 0, s>>>(r, splits, partial, ldp));
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_fp8_gemm(const Fp8Gemm& g, hipStream_t s) {
+hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s) {
     if (g.K % 128 != 0 || g.N % 16 != 0) return hipErrorInvalidValue;
-    if (g.M <= 64) return run_fp8<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, s);
-    return run_fp8<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, s);
+    if (g.epi != EPI_STORE && g.epi != EPI_RELU2 && g.epi != EPI_ADD) return hipErrorInvalidValue;
+    if (g.M <= 64)  // weight streaming: split-K over the partial-sum workspace
+        return run_fp8<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, splitk_ws, splitk_bytes, s);
+    return run_fp8<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
 }
 
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to

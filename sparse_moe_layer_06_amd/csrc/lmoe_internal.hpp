@@ -91,8 +91,9 @@ struct GroupedGemm {
 
 // FP8 (E4M3 x E4M3) GEMM with per-row scales, fp32 accumulate:
 // C[m][n] = epi(a_scale[m] * b_scale[n] * sum_k A[m][k] * B[n][k]), epi
-// EPI_RELU2 (store bf16) or EPI_ADD.  K is a multiple of 128; N, lda,
-// ldb and ldc are multiples of 16.
+// EPI_STORE, EPI_RELU2 (both store bf16) or EPI_ADD.  K is a multiple of
+// 128; N, lda, ldb and ldc are multiples of 16.  Calls with M <= 64 split K
+// over the given fp32 partial-sum workspace when it has room.
 struct Fp8Gemm {
     int M, N, K;
     const uint8_t* A;
@@ -105,7 +106,7 @@ struct Fp8Gemm {
     uint16_t* C;
     int64_t ldc;
 };
-hipError_t launch_fp8_gemm(const Fp8Gemm& g, hipStream_t s);
+hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s);
 
 // Per-row FP8 quantisation of a bf16 matrix [rows][cols] (row stride ld):
 // scale = max |v| / 448 (1 for an all-zero row), code = E4M3(v / scale),

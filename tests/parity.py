@@ -17,6 +17,10 @@
   max-norm relative error (max |gpu - ref| / max |ref|) against the
   tolerance of the activation format: 1e-5 fp32, 2e-2 bf16, 3e-2 NVFP4
   experts (the oracle decodes the same NVFP4 bytes).
+* FP8 up-projection: out is checked twice.  Step-wise, against the oracle's
+  fp8 up-projection of the GPU's stored c (the same codes, so only the
+  summation differs) within the activation tolerance; end to end, against
+  the oracle from x within FP8_PROJ_OUT_TOL (see there).
 """
 from __future__ import annotations
 
@@ -42,6 +46,21 @@ LOGIT_TOL_LATENT_BF16 = 1e-3
 GAP_TOL_LATENT_BF16 = 2e-3
 GATE_TOL = 1e-5
 GATE_TOL_LATENT_BF16 = 2e-3
+
+
+# The fp8 up-projection quantises c per token to E4M3 (3 mantissa bits: a
+# step of 1/8 to 1/16 of the value).  The GPU's c carries the bf16 roundings
+# of H and Y that the float64 oracle's c does not (0.3-0.6% of c's max-norm
+# on the fp8 cases here), so the two sides quantise slightly different values
+# and about one code in ten lands on the neighbouring E4M3 value (9.5-10.2%
+# measured).  Each such code moves an output by one step, about 0.09 |c_i
+# W_ni|: over l terms with random signs that is sqrt(0.1 l) * 0.09 |c_i W_ni|
+# against an rms output of sqrt(l) |c_i W_ni|, 2.8% of the rms, and the
+# largest of T d such errors is about 4 of those against a max-norm of about
+# 3.5 rms: 3.2% (measured: 0.7-2.5%).  So end to end the bound is 5e-2,
+# while the step-wise check above (identical codes; measured 0.3%) holds the
+# up-projection itself to the activation bound.
+FP8_PROJ_OUT_TOL = 5e-2
 
 
 def latent_bf16(cfg) -> bool:
@@ -202,10 +221,23 @@ def run_and_check(cfg, inp, n_sample: int = 1 << 30, lazy_experts: bool = False,
     errs["z"] = 0.0 if cfg.standard_moe else rel_err(to_f64(dbg["z"][tokens]), ref["z"])
     errs["c"] = rel_err(to_f64(dbg["c"][tokens]), ref["c"])
     errs["out"] = rel_err(to_f64(out[tokens]), ref["out"])
+    if cfg.proj_fp8:  # step-wise: the oracle's fp8 up-projection of the GPU's c as stored
+        step = O.project(to_f64(dbg["c"][tokens]), h, "W_up")
+        if h.get("W_s1") is not None:
+            step = step + O.shared_expert(h["x"][tokens], h)
+        errs["out_from_gpu_c"] = rel_err(to_f64(out[tokens]), step)
+        # share of c's E4M3 codes that differ between the two sides (reported)
+        qg, _ = O.quantize_rows_fp8(to_f64(dbg["c"][tokens]))
+        qo, _ = O.quantize_rows_fp8(O.round_to_bf16(ref["c"]))
+        errs["c_code_flips"] = float(np.mean(qg != qo))
     errs["tokens_checked"] = int(len(tokens))
     if report is not None:
         report(errs)
     assert errs["z"] <= zt, errs
     assert errs["c"] <= tol, errs
-    assert errs["out"] <= tol, errs
+    if cfg.proj_fp8:
+        assert errs["out_from_gpu_c"] <= tol, errs
+        assert errs["out"] <= FP8_PROJ_OUT_TOL, errs
+    else:
+        assert errs["out"] <= tol, errs
     return errs, out, dbg

@@ -68,6 +68,8 @@ def test_validate_accepts_every_workload():
     ("shared_dtype", 7, B.LMOE_ERR_DTYPE),
     ("shared_dtype", B.LMOE_F32, B.LMOE_ERR_DTYPE),  # fp32 shared weights with bf16 activations
     ("router_latent", 2, B.LMOE_ERR_SHAPE),
+    ("proj_dtype", 7, B.LMOE_ERR_DTYPE),
+    ("proj_dtype", B.LMOE_F32, B.LMOE_ERR_DTYPE),  # fp32 projections with bf16 activations
 ])
 def test_validate_rejects(field, value, code):
     d = dims()
@@ -184,6 +186,40 @@ def test_fp8_shared_rules():
     assert _forward(d, shared=B.Shared(FAKE, FAKE, FAKE, MIS)) == B.LMOE_ERR_ALIGN
     assert _forward(d, shared=B.Shared(FAKE, FAKE, FAKE, FAKE)) == B.LMOE_ERR_WORKSPACE
     assert B.lib().lmoe_workspace_bytes(ctypes.byref(d)) > B.lib().lmoe_workspace_bytes(ctypes.byref(dims()))
+
+
+def test_fp8_projection_rules():
+    d = dims(proj_fp8=True)  # bf16 activations, l = 1024
+    assert B.validate_dims(d) == B.LMOE_OK
+    f = B.dims_of(synth.CONFIGS["tiny_f32"])
+    f.proj_dtype = B.LMOE_FP8_E4M3  # fp8 projections need bf16 activations
+    assert B.validate_dims(f) == B.LMOE_ERR_DTYPE
+    std = dims(standard_moe=True, l=4096, proj_fp8=True)  # a standard MoE has no projections
+    assert B.validate_dims(std) == B.LMOE_ERR_DTYPE
+    assert B.validate_dims(dims(d=512, l=128, proj_fp8=True)) == B.LMOE_OK
+    assert B.validate_dims(dims(d=256, l=64, proj_fp8=True)) == B.LMOE_ERR_SHAPE  # fp8 K step of W_up
+
+    def mat(codes, scales):  # host lmoe_fp8_matrix naming device arrays
+        m = B.Fp8Matrix(codes, scales)
+        return m, ctypes.cast(ctypes.pointer(m), ctypes.c_void_p)
+
+    good, pg = mat(FAKE, FAKE)
+    no_scales, pn = mat(FAKE, None)
+    mis, pm = mat(MIS, FAKE)
+    assert _forward(d, W_down=pg, W_up=pg) == B.LMOE_ERR_WORKSPACE
+    assert _forward(d, W_down=None, W_up=pg) == B.LMOE_ERR_NULL
+    assert _forward(d, W_down=pg, W_up=pn) == B.LMOE_ERR_NULL
+    assert _forward(d, W_down=pm, W_up=pg) == B.LMOE_ERR_ALIGN
+    L = B.lib()
+    assert L.lmoe_workspace_bytes(ctypes.byref(d)) > L.lmoe_workspace_bytes(ctypes.byref(dims()))
+    need = L.lmoe_workspace_bytes(ctypes.byref(d))
+    sh = B.Shared(FAKE, FAKE)
+    assert L.lmoe_project_route(ctypes.byref(d), FAKE, pn, FAKE, None, ctypes.byref(sh), FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, need - 1, None) == B.LMOE_ERR_NULL
+    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, pm, ctypes.byref(sh), FAKE, None, FAKE, FAKE,
+                             need - 1, None) == B.LMOE_ERR_ALIGN
+    assert L.lmoe_combine_up(ctypes.byref(d), FAKE, FAKE, FAKE, pg, ctypes.byref(sh), FAKE, None, FAKE, FAKE,
+                             need - 1, None) == B.LMOE_ERR_WORKSPACE
 
 
 def test_quantize_rows_error_paths():

@@ -70,6 +70,16 @@ SMALL = {
     "standard_fp8_zipf": TINY.with_(name="standard_fp8_zipf", T=24, d=512, l=512, E=32, k=6, f=256, f_s=256,
                                     act="bf16", experts="bf16", shared_fp8=True, zipf_bias=True,
                                     standard_moe=True),
+    # FP8 down- and up-projections (E4M3 weights, per-token E4M3 inputs):
+    # many rows (256x256 fp8 tiles) with a bf16 shared expert added after
+    # the fp8 up-projection; few rows (split-K fp8 GEMMs) with everything
+    # else fp8 too; skewed routing without a shared expert
+    "fp8_proj": TINY.with_(name="fp8_proj", T=150, d=512, l=128, E=16, k=3, f=192, f_s=128,
+                           act="bf16", experts="bf16", proj_fp8=True),
+    "fp8_proj_few": TINY.with_(name="fp8_proj_few", T=20, d=1024, l=256, E=8, k=2, f=128, f_s=256,
+                               act="bf16", experts="nvfp4", proj_fp8=True, shared_fp8=True, router_latent=True),
+    "fp8_proj_zipf": TINY.with_(name="fp8_proj_zipf", T=64, d=2048, l=512, E=64, k=6, f=256, f_s=0,
+                                act="bf16", experts="bf16", proj_fp8=True, zipf_bias=True),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
@@ -134,7 +144,7 @@ def test_exact_logit_ties_break_to_lower_id():
 
 def test_staged_entry_points_compose_to_forward():
     for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide", "latent_bf16", "fp8_shared",
-                 "standard_bf16"):
+                 "standard_bf16", "fp8_proj", "fp8_proj_few"):
         cfg = SMALL[name]
         log(f"case staged {name}")
         inp = small_inputs(cfg)
@@ -320,3 +330,21 @@ def test_prefill_nvfp4_full_size():
     log(f"case {cfg}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     P.run_and_check(cfg, inp, n_sample=16, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_decode_fp8_projections_full_size():
+    # split-K fp8 GEMMs for both projections at d = 8192, 64 tokens
+    cfg = CFG["decode_bf16_zipf"].with_(name="decode_fp8_proj", proj_fp8=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    errs, _, dbg = P.run_and_check(cfg, inp, lazy_experts=True, report=log)
+    assert int(dbg["counts"].cpu()[0]) == cfg.T
+
+
+@pytest.mark.timeout(900)
+def test_prefill_fp8_projections_sampled():
+    cfg = CFG["prefill_bf16"].with_(name="prefill_fp8_proj", T=2048, proj_fp8=True, shared_fp8=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=12, lazy_experts=True, report=log)
