@@ -1046,6 +1046,22 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
     });
 }
 
+// E4M3 codes of 8 consecutive values v[0..7] / scale (two packed words).
+__device__ __forceinline__ uint2 fp8_codes8(const u32x4_t& v, float scale) {
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float a = bf16_to_f32((uint16_t)(v[2 * h] & 0xFFFFu)) / scale;
+        const float b = bf16_to_f32((uint16_t)(v[2 * h] >> 16)) / scale;
+        const float cc = bf16_to_f32((uint16_t)(v[2 * h + 1] & 0xFFFFu)) / scale;
+        const float d = bf16_to_f32((uint16_t)(v[2 * h + 1] >> 16)) / scale;
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(cc, d, p, true);
+        w[h] = (uint32_t)p;
+    }
+    return make_uint2(w[0], w[1]);
+}
+
 // One wave per row: the row's max |v| (a first pass), then the codes (a
 // second pass over the same 16-byte chunks, mostly cache hits).
 __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* __restrict__ src, int64_t rows,
@@ -1067,27 +1083,51 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const uint16_t* 
     amax = wave_max(amax);
     const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
     uint8_t* out = codes + r * (int64_t)cols;
-    for (int c = lane * 8; c < cols; c += 512) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c);
-        uint32_t w[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float a = bf16_to_f32((uint16_t)(v[2 * h] & 0xFFFFu)) / scale;
-            const float b = bf16_to_f32((uint16_t)(v[2 * h] >> 16)) / scale;
-            const float cc = bf16_to_f32((uint16_t)(v[2 * h + 1] & 0xFFFFu)) / scale;
-            const float d = bf16_to_f32((uint16_t)(v[2 * h + 1] >> 16)) / scale;
-            int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(cc, d, p, true);
-            w[h] = (uint32_t)p;
-        }
-        *reinterpret_cast<uint2*>(out + c) = make_uint2(w[0], w[1]);
-    }
+    for (int c = lane * 8; c < cols; c += 512)
+        *reinterpret_cast<uint2*>(out + c) = fp8_codes8(*reinterpret_cast<const u32x4_t*>(row + c), scale);
     if (lane == 0) scales[r] = scale;
+}
+
+// Few rows (decode-sized calls): one 256-thread block per row, so a row's
+// loads are spread over four waves instead of queued on one.  The same
+// scale and codes as quantize_rows_fp8_kernel.
+__global__ __launch_bounds__(256) void quantize_row_fp8_block_kernel(const uint16_t* __restrict__ src, int cols,
+                                                                     int64_t ld, uint8_t* __restrict__ codes,
+                                                                     float* __restrict__ scales) {
+    __shared__ float part[4];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t* row = src + r * ld;
+    float amax = 0.f;
+#pragma unroll 4
+    for (int c = tid * 8; c < cols; c += 2048) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[i] & 0xFFFFu))));
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[i] >> 16))));
+        }
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) part[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    uint8_t* out = codes + r * (int64_t)cols;
+#pragma unroll 4
+    for (int c = tid * 8; c < cols; c += 2048)
+        *reinterpret_cast<uint2*>(out + c) = fp8_codes8(*reinterpret_cast<const u32x4_t*>(row + c), scale);
+    if (tid == 0) scales[r] = scale;
 }
 
 hipError_t launch_quantize_rows_fp8(const uint16_t* src, int64_t rows, int cols, int64_t ld, uint8_t* codes,
                                     float* scales, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
+    if (rows <= 1024) {
+        LMOE_LAUNCH("quantize_fp8", s,
+                    quantize_row_fp8_block_kernel<<<(unsigned)rows, 256, 0, s>>>(src, cols, ld, codes, scales));
+        return hipGetLastError();
+    }
     const int64_t blocks = (rows + 3) / 4;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     LMOE_LAUNCH("quantize_fp8", s,

@@ -222,12 +222,14 @@ def test_tiled_expert_weights(name):
     P.run_and_check(cfg_t, inp, gpu_inp=inp_t, report=log)
 
 
-def test_quantize_rows_fp8_matches_oracle():
-    # rows of very different magnitudes, an all-zero row, and a ragged width
+@pytest.mark.parametrize("rows,cols", [(37, 1000), (1100, 264), (64, 8192)])
+def test_quantize_rows_fp8_matches_oracle(rows, cols):
+    # rows of very different magnitudes, an all-zero row, and ragged widths;
+    # up to 1024 rows take the block-per-row kernel, more the wave-per-row one
     g = torch.Generator().manual_seed(5)
-    v = torch.randn(37, 1000, generator=g) * torch.exp2(torch.randint(-20, 20, (37, 1), generator=g).float())
+    v = torch.randn(rows, cols, generator=g) * torch.exp2(torch.randint(-20, 20, (rows, 1), generator=g).float())
     v[4] = 0.0
-    v[6, :500] *= 1e-4  # values near the E4M3 subnormal range of that row
+    v[6, :cols // 2] *= 1e-4  # values near the E4M3 subnormal range of that row
     src = v.to(torch.bfloat16)
     codes, scales = B.quantize_rows_fp8(src.cuda())
     torch.cuda.synchronize()
