@@ -54,9 +54,10 @@ ties in float32 are broken by the lower expert id.
 Data format: bf16 tensors are numpy uint16 arrays of bf16 bit patterns;
 fp32 tensors are float32 arrays.  NVFP4 expert weights are byte arrays of
 E2M1 codes (two per byte, even element in the low nibble), E4M3 block scales
-(one per 16 consecutive fan-in elements) and one fp32 tensor scale per
-expert matrix (overview s3.1.1, NVFP4 format: E2M1 elements, 16-element
-micro-blocks, E4M3 block scale).
+(one per 16 consecutive fan-in elements, or one per 16 x 16 block of the 2-D
+variant) and one fp32 tensor scale per expert matrix (overview s3.1.1, NVFP4
+format: E2M1 elements, 16-element micro-blocks, E4M3 block scale; release
+news: two-dimensional weight blocks).
 """
 from __future__ import annotations
 
@@ -168,12 +169,20 @@ def quantize_rows_fp8(v) -> tuple:
 
 
 def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, tensor_scale: float) -> np.ndarray:
-    """w[r][c] = E2M1(code[r][c]) * E4M3(scale[r][c // 16]) * tensor_scale."""
+    """w[r][c] = E2M1(code[r][c]) * E4M3(scale[r][c // 16]) * tensor_scale,
+    or with 2-D blocks (one scale per 16 rows x 16 columns, scales
+    [R/16][K/16]; the Ultra release news describes the pretrained weights as
+    quantised in two-dimensional blocks) E4M3(scale[r // 16][c // 16])."""
     codes = np.asarray(codes)
+    scales = np.asarray(scales)
     q = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.float64)
     q[..., 0::2] = e2m1_value(codes & 0x0F)
     q[..., 1::2] = e2m1_value(codes >> 4)
     s = np.repeat(e4m3_value(scales), 16, axis=-1)
+    if scales.shape[-2] != codes.shape[-2]:
+        if scales.shape[-2] * 16 != codes.shape[-2]:
+            raise ValueError("block scales neither per row nor per 16 rows")
+        s = np.repeat(s, 16, axis=-2)
     return q * s * float(tensor_scale)
 
 

@@ -24,9 +24,9 @@ LMOE_ERR_ALIGN = -4
 LMOE_ERR_WORKSPACE = -5
 LMOE_ERR_HIP = -6
 
-LMOE_F32, LMOE_BF16, LMOE_NVFP4, LMOE_BF16_TILED, LMOE_FP8_E4M3 = 0, 1, 2, 3, 4
+LMOE_F32, LMOE_BF16, LMOE_NVFP4, LMOE_BF16_TILED, LMOE_FP8_E4M3, LMOE_NVFP4_2D = 0, 1, 2, 3, 4, 5
 DTYPE_CODE = {"f32": LMOE_F32, "bf16": LMOE_BF16, "nvfp4": LMOE_NVFP4, "bf16_tiled": LMOE_BF16_TILED,
-              "fp8": LMOE_FP8_E4M3}
+              "fp8": LMOE_FP8_E4M3, "nvfp4_2d": LMOE_NVFP4_2D}
 
 EXPORTED = ["lmoe_workspace_bytes", "lmoe_validate_dims", "lmoe_strerror", "lmoe_last_hip_error",
             "latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",

@@ -23,7 +23,9 @@ Recipe (one stream per tensor, so every tensor is reproducible alone):
     grid, a per-matrix fp32 tensor scale ts = 1/sqrt(fan_in), and the
     element code is W / (s * ts) clamped to [-6, 6] and rounded to the
     nearest E2M1 value (ties to the even mantissa).  Two codes per byte,
-    the even element in the low nibble.
+    the even element in the low nibble.  The 2-D variant (nvfp4_2d) draws
+    one block scale per 16 x 16 block (16 weight rows by 16 fan-in
+    elements) instead of per 16 fan-in elements of one row.
 
 The random draws depend on the torch device's generator: CPU and GPU
 streams differ.  Whatever is drawn, both sides of a comparison read the
@@ -48,8 +50,8 @@ class LayerDims:
     T tokens, hidden width d, latent width l (= d/4), E routed experts, top-k,
     expert intermediate width f, shared-expert intermediate width f_s
     (0 = no shared expert).  act is the activation/storage dtype ('f32' or
-    'bf16'); experts is the routed-expert weight format ('f32', 'bf16' or
-    'nvfp4'); zipf_bias adds the skewed router bias; router_latent makes the
+    'bf16'); experts is the routed-expert weight format ('f32', 'bf16',
+    'nvfp4' or 'nvfp4_2d'); zipf_bias adds the skewed router bias; router_latent makes the
     router read the latent z (W_r [E][l]) instead of x (W_r [E][d]);
     shared_fp8 stores the shared expert's weights as E4M3 codes with one fp32
     scale per output row; standard_moe is the comparison layer without the
@@ -150,11 +152,12 @@ def _e2m1_codes(v: torch.Tensor) -> torch.Tensor:
     return code | ((v < 0).to(torch.int32) << 3)
 
 
-def _nvfp4_quantize(W: torch.Tensor, scale_u: torch.Tensor, fan_in: int):
-    """W [R][K] fp32, scale_u [R][K/16] in [0.5, 2] -> (codes [R][K/2] u8, scales [R][K/16] u8, ts)."""
+def _nvfp4_quantize(W: torch.Tensor, scale_u: torch.Tensor, fan_in: int, rows_per_scale: int = 1):
+    """W [R][K] fp32, scale_u [R/rows_per_scale][K/16] in [0.5, 2] ->
+    (codes [R][K/2] u8, scales [R/rows_per_scale][K/16] u8, ts)."""
     ts = torch.tensor(1.0 / math.sqrt(fan_in), dtype=torch.float32).item()
     s = _round_to_e4m3_grid(scale_u)
-    v = W / (s.repeat_interleave(16, dim=-1) * ts)
+    v = W / (s.repeat_interleave(16, dim=-1).repeat_interleave(rows_per_scale, dim=-2) * ts)
     v = v.clamp_(-6.0, 6.0)
     code = _e2m1_codes(v)
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8)
@@ -174,18 +177,20 @@ def _expert_stack(cfg: LayerDims, which: str, seed: int, device, chunk: int = 32
             e1 = min(E, e0 + chunk)
             out[e0:e1] = _normal((e1 - e0, rows, fan_in), std, g, device, dt)
         return {which: out}
-    assert cfg.experts == "nvfp4"
+    assert cfg.experts in ("nvfp4", "nvfp4_2d")
     assert fan_in % 16 == 0
+    rps = 16 if cfg.experts == "nvfp4_2d" else 1  # weight rows per block scale
+    assert rows % rps == 0
     gs = _gen(device, seed, which + "_scale")
     codes = torch.empty((E, rows, fan_in // 2), dtype=torch.uint8, device=device)
-    scales = torch.empty((E, rows, fan_in // 16), dtype=torch.uint8, device=device)
+    scales = torch.empty((E, rows // rps, fan_in // 16), dtype=torch.uint8, device=device)
     ts_all = torch.empty((E,), dtype=torch.float32, device=device)
     for e0 in range(0, E, chunk):
         e1 = min(E, e0 + chunk)
         W = torch.randn((e1 - e0, rows, fan_in), generator=g, device=device, dtype=torch.float32).mul_(std)
-        su = torch.rand((e1 - e0, rows, fan_in // 16), generator=gs, device=device,
+        su = torch.rand((e1 - e0, rows // rps, fan_in // 16), generator=gs, device=device,
                         dtype=torch.float32).mul_(1.5).add_(0.5)
-        c, s, ts = _nvfp4_quantize(W, su, fan_in)
+        c, s, ts = _nvfp4_quantize(W, su, fan_in, rps)
         codes[e0:e1] = c
         scales[e0:e1] = s
         ts_all[e0:e1] = ts

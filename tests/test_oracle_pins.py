@@ -33,6 +33,7 @@ SMALL_BF16 = TINY.with_(name="small_bf16", T=48, d=128, l=32, E=12, k=3, f=64, f
                         act="bf16", experts="bf16")
 SMALL_NVFP4 = TINY.with_(name="small_nvfp4", T=40, d=128, l=32, E=8, k=2, f=64, f_s=0,
                          act="bf16", experts="nvfp4")
+SMALL_NVFP4_2D = SMALL_NVFP4.with_(name="small_nvfp4_2d", experts="nvfp4_2d")
 SMALL_ZIPF = SMALL_BF16.with_(name="small_zipf", zipf_bias=True, f_s=0)
 SMALL_LATENT = SMALL_BF16.with_(name="small_latent", router_latent=True)
 SMALL_FP8 = SMALL_BF16.with_(name="small_fp8_shared", f_s=128, shared_fp8=True)
@@ -96,27 +97,50 @@ def test_bf16_decode_matches_torch():
     assert np.array_equal(got, ref)
 
 
-def test_nvfp4_generator_roundtrip_is_nearest_grid_point():
+@pytest.mark.parametrize("rps", [1, 16], ids=["blocks_1x16", "blocks_16x16"])
+def test_nvfp4_generator_roundtrip_is_nearest_grid_point(rps):
     # The generator's encoder and the oracle's decoder are independent: decoding
     # what was encoded must give the nearest E2M1 point (ties to even mantissa)
-    # to W / (s * ts) clamped to [-6, 6].
+    # to W / (s * ts) clamped to [-6, 6], with one block scale per 16
+    # fan-in elements of a row (rps = 1) or per 16 x 16 block (rps = 16).
     g = torch.Generator().manual_seed(7)
     R, K = 64, 256
     W = torch.randn((R, K), generator=g) / math.sqrt(K)
     # plant exact midpoints and clamp cases
     ts = np.float32(1.0 / math.sqrt(K))
-    su = torch.rand((R, K // 16), generator=g) * 1.5 + 0.5
-    codes, scales, ts_val = synth._nvfp4_quantize(W, su, K)
+    su = torch.rand((R // rps, K // 16), generator=g) * 1.5 + 0.5
+    codes, scales, ts_val = synth._nvfp4_quantize(W, su, K, rps)
     s = O.e4m3_value(scales.numpy())
+    assert scales.shape == (R // rps, K // 16)
     assert np.all((s >= 0.5) & (s <= 2.0))
     w = O.nvfp4_dequant(codes.numpy(), scales.numpy(), ts_val)
     assert ts_val == float(ts)
-    v = np.clip(W.numpy().astype(np.float64) / (np.repeat(s, 16, axis=1) * float(np.float32(ts))), -6, 6)
-    q = w / (np.repeat(s, 16, axis=1) * ts_val)
+    s_full = np.repeat(np.repeat(s, 16, axis=1), rps, axis=0)  # the scale of every weight
+    v = np.clip(W.numpy().astype(np.float64) / (s_full * float(np.float32(ts))), -6, 6)
+    q = w / (s_full * ts_val)
     grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
     dist = np.abs(np.abs(v)[..., None] - grid)
     best = np.min(dist, axis=-1)
     assert np.allclose(np.abs(np.abs(q) - np.abs(v)), best, rtol=0, atol=1e-6)
+
+
+def test_nvfp4_2d_blocks_are_row_blocks_with_repeated_scales():
+    # a 16 x 16 block scale is the per-row 1 x 16 scale repeated over the
+    # block's 16 rows: the 2-D decode equals the 1-D decode of the expanded
+    # scale array, bit for bit
+    g = torch.Generator().manual_seed(11)
+    codes = torch.randint(0, 256, (3, 48, 32), generator=g, dtype=torch.uint8).numpy()
+    s2 = torch.randint(0x28, 0x40, (3, 3, 4), generator=g, dtype=torch.uint8).numpy()  # E4M3 0.25 .. 1.875
+    two_d = O.nvfp4_dequant(codes[1], s2[1], 0.125)
+    one_d = O.nvfp4_dequant(codes[1], np.repeat(s2[1], 16, axis=0), 0.125)
+    assert np.array_equal(two_d, one_d)
+    # element (r, c) takes scale (r // 16, c // 16): spot values by hand
+    for r, c in [(0, 0), (15, 15), (16, 15), (47, 63), (20, 33)]:
+        code = (codes[1, r, c // 2] >> (4 * (c % 2))) & 0xF
+        want = O.e2m1_value(code) * O.e4m3_value(s2[1, r // 16, c // 16]) * 0.125
+        assert two_d[r, c] == want
+    with pytest.raises(ValueError):
+        O.nvfp4_dequant(codes[1], s2[1][:2], 1.0)  # 2 scale rows for 48 weight rows
 
 
 def test_nvfp4_ties_go_to_even_mantissa():
@@ -223,7 +247,7 @@ def dense_bruteforce(inp, k):
     return out
 
 
-@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_ZIPF, SMALL_LATENT, TINY_LATENT, SMALL_FP8,
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_NVFP4_2D, SMALL_ZIPF, SMALL_LATENT, TINY_LATENT, SMALL_FP8,
                                  SMALL_STANDARD,
                                  TINY.with_(k=1), TINY.with_(E=5, k=5)], ids=lambda c: f"{c.name}-E{c.E}k{c.k}")
 def test_sparse_equals_dense_bruteforce(cfg):
@@ -315,8 +339,8 @@ def test_shared_expert_alone():
     assert rel_err(r["out"], ref.numpy()) <= 1e-12
 
 
-def test_nvfp4_forward_equals_dense_forward_on_dequantised_weights():
-    cfg = SMALL_NVFP4
+@pytest.mark.parametrize("cfg", [SMALL_NVFP4, SMALL_NVFP4_2D], ids=lambda c: c.name)
+def test_nvfp4_forward_equals_dense_forward_on_dequantised_weights(cfg):
     inp = host_inputs(cfg)
     dense = dict(inp)
     dense["W1"] = np.stack([O.nvfp4_dequant(inp["W1_codes"][e], inp["W1_scales"][e], inp["W1_ts"][e]) for e in range(cfg.E)])
