@@ -213,7 +213,7 @@ def decode(cfg, steps, torch, B, synth, layout="tiled", graph=False):
 def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     """The other MFMA-bound workloads (same metric, reported beside the headline)."""
     inp, out, ms, _, kernels, _ = prefill(cfg, steps, warmup, torch, B, synth, layout)
-    gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
+    gname = "grouped_gemm_nvfp4" if cfg.experts in ("nvfp4", "nvfp4_2d") else "grouped_gemm"
     g = kernels.get(gname)
     res = dict(workload=f"{cfg.name}: T={cfg.T} d={cfg.d} l={cfg.l} E={cfg.E} k={cfg.k} f={cfg.f} f_s={cfg.f_s}, "
                         f"{cfg.experts} experts, router reads {'z (latent)' if cfg.router_latent else 'x'}"
@@ -316,7 +316,7 @@ def main():
     layer_tflops = cfg.flops / (ms * 1e-3) / 1e12
 
     # Dominant kernel: the grouped expert GEMM (two launches per step, equal FLOPs).
-    gname = "grouped_gemm_nvfp4" if cfg.experts == "nvfp4" else "grouped_gemm"
+    gname = "grouped_gemm_nvfp4" if cfg.experts in ("nvfp4", "nvfp4_2d") else "grouped_gemm"
     g = kernels.get(gname)
     flops_per_launch = 2.0 * cfg.T * cfg.k * cfg.l * cfg.f
     roofline = None
@@ -360,6 +360,7 @@ def main():
     if not args.no_extra:
         C = synth.CONFIGS
         extra = [C[n] for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload]
+        extra.append(C["prefill_nvfp4"].with_(name="prefill_nvfp4_2d", experts="nvfp4_2d"))
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_latent_router", router_latent=True))
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_shared", shared_fp8=True))
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_proj_shared", shared_fp8=True, proj_fp8=True))

@@ -63,6 +63,7 @@ extern "C" {
 #define LMOE_NVFP4 2  /* routed-expert weights only, see lmoe_experts */
 #define LMOE_BF16_TILED 3  /* routed-expert bf16 weights in the tiled layout, see lmoe_pack_expert_weights */
 #define LMOE_FP8_E4M3 4    /* shared-expert and projection weights, see lmoe_shared, lmoe_fp8_matrix */
+#define LMOE_NVFP4_2D 5    /* routed-expert weights only: NVFP4 with 16 x 16 scale blocks, see lmoe_experts */
 
 /*
  * Layer sizes.  Constraints (LMOE_ERR_SHAPE otherwise):
@@ -71,8 +72,8 @@ extern "C" {
  *   f >= 64 and f % 64 == 0; f_s == 0 (no shared expert) or f_s % 64 == 0.
  * Dtypes (LMOE_ERR_DTYPE otherwise):
  *   act_dtype LMOE_F32 with expert_dtype LMOE_F32, or
- *   act_dtype LMOE_BF16 with expert_dtype LMOE_BF16, LMOE_BF16_TILED or
- *   LMOE_NVFP4.
+ *   act_dtype LMOE_BF16 with expert_dtype LMOE_BF16, LMOE_BF16_TILED,
+ *   LMOE_NVFP4 or LMOE_NVFP4_2D.
  * router_latent (0 or 1, LMOE_ERR_SHAPE otherwise): 0 = the router reads x in
  *   d, W_r [E][d] (the overview's paragraph after the section 2.2 table keeps
  *   the gate in d); 1 = the router reads the latent z as stored (act dtype),
@@ -132,7 +133,11 @@ typedef struct lmoe_fp8_matrix {
  *   M_scales [E][rows][K/16] uint8: E4M3 (FN) scale of each 16-element block
  *                                   along K;
  *   M_ts     [E] fp32: per-expert tensor scale.
- * The weight is w = E2M1(code) * E4M3(scale) * ts.  LMOE_BF16_TILED uses
+ * The weight is w = E2M1(code) * E4M3(scale) * ts.  LMOE_NVFP4_2D (the Ultra
+ * release news: weights quantised in two-dimensional blocks) shares one
+ * scale among 16 rows x 16 elements: M_scales [E][rows/16][K/16], the
+ * weight in row r and column c taking scale [r/16][c/16]; codes and ts as
+ * above.  LMOE_BF16_TILED uses
  * W1 and W2 as written by lmoe_pack_expert_weights from the BF16 stacks (the
  * same values; results are identical to passing the BF16 stacks).  Unused
  * fields are ignored.

@@ -238,7 +238,7 @@ static int check_workspace(const lmoe_dims& d, const void* ws, size_t bytes) {
 
 static int check_experts(const lmoe_dims& d, const lmoe_experts* x) {
     if (!x) return LMOE_ERR_NULL;
-    if (d.expert_dtype == LMOE_NVFP4)
+    if (d.expert_dtype == LMOE_NVFP4 || d.expert_dtype == LMOE_NVFP4_2D)
         return check_ptrs({x->W1_codes, x->W1_scales, x->W1_ts, x->W2_codes, x->W2_scales, x->W2_ts});
     return check_ptrs({x->W1, x->W2});
 }
@@ -438,7 +438,8 @@ int lmoe_validate_dims(const lmoe_dims* d) {
         if (d->expert_dtype != LMOE_F32) return LMOE_ERR_DTYPE;
         if (max_tiles(*d) > 65535) return LMOE_ERR_SHAPE;  // grid.y of the fp32 grouped kernel
     } else if (d->act_dtype == LMOE_BF16) {
-        if (d->expert_dtype != LMOE_BF16 && d->expert_dtype != LMOE_BF16_TILED && d->expert_dtype != LMOE_NVFP4)
+        if (d->expert_dtype != LMOE_BF16 && d->expert_dtype != LMOE_BF16_TILED && d->expert_dtype != LMOE_NVFP4 &&
+            d->expert_dtype != LMOE_NVFP4_2D)
             return LMOE_ERR_DTYPE;
     } else {
         return LMOE_ERR_DTYPE;

@@ -643,7 +643,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         return make_int4(t.x, t.y, t.z, (w % nN) * C::BN);
     };
 
-    constexpr bool B_DMA = C::DMA && BFMT != LMOE_NVFP4;
+    // NVFP4 weights, with block scales per 16 fan-in elements of a row or
+    // (LMOE_NVFP4_2D) per 16 x 16 block
+    constexpr bool FP4 = BFMT == LMOE_NVFP4 || BFMT == LMOE_NVFP4_2D;
+    constexpr bool B_DMA = C::DMA && !FP4;
     static_assert(BFMT != LMOE_BF16_TILED || (C::DMA && C::BK == 64 && C::BN % 64 == 0),
                   "tiled weights: LDS-DMA, K step 64, whole 64-row slabs");
     using SA = Slots<C, C::BM>;
@@ -652,13 +655,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     // elements (EPL/2 code bytes, EPL/16 scale bytes) per lane, loaded into
     // registers and decoded into the LDS tile.
     constexpr int LPR = C::NT / C::BN, EPL = C::BK / (LPR > 0 ? LPR : 1);
-    static_assert(BFMT != LMOE_NVFP4 || (C::NT % C::BN == 0 && (LPR == 2 || LPR == 4) && C::BK == 64),
+    static_assert(!FP4 || (C::NT % C::BN == 0 && (LPR == 2 || LPR == 4) && C::BK == 64),
                   "NVFP4 tiles: 2 or 4 lanes per weight row, K step 64");
     typedef uint32_t code_words_t __attribute__((ext_vector_type(EPL >= 16 ? EPL / 8 : 2)));
 
     // ---- fill side: pointers of the item whose K steps are being issued
     const uint16_t* a_ptr[SA::N];
-    const uint16_t* b_ptr[BFMT == LMOE_NVFP4 ? 1 : SB::N];
+    const uint16_t* b_ptr[FP4 ? 1 : SB::N];
     const uint8_t* c_ptr = nullptr;  // NVFP4: this lane's codes and scales
     const uint8_t* s_ptr = nullptr;
     int4 fdesc = load_item(0);
@@ -701,10 +704,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             const int ar = a_row(j, row0, rows);
             a_ptr[j] = (const uint16_t*)g.A + (int64_t)ar * g.lda + SA::lchunk(j, tid) * 8;
         }
-        if constexpr (BFMT == LMOE_NVFP4) {
+        if constexpr (FP4) {
             const int64_t n = (int64_t)e * N + min(n0 + tid / LPR, N - 1);
             c_ptr = g.B_codes + n * (K / 2) + (tid % LPR) * (EPL / 2);
-            s_ptr = g.B_scales + n * (K / 16) + (tid % LPR) * (EPL / 16);
+            // 2-D blocks: N is a multiple of 16, so weight row n of the stack
+            // has scale row n / 16 of [E][N/16][K/16]
+            const int64_t srow = BFMT == LMOE_NVFP4_2D ? n >> 4 : n;
+            s_ptr = g.B_scales + srow * (K / 16) + (tid % LPR) * (EPL / 16);
         } else if constexpr (BFMT == LMOE_BF16_TILED) {
             // 64-row slabs of 64x64 tiles, each stored in the swizzled order of
             // the LDS tile (the swizzle repeats every 16 rows and n0 is a
@@ -725,7 +731,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     };
     setup(fdesc);
 
-    u32x4_t ra[C::DMA ? 1 : SA::N], rb[B_DMA || BFMT == LMOE_NVFP4 ? 1 : SB::N];
+    u32x4_t ra[C::DMA ? 1 : SA::N], rb[B_DMA || FP4 ? 1 : SB::N];
     code_words_t rc;  // NVFP4: EPL codes
     uint32_t rs = 0;  // NVFP4: EPL/16 scale bytes
     // issues the next K step of the fill item into stage (As, Bs)
@@ -739,7 +745,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         }
         const int kt = f_kt++;
         const int kk = kt * C::BK;
-        if constexpr (BFMT == LMOE_NVFP4) {
+        if constexpr (FP4) {
             // register loads first, so waiting for them does not wait for the DMA
             rc = *reinterpret_cast<const code_words_t*>(c_ptr + kt * (C::BK / 2));
             if constexpr (EPL == 32)
@@ -770,7 +776,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 #pragma unroll
             for (int j = 0; j < SA::N; ++j) As[lds_idx<C>(SA::row(j, tid), SA::lchunk(j, tid))] = ra[j];
         }
-        if constexpr (BFMT == LMOE_NVFP4) {
+        if constexpr (FP4) {
             static_for<EPL / 8>([&](auto wc) __attribute__((always_inline)) {
                 constexpr int w = decltype(wc)::value;  // 8 elements; scale block w / 2
                 float pw, mt;
@@ -788,7 +794,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     int4 mdesc = fdesc;
     float mscale = 1.0f;
     auto fetch_scale = [&](const int4& d) __attribute__((always_inline)) {
-        if constexpr (BFMT == LMOE_NVFP4) mscale = sload_f32(g.B_ts + d.x);
+        if constexpr (FP4) mscale = sload_f32(g.B_ts + d.x);
     };
     fetch_scale(mdesc);
     auto epilogue = [&](const int4& d, f32x16_t (&acc)[C::TM][C::TN]) __attribute__((always_inline)) {
@@ -1229,7 +1235,7 @@ template <class C, int BFMT, bool SK>
 static void launch_grouped_fmt(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
     constexpr int RPI = Slots<C, C::BM>::RPI;
     constexpr bool can_scalar = C::DMA && (RPI == 8 || RPI == 16);
-    const char* name = BFMT == LMOE_NVFP4 ? "grouped_gemm_nvfp4" : "grouped_gemm";
+    const char* name = (BFMT == LMOE_NVFP4 || BFMT == LMOE_NVFP4_2D) ? "grouped_gemm_nvfp4" : "grouped_gemm";
     if (!g.a_row_map)
         LMOE_LAUNCH(name, s, grouped_gemm_kernel<C, BFMT, GATHER_NONE, SK><<<grid, C::NT, 0, s>>>(g, nN));
     else if (can_scalar && g.n_rows >= RPI)
@@ -1244,6 +1250,8 @@ template <class C, bool SK>
 static void launch_grouped_any(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
     if (g.b_fmt == LMOE_NVFP4)
         launch_grouped_fmt<C, LMOE_NVFP4, SK>(g, grid, nN, s);
+    else if (g.b_fmt == LMOE_NVFP4_2D)
+        launch_grouped_fmt<C, LMOE_NVFP4_2D, SK>(g, grid, nN, s);
     else if (g.b_fmt == LMOE_BF16_TILED)
         launch_grouped_fmt<C, LMOE_BF16_TILED, SK>(g, grid, nN, s);
     else

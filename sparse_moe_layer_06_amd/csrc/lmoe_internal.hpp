@@ -78,10 +78,10 @@ struct GroupedGemm {
     const int* a_row_map;
     int a_row_div;
     int n_rows;  // sorted rows in total (T * k): bound of a_row_map
-    int b_fmt;  // LMOE_F32 / LMOE_BF16 dense stack [E][N][K], LMOE_BF16_TILED, or LMOE_NVFP4
+    int b_fmt;  // LMOE_F32 / LMOE_BF16 dense stack [E][N][K], LMOE_BF16_TILED, LMOE_NVFP4 or LMOE_NVFP4_2D
     const void* B;
     const uint8_t* B_codes;   // [E][N][K/2]
-    const uint8_t* B_scales;  // [E][N][K/16]
+    const uint8_t* B_scales;  // [E][N][K/16], or [E][N/16][K/16] with 2-D blocks
     const float* B_ts;        // [E]
     int epi;                  // EPI_RELU2 or EPI_STORE
     void* C;

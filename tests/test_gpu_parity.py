@@ -80,6 +80,12 @@ SMALL = {
                                act="bf16", experts="nvfp4", proj_fp8=True, shared_fp8=True, router_latent=True),
     "fp8_proj_zipf": TINY.with_(name="fp8_proj_zipf", T=64, d=2048, l=512, E=64, k=6, f=256, f_s=0,
                                 act="bf16", experts="bf16", proj_fp8=True, zipf_bias=True),
+    # NVFP4 with 16 x 16 scale blocks: 192-row tiles, and the split-K 64 x 256
+    # tiles with a ragged N = 1280
+    "nvfp4_2d_deep": TINY.with_(name="nvfp4_2d_deep", T=300, d=512, l=128, E=4, k=2, f=256, f_s=0,
+                                act="bf16", experts="nvfp4_2d"),
+    "nvfp4_2d_few_wide": TINY.with_(name="nvfp4_2d_few_wide", T=16, d=4096, l=1024, E=16, k=2, f=1280, f_s=0,
+                                    act="bf16", experts="nvfp4_2d"),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
@@ -329,6 +335,14 @@ def test_decode_standard_moe_full_size():
 @pytest.mark.timeout(900)
 def test_prefill_nvfp4_full_size():
     cfg = CFG["prefill_nvfp4"]
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=16, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_nvfp4_2d_full_size():
+    cfg = CFG["prefill_nvfp4"].with_(name="prefill_nvfp4_2d", experts="nvfp4_2d")
     log(f"case {cfg}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     P.run_and_check(cfg, inp, n_sample=16, lazy_experts=True, report=log)
