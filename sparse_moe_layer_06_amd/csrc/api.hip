@@ -6,6 +6,7 @@
 // steps 1-3; shared expert per the paragraph after its table):
 //   1. dense MFMA GEMM  x [W_down; W_r; W_s1]^T -> z, logits (+bias), hs
 //   2. top-k + softmax gate                     -> idx, gate
+//      (with few tokens: in step 1's split-K reduction)
 //   3. permutation (hist, scan + tile table, stable scatter)
 //   4. grouped GEMM  H = relu(z[perm] W1_e^T)^2
 //   5. grouped GEMM  Y = H W2_e^T
@@ -286,7 +287,17 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
                                     hipStream_t s) {
     const DenseGemm g = gemm_in(d, x, W_down, W_r, bias, sh ? sh->W_s1 : nullptr, z, logits, hs);
     hipError_t e = hipSuccess;
-    if (g.N > 0) e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
+    // Few tokens with the router in d: the top-k is taken in this GEMM's
+    // split-K reduction, from the logits columns (after the latent ones).
+    const bool route_fused = !d.router_latent && d.act_dtype == LMOE_BF16 &&
+                             dense_topk_fusable(g, L.splitk_bytes, (int)d.E, (int)d.k);
+    if (route_fused) {
+        const int lc0 = (d.standard_moe || proj_fp8(d)) ? 0 : (int)d.l;
+        e = launch_dense_gemm_topk_bf16(g, ws + L.splitk, L.splitk_bytes, lc0, (int)d.E, bias, (int)d.k, idx, gate,
+                                        s);
+    } else if (g.N > 0) {
+        e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
+    }
     if (e != hipSuccess) return e;
     uint8_t* qx = (uint8_t*)(ws + L.q_x);
     float* sx = (float*)(ws + L.s_x);
@@ -323,6 +334,7 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
         e = launch_fp8_gemm(f, ws + L.splitk, L.splitk_bytes, s);
         if (e != hipSuccess) return e;
     }
+    if (route_fused) return hipSuccess;
     return launch_topk_softmax(logits, (int)d.T, (int)d.E, (int)d.k, idx, gate, s);
 }
 

@@ -31,6 +31,7 @@
 
 #include "device_common.hpp"
 #include "lmoe_internal.hpp"
+#include "topk_row.hpp"
 
 namespace lmoe {
 
@@ -519,6 +520,57 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseGemm g, int spl
     } else {
         for (int c = 0; c < 4 && n + c < g.N; ++c) dense_store1(g, m, n + c, v[c]);
     }
+}
+
+// The decode-sized first GEMM's reduction with the router folded in: one
+// block per token row sums the row's split partials in split order and
+// stores them through the column groups' epilogues, as splitk_reduce_kernel
+// does, and keeps the row's logits (columns [lc0, lc0 + E), bias added: the
+// values the logits epilogue stores) in LDS; its first wave then selects the
+// token's top-k and gates from there, as the router kernel does from the
+// stored logits.  This saves the router kernel's launch and its re-read.
+// 1024 threads, so a decode row's 2560 columns take one pass of float4
+// chunks, with up to 16 splits' loads in flight per thread.
+template <int S>
+__global__ __launch_bounds__(1024) void splitk_reduce_topk_kernel(DenseGemm g, int splits,
+                                                                 const float* __restrict__ partial, int ldp,
+                                                                 int lc0, int E, const float* __restrict__ bias,
+                                                                 int k, int32_t* __restrict__ idx,
+                                                                 float* __restrict__ gate) {
+    __shared__ float s_l[S * kWave];
+    __shared__ uint64_t by_id[kWave], by_rank[kWave];
+    const int m = blockIdx.x;
+    for (int n = threadIdx.x * 4; n < g.N; n += 1024 * 4) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        constexpr int kBatch = 16;
+        for (int sp0 = 0; sp0 < splits; sp0 += kBatch) {
+            float4 p[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                if (sp0 + b < splits)
+                    p[b] = *reinterpret_cast<const float4*>(partial + ((int64_t)(sp0 + b) * g.M + m) * ldp + n);
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                if (sp0 + b < splits) {
+                    v[0] += p[b].x;
+                    v[1] += p[b].y;
+                    v[2] += p[b].z;
+                    v[3] += p[b].w;
+                }
+        }
+        if (n + 3 < g.N) {
+            dense_store4(g, m, n, v);
+        } else {
+            for (int c = 0; c < 4 && n + c < g.N; ++c) dense_store1(g, m, n + c, v[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = n + c - lc0;
+            if (e >= 0 && e < E) s_l[e] = v[c] + (bias ? bias[e] : 0.f);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) topk_select_row<S>(s_l, E, k, m, by_id, by_rank, idx, gate);
 }
 
 // ---------------------------------------------------------------------------
@@ -1335,9 +1387,52 @@ size_t dense_tail_split_bytes(const DenseGemm& g) {
 // fastest shape measured for the 8192-wide projections; 256x192 where that
 // fills the GPU better (narrow N, few M tiles).  Decode-sized M uses 64x64
 // tiles with split-K.
+// Few rows (decode): weight streaming with 64x64 tiles, 4 stages, 2 blocks
+// per CU, split-K.
+using DecodeDenseCfg = MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>;
+
+static int decode_dense_splits(const DenseGemm& g, size_t ws_bytes) {
+    using C = DecodeDenseCfg;
+    const int tiles = (g.M + C::BM - 1) / C::BM * ((g.N + C::BN - 1) / C::BN);
+    const int nk = g.K[0] / C::BK + (g.nseg > 1 ? g.K[1] / C::BK : 0);
+    return splitk_factor(tiles, nk, g.M, (g.N + 3) / 4 * 4, ws_bytes, C::MINB);
+}
+
+bool dense_topk_fusable(const DenseGemm& g, size_t splitk_bytes, int E, int k) {
+    return g.M <= 64 && k <= kWave && E <= 1024 && decode_dense_splits(g, splitk_bytes) > 1;
+}
+
+hipError_t launch_dense_gemm_topk_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, int lc0, int E,
+                                       const float* bias, int k, int32_t* idx, float* gate, hipStream_t s) {
+    using C = DecodeDenseCfg;
+    if (!dense_topk_fusable(g, splitk_bytes, E, k) || lc0 < 0 || lc0 + E > g.N) return hipErrorInvalidValue;
+    const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
+    const int ldp = (g.N + 3) / 4 * 4;
+    const int splits = decode_dense_splits(g, splitk_bytes);
+    float* partial = (float*)splitk_ws;
+    LMOE_LAUNCH("dense_gemm", s,
+                dense_gemm_kernel<C><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
+                                                                                  partial, ldp));
+#define LMOE_REDUCE_TOPK(S_)                                                                                  \
+    LMOE_LAUNCH("splitk_reduce_topk", s,                                                                      \
+                splitk_reduce_topk_kernel<S_><<<g.M, 1024, 0, s>>>(g, splits, partial, ldp, lc0, E, bias, k, idx, \
+                                                                 gate))
+    if (E <= 64)
+        LMOE_REDUCE_TOPK(1);
+    else if (E <= 128)
+        LMOE_REDUCE_TOPK(2);
+    else if (E <= 256)
+        LMOE_REDUCE_TOPK(4);
+    else if (E <= 512)
+        LMOE_REDUCE_TOPK(8);
+    else
+        LMOE_REDUCE_TOPK(16);
+#undef LMOE_REDUCE_TOPK
+    return hipGetLastError();
+}
+
 hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s) {
-    if (g.M <= 64)  // weight streaming: 64x64 tiles, 4 stages, 2 blocks per CU, split-K
-        return run_dense<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, splitk_ws, splitk_bytes, s);
+    if (g.M <= 64) return run_dense<DecodeDenseCfg>(g, splitk_ws, splitk_bytes, s);
     using C256 = MfmaCfg<256, 256, 4, 2, true, 64, 2>;
     // The cost of a shape is its rounds of tiles over the CUs times the tile
     // width (a split tail round costs about a quarter); 256-wide tiles

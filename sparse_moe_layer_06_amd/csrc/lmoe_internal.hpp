@@ -106,6 +106,13 @@ struct Fp8Gemm {
     uint16_t* C;
     int64_t ldc;
 };
+// The decode-sized first dense GEMM (bf16, split along K) with the router's
+// top-k and gates taken in its reduction, from the logits columns
+// [lc0, lc0 + E) (+ bias): dense_topk_fusable says whether a call takes
+// that path (at most 64 rows, k <= 64, a split, E <= 1024).
+bool dense_topk_fusable(const DenseGemm& g, size_t splitk_bytes, int E, int k);
+hipError_t launch_dense_gemm_topk_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, int lc0, int E,
+                                       const float* bias, int k, int32_t* idx, float* gate, hipStream_t s);
 hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s);
 
 // Per-row FP8 quantisation of a bf16 matrix [rows][cols] (row stride ld):

@@ -24,20 +24,11 @@
 // j % 64 keeps selection j in register slot j / 64.
 #include "device_common.hpp"
 #include "lmoe_internal.hpp"
+#include "topk_row.hpp"
 
 namespace lmoe {
 
 constexpr int kMaxE = 1024;
-
-__device__ __forceinline__ uint32_t ordered_bits(float v) {
-    uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0: equal logits compare equal
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float unordered_value(uint32_t o) {
-    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-    return __uint_as_float(u);
-}
 
 // v = max(v, v moved by one DPP pattern); lanes the pattern does not reach
 // read 0, the smallest key.
@@ -145,77 +136,14 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     }
 }
 
-// Gates of the k (<= 64) selections held by lanes 0..k-1, in rank order:
-// softmax with the rank-0 logit as the shift.
-__device__ __forceinline__ void write_gates(float v, int e, int lane, int64_t t, int k, int32_t* __restrict__ idx,
-                                            float* __restrict__ gate) {
-    const float vmax = __shfl(v, 0, kWave);
-    const float w = lane < k ? expf(v - vmax) : 0.f;
-    const float inv_sum = 1.0f / wave_sum(w);
-    if (lane < k) {
-        idx[t * k + lane] = e;
-        gate[t * k + lane] = w * inv_sum;
-    }
-}
-
 template <int S>
 __global__ __launch_bounds__(256) void topk_select_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ gate) {
     __shared__ uint64_t by_id[4][kWave], by_rank[4][kWave];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;  // whole wave exits together
-    const float* s = logits + (int64_t)t * E;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-    uint32_t v[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-        const int e = lane + i * kWave;
-        v[i] = (e < E) ? ordered_bits(s[e]) : 0u;  // 0 is below every encoded logit
-    }
-    auto count_ge = [&](uint32_t y) __attribute__((always_inline)) {
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < S; ++i) c += __popcll(__ballot(v[i] >= y));
-        return c;
-    };
-    uint32_t X = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t y = X | (1u << b);
-        if (count_ge(y) >= k) X = y;
-    }
-    // logits above X are all selected; ties at X go to the lowest ids
-    int need = k;
-#pragma unroll
-    for (int i = 0; i < S; ++i) need -= __popcll(__ballot(v[i] > X));
-    int base = 0;  // position of this slot's first selection in id order
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-        const int e = lane + i * kWave;
-        const bool eq = e < E && v[i] == X;
-        const uint64_t m_eq = __ballot(eq);
-        const bool take = v[i] > X || (eq && __popcll(m_eq & lt_mask) < need);
-        need -= min(need, __popcll(m_eq));
-        const uint64_t m = __ballot(take);
-        if (take) by_id[wv][base + __popcll(m & lt_mask)] = ((uint64_t)v[i] << 32) | (uint32_t)(~(uint32_t)e);
-        base += __popcll(m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // rank = the number of selected keys above this one (keys are distinct)
-    if (lane < k) {
-        const uint64_t key = by_id[wv][lane];
-        int rank = 0;
-        for (int q = 0; q < k; ++q) rank += by_id[wv][q] > key;
-        by_rank[wv][rank] = key;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint64_t key = lane < k ? by_rank[wv][lane] : 0ull;
-    write_gates(unordered_value((uint32_t)(key >> 32)), (int)(~(uint32_t)key), lane, t, k, idx, gate);
+    topk_select_row<S>(logits + (int64_t)t * E, E, k, t, by_id[wv], by_rank[wv], idx, gate);
 }
 
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* gate,

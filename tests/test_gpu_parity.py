@@ -135,17 +135,23 @@ def test_all_tokens_to_one_expert():
     assert counts[3] == counts[7] == counts[1] == cfg.T and counts.sum() == cfg.T * cfg.k
 
 
-def test_exact_logit_ties_break_to_lower_id():
-    # x = 0 makes every logit equal to its bias; equal biases must pick the lower ids.
-    cfg = SMALL["bf16_ragged"].with_(f_s=0)
+@pytest.mark.parametrize("T,d", [(193, 256), (64, 1024)], ids=["router_kernel", "in_gemm_reduction"])
+def test_exact_logit_ties_break_to_lower_id(T, d):
+    # x = 0 makes every logit equal to its bias; equal biases must pick the
+    # lower ids.  64 tokens with d = 1024 take the top-k inside the first
+    # GEMM's split-K reduction.
+    cfg = SMALL["bf16_ragged"].with_(f_s=0, T=T, d=d, l=d // 4)
     inp = small_inputs(cfg)
     inp["x"].zero_()
     inp["b_r"] = torch.tensor([0.5, 1.0, 1.0, 0.0, 1.0, 0.5, 2.0, 1.0, 0, 0, 0, 0], dtype=torch.float32).cuda()
     dbg = P.debug_buffers(cfg, cfg.T)
-    B.forward(cfg, inp, debug=dbg)
-    torch.cuda.synchronize()
+    with B.KernelTimer() as kt:
+        B.forward(cfg, inp, debug=dbg)
+        torch.cuda.synchronize()
     idx = dbg["topk_idx"].cpu().numpy()
     assert np.all(idx == np.array([6, 1, 2])), idx[:2]
+    fused = "splitk_reduce_topk" in kt.by_kernel()
+    assert fused == (T == 64) and fused != ("topk_softmax" in kt.by_kernel())
 
 
 def test_staged_entry_points_compose_to_forward():
