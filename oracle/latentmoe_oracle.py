@@ -34,10 +34,12 @@ paragraph):
      in bf16) is quantised per token to E4M3 with scale max|v|/448 before
      its product
   FP8 projections (the Ultra model card, "Model design", keeps the latent
-  projections out of NVFP4, in BF16 or MXFP8; here the 8-bit option takes
-  the shared expert's scheme, not MX blocks): W_down and W_up as E4M3 codes
-  times one scale per output row, each input quantised per token like the
-  shared expert's (x before W_down; c as stored in bf16 before W_up).
+  projections out of NVFP4, in BF16 or MXFP8): either the shared expert's
+  scheme (W_down and W_up as E4M3 codes times one scale per output row,
+  each input quantised per token), or MXFP8 (OCP microscaling: E4M3
+  elements sharing one power-of-two E8M0 scale per 32 consecutive fan-in
+  elements, for the weights and for each input row).  The inputs are x
+  before W_down and c as stored in bf16 before W_up.
   Without W_down and W_up the same steps describe the standard MoE layer the
   overview compares against (section 2.2 table: 128 experts, top-6, experts
   in the hidden width): z_t = x_t and out_t = c_t (+ shared expert).
@@ -168,6 +170,45 @@ def quantize_rows_fp8(v) -> tuple:
     return e4m3_encode(q.astype(np.float64)), scale
 
 
+def e8m0_value(byte) -> np.ndarray:
+    """E8M0 scale byte -> float64: 2^(byte - 127); 255 is NaN."""
+    b = np.asarray(byte).astype(np.int64)
+    return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+def quantize_blocks_mxfp8(v) -> tuple:
+    """MXFP8 quantisation of the rows of v [n][K] (K a multiple of 32), per
+    block of 32 consecutive elements: shared exponent e = floor(log2 max|v|)
+    minus 8 (the largest E4M3 exponent), clamped to [-127, 127], so the
+    block's largest magnitude lands in [256, 512) times 2^-e; the scale is
+    the E8M0 byte e + 127 (127 for an all-zero block); each element is the
+    E4M3 code (nearest, ties to even) of v / 2^e saturated to +-448.  The
+    division by a power of two is exact.  Returns (codes uint8 [n][K],
+    scales uint8 [n][K/32])."""
+    v = np.asarray(v, dtype=np.float64)
+    n, K = v.shape
+    blocks = v.reshape(n, K // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, p = np.frexp(amax)                      # amax = f 2^p, f in [0.5, 1)
+    e = np.where(amax > 0, p.astype(np.int64) - 1 - 8, 0)
+    e = np.clip(e, -127, 127)
+    q = np.clip(blocks / np.ldexp(1.0, e)[..., None], -448.0, 448.0)
+    codes = e4m3_encode(q).reshape(n, K)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """E4M3(code) * E8M0(scale of its 32-element block) for [rows][K]."""
+    return e4m3_value(codes) * np.repeat(e8m0_value(scales), 32, axis=-1)
+
+
+def mxfp8_product(v: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """v W^T with MXFP8 weights W (codes, E8M0 block scales), the rows of v
+    quantised to MXFP8 first (quantize_blocks_mxfp8)."""
+    qv, sv = quantize_blocks_mxfp8(as_f64(v))
+    return mxfp8_dequant(qv, sv) @ mxfp8_dequant(codes, scales).T
+
+
 def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, tensor_scale: float) -> np.ndarray:
     """w[r][c] = E2M1(code[r][c]) * E4M3(scale[r][c // 16]) * tensor_scale,
     or with 2-D blocks (one scale per 16 rows x 16 columns, scales
@@ -242,8 +283,11 @@ def fp8_product(v: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndar
 def project(v: np.ndarray, inp: dict, name: str) -> np.ndarray:
     """v W^T for the projection weight inp[name] (W_down or W_up) in its
     stored format: bf16 / fp32 values, or E4M3 codes (uint8) with per-row
-    scales under name + '_scale'."""
+    fp32 scales under name + '_scale', or MXFP8 codes with E8M0 block scales
+    (uint8 [rows][K/32]) under name + '_mxscale'."""
     W = np.asarray(inp[name])
+    if W.dtype == np.uint8 and inp.get(name + "_mxscale") is not None:
+        return mxfp8_product(v, W, np.asarray(inp[name + "_mxscale"]))
     if W.dtype == np.uint8:
         return fp8_product(v, W, inp[name + "_scale"])
     return as_f64(v) @ as_f64(W).T

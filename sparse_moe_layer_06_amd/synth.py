@@ -15,7 +15,9 @@ Recipe (one stream per tensor, so every tensor is reproducible alone):
     bf16 (round to nearest even) for bf16 tensors.
   * FP8 shared-expert weights (shared_fp8) and FP8 projection weights
     (proj_fp8, W_down and W_up): the same fp32 draws, stored as E4M3 codes
-    with one fp32 scale per output row (max |row| / 448).
+    with one fp32 scale per output row (max |row| / 448).  MXFP8 projection
+    weights (proj_mxfp8): E4M3 codes with one E8M0 scale per 32 fan-in
+    elements, 2^(floor(log2 max|block|) - 8), codes saturated to +-448.
   * The skewed-routing workload adds a per-expert router bias
     b_e = 2 * log(1 / (e + 1)), stored in fp32.
   * NVFP4 expert weights: W ~ N(0, 1/fan_in) in fp32, a block scale
@@ -56,7 +58,8 @@ class LayerDims:
     shared_fp8 stores the shared expert's weights as E4M3 codes with one fp32
     scale per output row; standard_moe is the comparison layer without the
     latent projections (l = d, no W_down / W_up); proj_fp8 stores W_down and
-    W_up that way too.
+    W_up that way too; proj_mxfp8 stores them as MXFP8 (E4M3 with an E8M0
+    scale per 32 fan-in elements) instead.
     """
     name: str
     T: int
@@ -73,6 +76,7 @@ class LayerDims:
     shared_fp8: bool = False
     standard_moe: bool = False
     proj_fp8: bool = False
+    proj_mxfp8: bool = False
 
     def with_(self, **kw) -> "LayerDims":
         return dataclasses.replace(self, **kw)
@@ -234,10 +238,29 @@ def make_inputs(cfg: LayerDims, seed: int = 0, device="cpu") -> Dict[str, Option
 def _proj_weight(cfg: LayerDims, shape, fan_in: int, gen, dev, act, inp, name: str):
     """A projection weight in the activation dtype, or as E4M3 codes (its
     per-row scales stored under name + '_scale') with proj_fp8."""
+    if cfg.proj_mxfp8:
+        codes, inp[name + "_mxscale"] = _mxfp8_rows(_normal(shape, 1.0 / math.sqrt(fan_in), gen, dev,
+                                                            torch.float32))
+        return codes
     if not cfg.proj_fp8:
         return _normal(shape, 1.0 / math.sqrt(fan_in), gen, dev, act)
     codes, inp[name + "_scale"] = _fp8_rows(_normal(shape, 1.0 / math.sqrt(fan_in), gen, dev, torch.float32))
     return codes
+
+
+def _mxfp8_rows(W: torch.Tensor):
+    """fp32 W [rows][K] -> (E4M3 codes uint8 [rows][K], E8M0 scale bytes
+    uint8 [rows][K/32]): per 32 consecutive elements e = floor(log2 max|w|)
+    - 8 (clamped to [-127, 127]; 0 for an all-zero block), codes = torch's
+    float8_e4m3fn cast of w / 2^e saturated to +-448."""
+    rows, K = W.shape
+    b = W.reshape(rows, K // 32, 32)
+    amax = b.abs().amax(dim=2)
+    _, p = torch.frexp(amax)
+    e = torch.where(amax > 0, p - 9, torch.zeros_like(p)).clamp(-127, 127)
+    q = (b / torch.ldexp(torch.ones_like(amax), e)[..., None]).clamp(-448.0, 448.0)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(rows, K)
+    return codes.contiguous(), (e + 127).to(torch.uint8).contiguous()
 
 
 def _fp8_rows(W: torch.Tensor):

@@ -40,6 +40,7 @@ SMALL_FP8 = SMALL_BF16.with_(name="small_fp8_shared", f_s=128, shared_fp8=True)
 SMALL_STANDARD = SMALL_BF16.with_(name="small_standard", l=128, E=8, k=2, standard_moe=True)
 TINY_LATENT = TINY.with_(name="tiny_latent", router_latent=True)
 SMALL_FP8_PROJ = SMALL_BF16.with_(name="small_fp8_proj", proj_fp8=True)
+SMALL_MXFP8_PROJ = SMALL_BF16.with_(name="small_mxfp8_proj", proj_mxfp8=True)
 
 
 # ---------------------------------------------------------------------------
@@ -568,23 +569,82 @@ def test_standard_moe_is_latent_layer_with_identity_projections():
 # FP8 down- and up-projections
 # ---------------------------------------------------------------------------
 
+def torch_mx_quant(v64):
+    """MXFP8 by torch: frexp for the block exponent, ldexp, clamp, the
+    float8_e4m3fn cast for the codes and float8_e8m0fnu to decode the scale."""
+    v = torch.from_numpy(np.asarray(v64, dtype=np.float64))
+    n, K = v.shape
+    b = v.reshape(n, K // 32, 32)
+    amax = b.abs().amax(dim=2)
+    _, p = torch.frexp(amax)
+    e = torch.where(amax > 0, p - 9, torch.zeros_like(p)).clamp(-127, 127)
+    codes = (b / torch.ldexp(torch.ones_like(amax), e)[..., None]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    scales = (e + 127).to(torch.uint8)
+    return codes.view(torch.uint8).reshape(n, K), scales
+
+
+def torch_mx_dequant(codes, scales):
+    c = torch.as_tensor(codes).view(torch.float8_e4m3fn).to(torch.float64)
+    s = torch.as_tensor(scales).view(torch.float8_e8m0fnu).to(torch.float64)
+    return c * s.repeat_interleave(32, dim=-1)
+
+
+def test_mxfp8_quantisation_against_torch():
+    # blocks of very different magnitudes, an all-zero block, blocks whose
+    # largest element saturates (|v| / 2^e in (448, 512)), exact powers of
+    # two and E4M3 midpoints
+    g = torch.Generator().manual_seed(13)
+    v = torch.randn(24, 256, generator=g, dtype=torch.float64)
+    v = v * torch.exp2(torch.randint(-30, 30, (24, 8), generator=g).double()).repeat_interleave(32, dim=1)
+    v[3, 32:64] = 0.0
+    v[4, :32] = torch.linspace(-1, 1, 32, dtype=torch.float64) * 0.99
+    v[4, 5] = 1.97  # e = 0 - 8: 1.97 * 256 = 504 saturates to 448
+    v[5, :32] = 2.0 ** torch.arange(-16, 16, dtype=torch.float64)
+    v[6, :32] = (torch.arange(32, dtype=torch.float64) + 0.5) / 16  # many E4M3 midpoints
+    v = v.to(torch.float32).to(torch.float64)  # float32-representable values
+    codes, scales = O.quantize_blocks_mxfp8(v.numpy())
+    tc, ts = torch_mx_quant(v.numpy())
+    assert np.array_equal(scales, ts.numpy())
+    assert np.array_equal(codes, tc.numpy())
+    assert scales[3, 1] == 127 and not codes[3, 32:64].any()
+    assert O.e4m3_value(codes[4, 5]) == 448.0
+    deq = O.mxfp8_dequant(codes, scales)
+    assert np.array_equal(deq, torch_mx_dequant(tc, ts).numpy())
+    # every non-zero block's largest magnitude decodes into [256, 448] 2^e
+    amax = np.max(np.abs(O.e4m3_value(codes)).reshape(24, 8, 32), axis=2)
+    nz = amax > 0
+    assert np.all((amax[nz] >= 256) & (amax[nz] <= 448))
+
+
+def test_e8m0_decode_matches_torch():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = O.e8m0_value(b)
+    assert np.array_equal(got[:255], ref[:255]) and np.isnan(got[255]) and np.isnan(ref[255])
+
+
+@pytest.mark.parametrize("fmt", ["fp8_rows", "mxfp8"])
 @pytest.mark.parametrize("latent", [False, True], ids=["router_in_d", "router_in_l"])
-def test_fp8_projections_against_torch_casts(latent):
-    # the layer with E4M3 W_down / W_up re-derived with torch's float8 and
-    # bf16 casts: z from the per-token codes of x, the routed part by the
-    # dense brute force (every expert, masked softmax), and out from the
-    # per-token codes of c as stored in bf16
-    cfg = SMALL_FP8_PROJ.with_(router_latent=latent)
+def test_fp8_projections_against_torch_casts(latent, fmt):
+    # the layer with 8-bit W_down / W_up re-derived with torch's float8 and
+    # bf16 casts: z from the quantised x, the routed part by the dense brute
+    # force (every expert, masked softmax), and out from the quantised c as
+    # stored in bf16; per-row E4M3 scales or MXFP8 blocks
+    cfg = (SMALL_MXFP8_PROJ if fmt == "mxfp8" else SMALL_FP8_PROJ).with_(router_latent=latent)
     inp = host_inputs(cfg)
     f8 = torch.float8_e4m3fn
 
     def quant(v64):
+        if fmt == "mxfp8":
+            return torch_mx_dequant(*torch_mx_quant(v64))
         v = torch.from_numpy(np.asarray(v64, dtype=np.float64)).to(torch.float32)
         amax = v.abs().amax(dim=1)
         sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
         return (v / sc[:, None]).to(f8).to(torch.float64) * sc.to(torch.float64)[:, None]
 
     def weights(name):
+        if fmt == "mxfp8":
+            return torch_mx_dequant(torch.from_numpy(inp[name]), torch.from_numpy(inp[name + "_mxscale"]))
         return (torch.from_numpy(inp[name]).view(f8).to(torch.float64)
                 * torch.from_numpy(inp[name + "_scale"]).to(torch.float64)[:, None])
 
