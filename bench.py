@@ -195,7 +195,8 @@ def decode(cfg, steps, torch, B, synth, layout="tiled", graph=False):
     l, f, d, E, T = cfg.l, cfg.f, cfg.d, cfg.E, cfg.T
     r_in = l if cfg.router_latent else d  # router weights W_r [E][r_in]
     # W_down and W_up: bf16, or E4M3 codes plus one fp32 scale per row
-    proj = 0 if cfg.standard_moe else (2 * d * l + 4 * (l + d) if cfg.proj_fp8 else 2 * d * l * 2)
+    proj = (0 if cfg.standard_moe else 2 * d * l + 4 * (l + d) if cfg.proj_fp8
+            else 2 * d * l + 2 * d * l // 32 if cfg.proj_mxfp8 else 2 * d * l * 2)
     bytes_alg = (touched * 2 * l * f * 2 + proj + r_in * E * 2 + 2 * T * d * 2
                  + (E * 4 if cfg.zipf_bias else 0))
     gbs = bytes_alg / (ms * 1e-3) / 1e9
@@ -203,7 +204,8 @@ def decode(cfg, steps, torch, B, synth, layout="tiled", graph=False):
                          f"({layout if cfg.experts == 'bf16' else 'as stored'}), router reads "
                          f"{'z (latent)' if cfg.router_latent else 'x'}"
                          f"{', standard MoE (experts in d)' if cfg.standard_moe else ''}"
-                         f"{', FP8 projections' if cfg.proj_fp8 else ''}", tokens_per_s=T / (ms * 1e-3),
+                         f"{', FP8 projections' if cfg.proj_fp8 else ''}"
+                         f"{', MXFP8 projections' if cfg.proj_mxfp8 else ''}", tokens_per_s=T / (ms * 1e-3),
                 ms_per_step=ms, experts_touched=touched, alg_bytes=bytes_alg, achieved_GBps=gbs,
                 hbm_frac=gbs * 1e9 / PEAK_HBM_BYTES, timing="median of %d single-step hipEvent timings, "
                 "1 GiB buffer read between steps (cache eviction)" % steps, kernels=kernels,
@@ -219,6 +221,7 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
                         f"{cfg.experts} experts, router reads {'z (latent)' if cfg.router_latent else 'x'}"
                         f"{', FP8 shared expert (E4M3 x E4M3 MFMA)' if cfg.shared_fp8 else ''}"
                         f"{', FP8 down- and up-projections' if cfg.proj_fp8 else ''}"
+                        f"{', MXFP8 down- and up-projections' if cfg.proj_mxfp8 else ''}"
                         f"{', standard MoE (experts in d, no latent projections)' if cfg.standard_moe else ''}",
                ms_per_step=ms, tokens_per_s=cfg.T / (ms * 1e-3),
                layer_tflops=cfg.flops / (ms * 1e-3) / 1e12, layer_mfma_frac=cfg.flops / (ms * 1e-3) / PEAK_BF16_FLOPS)
@@ -230,7 +233,7 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     # the fp8 products: the shared expert's two (2 T d f_s FLOPs each) and
     # the two projections (2 T d l each)
     f8_flops = (4.0 * cfg.T * cfg.d * cfg.f_s if cfg.shared_fp8 else 0.0) + \
-        (4.0 * cfg.T * cfg.d * cfg.l if cfg.proj_fp8 else 0.0)
+        (4.0 * cfg.T * cfg.d * cfg.l if cfg.proj_fp8 or cfg.proj_mxfp8 else 0.0)
     if f8 and f8_flops > 0:
         ach = f8_flops / (f8["ms_per_step"] * 1e-3)
         res["fp8_gemm"] = dict(avg_launch_ms=f8["avg_ms"], launches_per_step=f8["launches_per_step"],
@@ -364,6 +367,8 @@ def main():
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_latent_router", router_latent=True))
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_shared", shared_fp8=True))
         extra.append(C["prefill_bf16"].with_(name="prefill_bf16_fp8_proj_shared", shared_fp8=True, proj_fp8=True))
+        extra.append(C["prefill_bf16"].with_(name="prefill_bf16_mxfp8_proj_fp8_shared", shared_fp8=True,
+                                             proj_mxfp8=True))
         # the standard MoE the overview compares against: 128 experts of d, top-6
         extra.append(C["prefill_bf16"].with_(name="prefill_standard_moe", l=C["prefill_bf16"].d, E=128, k=6,
                                              standard_moe=True))
@@ -375,6 +380,9 @@ def main():
                 args.decode_steps, torch, B, synth, args.expert_layout)
             result["other_workloads"]["decode_fp8_proj"] = decode(
                 C["decode_bf16_zipf"].with_(name="decode_fp8_proj", proj_fp8=True),
+                args.decode_steps, torch, B, synth, args.expert_layout)
+            result["other_workloads"]["decode_mxfp8_proj"] = decode(
+                C["decode_bf16_zipf"].with_(name="decode_mxfp8_proj", proj_mxfp8=True),
                 args.decode_steps, torch, B, synth, args.expert_layout)
             result["other_workloads"]["decode_standard_moe"] = decode(
                 C["decode_bf16_zipf"].with_(name="decode_standard_moe", l=C["decode_bf16_zipf"].d, E=128, k=6,

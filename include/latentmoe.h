@@ -64,6 +64,7 @@ extern "C" {
 #define LMOE_BF16_TILED 3  /* routed-expert bf16 weights in the tiled layout, see lmoe_pack_expert_weights */
 #define LMOE_FP8_E4M3 4    /* shared-expert and projection weights, see lmoe_shared, lmoe_fp8_matrix */
 #define LMOE_NVFP4_2D 5    /* routed-expert weights only: NVFP4 with 16 x 16 scale blocks, see lmoe_experts */
+#define LMOE_MXFP8 6       /* projection weights only: OCP MXFP8, see lmoe_mxfp8_matrix */
 
 /*
  * Layer sizes.  Constraints (LMOE_ERR_SHAPE otherwise):
@@ -97,7 +98,11 @@ extern "C" {
  *   lmoe_quantize_rows_fp8 does (x before W_down; the combined latent c, as
  *   stored in bf16, before W_up) and runs as an fp8 x fp8 MFMA GEMM with
  *   fp32 accumulation; z and out stay bf16.  The router and the expert FFNs
- *   are unchanged.
+ *   are unchanged.  LMOE_MXFP8 (the Ultra model card's "Model design" names
+ *   MXFP8 for the latent projections) works the same way with OCP MXFP8
+ *   blocks instead: W_down and W_up point to lmoe_mxfp8_matrix, and x and c
+ *   are quantised as lmoe_quantize_rows_mxfp8 does; the scaled fp8 MFMA
+ *   applies the block scales.
  */
 typedef struct lmoe_dims {
     int64_t T, d, l, E, k, f, f_s;
@@ -120,6 +125,18 @@ typedef struct lmoe_fp8_matrix {
     const uint8_t* codes;
     const float* scales;
 } lmoe_fp8_matrix;
+
+/*
+ * An MXFP8 weight matrix [rows][cols] (OCP microscaling: E4M3 elements, one
+ * E8M0 scale 2^(s - 127) per 32 consecutive elements of a row): codes
+ * [rows][cols] uint8 and scales [rows][cols/32] uint8, both device memory,
+ * 16-byte aligned; the struct itself is host memory, read during the call.
+ * Used for W_down and W_up with dims.proj_dtype = LMOE_MXFP8.
+ */
+typedef struct lmoe_mxfp8_matrix {
+    const uint8_t* codes;
+    const uint8_t* scales;
+} lmoe_mxfp8_matrix;
 
 /*
  * Routed-expert weights.  Dense formats (F32/BF16) use W1 [E][f][l] and
@@ -256,13 +273,28 @@ int lmoe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const void* 
 int lmoe_quantize_rows_fp8(int64_t rows, int64_t cols, const void* src, uint8_t* codes, float* scales,
                            void* stream);
 
+/*
+ * MXFP8 quantisation (OCP microscaling) of a row-major bf16 matrix [rows]
+ * [cols], as the MXFP8 projections quantise their inputs: per block of 32
+ * consecutive elements of a row, e = floor(log2 max|v|) - 8 (the largest
+ * E4M3 exponent), clamped to [-127, 127] and 0 for an all-zero block; the
+ * scale byte is e + 127 (E8M0) and each element's code is E4M3 (FN, nearest,
+ * ties to even) of v / 2^e saturated to +-448.  codes [rows][cols] uint8,
+ * scales [rows][cols/32] uint8.  rows >= 1, cols a positive multiple of 32
+ * up to 2^20 (LMOE_ERR_SHAPE); pointers 16-byte aligned.  Asynchronous on
+ * stream.
+ */
+int lmoe_quantize_rows_mxfp8(int64_t rows, int64_t cols, const void* src, uint8_t* codes, uint8_t* scales,
+                             void* stream);
+
 /* ---- the layer ------------------------------------------------------- */
 
 /*
  * The whole forward: out [T][d] = LatentMoE(x).  router_bias [E] fp32 may be
  * NULL (no bias); shared may be NULL (then dims.f_s must be 0); dbg may be
  * NULL.  W_down and W_up are device arrays in the activation dtype, or
- * host pointers to lmoe_fp8_matrix with dims.proj_dtype = LMOE_FP8_E4M3.  workspace must hold lmoe_workspace_bytes(dims) bytes.  The result
+ * host pointers to lmoe_fp8_matrix with dims.proj_dtype = LMOE_FP8_E4M3, or
+ * to lmoe_mxfp8_matrix with dims.proj_dtype = LMOE_MXFP8.  workspace must hold lmoe_workspace_bytes(dims) bytes.  The result
  * equals running lmoe_project_route, lmoe_permute, lmoe_experts_ffn and
  * lmoe_combine_up in that order.
  */

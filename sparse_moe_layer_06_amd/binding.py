@@ -24,14 +24,14 @@ LMOE_ERR_ALIGN = -4
 LMOE_ERR_WORKSPACE = -5
 LMOE_ERR_HIP = -6
 
-LMOE_F32, LMOE_BF16, LMOE_NVFP4, LMOE_BF16_TILED, LMOE_FP8_E4M3, LMOE_NVFP4_2D = 0, 1, 2, 3, 4, 5
+LMOE_F32, LMOE_BF16, LMOE_NVFP4, LMOE_BF16_TILED, LMOE_FP8_E4M3, LMOE_NVFP4_2D, LMOE_MXFP8 = 0, 1, 2, 3, 4, 5, 6
 DTYPE_CODE = {"f32": LMOE_F32, "bf16": LMOE_BF16, "nvfp4": LMOE_NVFP4, "bf16_tiled": LMOE_BF16_TILED,
-              "fp8": LMOE_FP8_E4M3, "nvfp4_2d": LMOE_NVFP4_2D}
+              "fp8": LMOE_FP8_E4M3, "nvfp4_2d": LMOE_NVFP4_2D, "mxfp8": LMOE_MXFP8}
 
 EXPORTED = ["lmoe_workspace_bytes", "lmoe_validate_dims", "lmoe_strerror", "lmoe_last_hip_error",
             "latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
             "lmoe_combine_up", "lmoe_timing_start", "lmoe_timing_stop", "lmoe_pack_expert_weights",
-            "lmoe_quantize_rows_fp8"]
+            "lmoe_quantize_rows_fp8", "lmoe_quantize_rows_mxfp8"]
 
 
 class Dims(ctypes.Structure):
@@ -44,7 +44,9 @@ class Dims(ctypes.Structure):
 
 
 class Fp8Matrix(ctypes.Structure):
-    """lmoe_fp8_matrix: E4M3 codes [rows][cols] and fp32 scales [rows] (device)."""
+    """lmoe_fp8_matrix: E4M3 codes [rows][cols] and fp32 scales [rows] (device);
+    also lmoe_mxfp8_matrix (codes, E8M0 scale bytes [rows][cols/32]): the
+    same two pointers."""
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
@@ -109,6 +111,7 @@ def lib() -> ctypes.CDLL:
         L.lmoe_pack_expert_weights.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
         L.lmoe_pack_expert_weights.restype = ctypes.c_int
         L.lmoe_quantize_rows_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, vp]
+        L.lmoe_quantize_rows_mxfp8.argtypes = [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, vp]
         L.lmoe_quantize_rows_fp8.restype = ctypes.c_int
         for n in ("latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
                   "lmoe_combine_up"):
@@ -133,7 +136,7 @@ def dims_of(cfg: LayerDims, T: Optional[int] = None) -> Dims:
     return Dims(T if T is not None else cfg.T, cfg.d, cfg.l, cfg.E, cfg.k, cfg.f, cfg.f_s,
                 DTYPE_CODE[cfg.act], DTYPE_CODE[cfg.experts], 1 if cfg.router_latent else 0,
                 DTYPE_CODE["fp8" if cfg.shared_fp8 else cfg.act], 1 if cfg.standard_moe else 0,
-                DTYPE_CODE["fp8" if cfg.proj_fp8 else cfg.act])
+                DTYPE_CODE["mxfp8" if cfg.proj_mxfp8 else "fp8" if cfg.proj_fp8 else cfg.act])
 
 
 class _Proj:
@@ -142,8 +145,8 @@ class _Proj:
 
     def __init__(self, cfg: LayerDims, inp, name: str):
         self.m = None
-        if cfg.proj_fp8:
-            self.m = Fp8Matrix(_p(inp[name]), _p(inp[name + "_scale"]))
+        if cfg.proj_fp8 or cfg.proj_mxfp8:
+            self.m = Fp8Matrix(_p(inp[name]), _p(inp[name + ("_mxscale" if cfg.proj_mxfp8 else "_scale")]))
             self.arg = ctypes.cast(ctypes.pointer(self.m), ctypes.c_void_p)
         else:
             self.arg = _p(inp.get(name))
@@ -227,6 +230,19 @@ def _byref_opt(s):
 
 def act_dtype(cfg: LayerDims) -> torch.dtype:
     return torch.bfloat16 if cfg.act == "bf16" else torch.float32
+
+
+def quantize_rows_mxfp8(src: torch.Tensor, stream=None):
+    """(codes uint8 [rows][cols], E8M0 scales uint8 [rows][cols/32]) of a
+    contiguous bf16 matrix, per 32-element block (OCP MXFP8)."""
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or not src.is_contiguous():
+        raise LatentMoEError(LMOE_ERR_DTYPE, "quantize_rows_mxfp8 needs a contiguous [rows][cols] bf16 matrix")
+    rows, cols = src.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=src.device)
+    _check(lib().lmoe_quantize_rows_mxfp8(rows, cols, _p(src), _p(codes), _p(scales), _stream(stream)),
+           "lmoe_quantize_rows_mxfp8")
+    return codes, scales
 
 
 class Call:

@@ -55,11 +55,14 @@ static int64_t max_tiles(const lmoe_dims& d) {
 // the last).
 static bool shared_fp8(const lmoe_dims& d) { return d.f_s > 0 && d.shared_dtype == LMOE_FP8_E4M3; }
 static bool shared_dense(const lmoe_dims& d) { return d.f_s > 0 && d.shared_dtype != LMOE_FP8_E4M3; }
-// FP8 down- and up-projections: fp8 GEMMs of their own, like the shared expert's.
+// 8-bit down- and up-projections: fp8 GEMMs of their own, like the shared
+// expert's, with per-row scales (FP8) or MXFP8 blocks.
 static bool proj_fp8(const lmoe_dims& d) { return d.proj_dtype == LMOE_FP8_E4M3; }
+static bool proj_mx(const lmoe_dims& d) { return d.proj_dtype == LMOE_MXFP8; }
+static bool proj_8bit(const lmoe_dims& d) { return proj_fp8(d) || proj_mx(d); }
 // Whether the last dense GEMM only adds the shared expert to an out that
-// already holds the routed result (standard MoE, or an fp8 up-projection).
-static bool out_add_only(const lmoe_dims& d) { return d.standard_moe || proj_fp8(d); }
+// already holds the routed result (standard MoE, or an 8-bit up-projection).
+static bool out_add_only(const lmoe_dims& d) { return d.standard_moe || proj_8bit(d); }
 
 // x [W_down; W_r; W_s1]^T -> z, logits (+ bias), hs (the shared expert's
 // hidden layer, only with f_s > 0 in the activation dtype).  With a latent
@@ -68,7 +71,7 @@ static bool out_add_only(const lmoe_dims& d) { return d.standard_moe || proj_fp8
 static DenseGemm gemm_in(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r, const float* bias,
                          const void* W_s1, void* z, float* logits, void* hs) {
     DenseGemm g{};
-    const int L = (d.standard_moe || proj_fp8(d)) ? 0 : (int)d.l;  // latent columns here
+    const int L = (d.standard_moe || proj_8bit(d)) ? 0 : (int)d.l;  // latent columns here
     const int E = d.router_latent ? 0 : (int)d.E;       // router columns in this GEMM
     const int fs = shared_dense(d) ? (int)d.f_s : 0;
     g.M = (int)d.T;
@@ -133,7 +136,8 @@ static DenseGemm gemm_out(const lmoe_dims& d, const void* c, const void* hs, con
 
 struct Layout {
     size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
-        c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, q_x, s_x, q_h, s_h, q_c, s_c, total;
+        c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, q_x, s_x, q_h, s_h, q_c, s_c, mq_x, ms_x, mq_c,
+        ms_c, total;
 };
 
 // Whether the few-rows expert GEMMs may take the split-K 64 x 256 tiles
@@ -201,6 +205,12 @@ static Layout plan(const lmoe_dims& d) {
         L.q_c = take((size_t)d.T * d.l);
         L.s_c = take((size_t)d.T * 4);
     }
+    if (proj_mx(d)) {  // MXFP8 codes and block scales of x and c
+        L.mq_x = take((size_t)d.T * d.d);
+        L.ms_x = take((size_t)d.T * (d.d / 32));
+        L.mq_c = take((size_t)d.T * d.l);
+        L.ms_c = take((size_t)d.T * (d.l / 32));
+    }
     if (expert_split_k(d)) {
         const int64_t widest_n = d.f > d.l ? d.f : d.l;
         L.sk_count_len = (size_t)(max_tiles(d) * ((widest_n + kSkBN - 1) / kSkBN));
@@ -247,8 +257,12 @@ static int check_experts(const lmoe_dims& d, const lmoe_experts* x) {
 // W_down or W_up as passed: a device array, or with FP8 projections a host
 // lmoe_fp8_matrix naming the codes and the per-row scales.
 static int check_proj(const lmoe_dims& d, const void* W) {
-    if (!proj_fp8(d)) return check_ptrs({W});
+    if (!proj_8bit(d)) return check_ptrs({W});
     if (!W) return LMOE_ERR_NULL;
+    if (proj_mx(d)) {
+        const lmoe_mxfp8_matrix* m = (const lmoe_mxfp8_matrix*)W;
+        return check_ptrs({m->codes, m->scales});
+    }
     const lmoe_fp8_matrix* m = (const lmoe_fp8_matrix*)W;
     return check_ptrs({m->codes, m->scales});
 }
@@ -292,7 +306,7 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
     const bool route_fused = !d.router_latent && d.act_dtype == LMOE_BF16 &&
                              dense_topk_fusable(g, L.splitk_bytes, (int)d.E, (int)d.k);
     if (route_fused) {
-        const int lc0 = (d.standard_moe || proj_fp8(d)) ? 0 : (int)d.l;
+        const int lc0 = (d.standard_moe || proj_8bit(d)) ? 0 : (int)d.l;
         e = launch_dense_gemm_topk_bf16(g, ws + L.splitk, L.splitk_bytes, lc0, (int)d.E, bias, (int)d.k, idx, gate,
                                         s);
     } else if (g.N > 0) {
@@ -309,6 +323,17 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
         const lmoe_fp8_matrix* W = (const lmoe_fp8_matrix*)W_down;
         e = launch_fp8_gemm(Fp8Gemm{(int)d.T, (int)d.l, (int)d.d, qx, d.d, sx, W->codes, d.d, W->scales, EPI_STORE,
                                     (uint16_t*)z, d.l},
+                            ws + L.splitk, L.splitk_bytes, s);
+        if (e != hipSuccess) return e;
+    }
+    if (proj_mx(d)) {  // z = MX(x) MX(W_down)^T
+        uint8_t* mq = (uint8_t*)(ws + L.mq_x);
+        uint8_t* ms = (uint8_t*)(ws + L.ms_x);
+        e = launch_quantize_blocks_mxfp8((const uint16_t*)x, d.T, (int)d.d, d.d, mq, ms, s);
+        if (e != hipSuccess) return e;
+        const lmoe_mxfp8_matrix* W = (const lmoe_mxfp8_matrix*)W_down;
+        e = launch_fp8_gemm(Fp8Gemm{(int)d.T, (int)d.l, (int)d.d, mq, d.d, nullptr, W->codes, d.d, nullptr,
+                                    EPI_STORE, (uint16_t*)z, d.l, ms, W->scales},
                             ws + L.splitk, L.splitk_bytes, s);
         if (e != hipSuccess) return e;
     }
@@ -402,6 +427,17 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
                             ws + L.splitk, L.splitk_bytes, s);
         if (e != hipSuccess) return e;
     }
+    if (proj_mx(d)) {  // out = MX(c) MX(W_up)^T, from c as stored
+        uint8_t* mq = (uint8_t*)(ws + L.mq_c);
+        uint8_t* ms = (uint8_t*)(ws + L.ms_c);
+        e = launch_quantize_blocks_mxfp8((const uint16_t*)c, d.T, (int)d.l, d.l, mq, ms, s);
+        if (e != hipSuccess) return e;
+        const lmoe_mxfp8_matrix* W = (const lmoe_mxfp8_matrix*)W_up;
+        e = launch_fp8_gemm(Fp8Gemm{(int)d.T, (int)d.d, (int)d.l, mq, d.l, nullptr, W->codes, d.l, nullptr,
+                                    EPI_STORE, (uint16_t*)out, d.d, ms, W->scales},
+                            ws + L.splitk, L.splitk_bytes, s);
+        if (e != hipSuccess) return e;
+    }
     if (!out_add_only(d) || shared_dense(d)) {
         const DenseGemm g = gemm_out(d, c, hs, W_up, sh ? sh->W_s2 : nullptr, out);
         e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
@@ -460,9 +496,11 @@ int lmoe_validate_dims(const lmoe_dims* d) {
         return LMOE_ERR_DTYPE;
     if (d->shared_dtype == LMOE_FP8_E4M3 && d->f_s % 128 != 0) return LMOE_ERR_SHAPE;  // fp8 K step
     if (d->proj_dtype != d->act_dtype &&
-        !(d->act_dtype == LMOE_BF16 && d->proj_dtype == LMOE_FP8_E4M3 && d->standard_moe == 0))
+        !(d->act_dtype == LMOE_BF16 && (d->proj_dtype == LMOE_FP8_E4M3 || d->proj_dtype == LMOE_MXFP8) &&
+          d->standard_moe == 0))
         return LMOE_ERR_DTYPE;
-    if (d->proj_dtype == LMOE_FP8_E4M3 && d->l % 128 != 0) return LMOE_ERR_SHAPE;  // fp8 K step of W_up
+    if ((d->proj_dtype == LMOE_FP8_E4M3 || d->proj_dtype == LMOE_MXFP8) && d->l % 128 != 0)
+        return LMOE_ERR_SHAPE;  // fp8 K step of W_up
     return LMOE_OK;
 }
 
@@ -503,6 +541,15 @@ int lmoe_quantize_rows_fp8(int64_t rows, int64_t cols, const void* src, uint8_t*
     LMOE_TRY(check_ptrs({src, codes, scales}));
     return hip_status(launch_quantize_rows_fp8((const uint16_t*)src, rows, (int)cols, cols, codes, scales,
                                                (hipStream_t)stream));
+}
+
+int lmoe_quantize_rows_mxfp8(int64_t rows, int64_t cols, const void* src, uint8_t* codes, uint8_t* scales,
+                             void* stream) {
+    if (rows < 1 || rows > ((int64_t)1 << 31) || cols < 32 || cols % 32 != 0 || cols > (1 << 20))
+        return LMOE_ERR_SHAPE;
+    LMOE_TRY(check_ptrs({src, codes, scales}));
+    return hip_status(launch_quantize_blocks_mxfp8((const uint16_t*)src, rows, (int)cols, cols, codes, scales,
+                                                   (hipStream_t)stream));
 }
 
 int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,

@@ -60,12 +60,25 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_
 }
 
 // 32x32x64 fp8 (E4M3 x E4M3) MFMA, fp32 accumulate: acc += A(32x64) * B(64x32).
-// Lane l supplies row (l % 32) of A and column (l % 32) of B, each as 32
-// consecutive k values starting at 32 * (l / 32) (checked on the device).
-// The block-scale operands are unused (0 selects the unscaled form).
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, 32 codes each.
+// The unscaled product only needs a lane's A and B codes to cover the same
+// k; the hardware's own K order (measured on the device with block scales)
+// is k 16 (l/32) + [0, 16) in the first four registers and 32 + 16 (l/32)
+// + [0, 16) in the last four.  The block-scale operands are unused here (0
+// selects the unscaled form).
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x16_t mfma32x32x64_fp8(const i32x8_t& a, const i32x8_t& b, f32x16_t acc) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+}
+
+// The same MFMA with MX block scales (OCP microscaling, E8M0: 2^(s - 127)):
+// lane l passes the scale byte of the 32-element K block it holds, for its
+// A row in sa and for its B column in sb, in byte OPSEL of the register
+// (checked on the device with runtime scales, 127 being 1).
+template <int OPSEL>
+__device__ __forceinline__ f32x16_t mfma32x32x64_mxfp8(const i32x8_t& a, const i32x8_t& b, f32x16_t acc, int sa,
+                                                       int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, OPSEL, sa, OPSEL, sb);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {

@@ -256,6 +256,65 @@ __device__ __forceinline__ void mma_tile_fp8(const u32x4_t* __restrict__ As, con
     });
 }
 
+// MXFP8 variant of mma_tile_fp8: the stage also holds one 32-bit word of
+// E8M0 block scales per A row and per B row (the 4 blocks of 32 codes of
+// this K step, block b in byte b) at S: A rows first, then B rows.  Sub-step
+// ks multiplies blocks 2 ks and 2 ks + 1, and lane l passes the scale of
+// block 2 ks + l / 32 of its row (measured on the device: lanes 0..31's
+// scales cover the sub-step's k 0..31, lanes 32..63's k 32..63).  Each lane
+// shifts its words right by 8 (l / 32) once, so the byte it needs is byte
+// 2 ks for every lane, picked by the MFMA's operand select, and no scale
+// register is rewritten between the tile's MFMAs.
+template <class C>
+__device__ __forceinline__ void mma_tile_mx(const u32x4_t* __restrict__ As, const u32x4_t* __restrict__ Bs,
+                                            const u32x4_t* __restrict__ S, f32x16_t (&acc)[C::TM][C::TN], int wm,
+                                            int wn, int lane) {
+    constexpr int KS = 2, NM = C::TM * C::TN, NR = 2 * (C::TM + C::TN);
+    const uint32_t* Su = reinterpret_cast<const uint32_t*>(S);
+    const int lane_shift = 8 * (lane >> 5);
+    int sa[C::TM], sb[C::TN];
+#pragma unroll
+    for (int tm = 0; tm < C::TM; ++tm) sa[tm] = (int)(Su[wm * C::WM + tm * 32 + (lane & 31)] >> lane_shift);
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) sb[tn] = (int)(Su[C::BM + wn * C::WN + tn * 32 + (lane & 31)] >> lane_shift);
+    i32x8_t af[2][C::TM], bfr[2][C::TN];
+    // The MFMA's true K order: lane l's first four registers are k 16 (l/32)
+    // + [0, 16) and its last four k 32 + 16 (l/32) + [0, 16), so scale block
+    // 0 (k 0..31, the scale of lanes 0..31) is code chunks 0 and 1 of the
+    // sub-step, held in the low halves of both lane halves.
+    auto frag = [&](const u32x4_t* T, int row, int ch) __attribute__((always_inline)) {
+        const u32x4_t lo = T[lds_idx<C>(row, ch)], hi = T[lds_idx<C>(row, ch + 2)];
+        return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto read = [&](int ks, int b) __attribute__((always_inline)) {
+        const int ch = ks * 4 + (lane >> 5);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = frag(As, wm * C::WM + tm * 32 + (lane & 31), ch);
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) bfr[b][tn] = frag(Bs, wn * C::WN + tn * 32 + (lane & 31), ch);
+    };
+    read(0, 0);
+    static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(kc)::value, b = ks & 1;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks + 1 < KS) read(ks + 1, b ^ 1);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn)
+                acc[tm][tn] = mfma32x32x64_mxfp8<2 * ks>(bfr[b][tn], af[b][tm], acc[tm][tn], sb[tn], sa[tm]);
+        if constexpr (ks + 1 < KS) {
+            static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value, r = (m + 1) * NR / NM - m * NR / NM;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS read
+            });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
 // K loop over nk tiles through a ring of C::STAGES LDS stages.
 //   fill(kt, As, Bs)  starts moving tile kt into a stage (DMA issue, and/or
 //                     global loads into registers);
@@ -263,11 +322,12 @@ __device__ __forceinline__ void mma_tile_fp8(const u32x4_t* __restrict__ As, con
 // Tile kt + STAGES - 1 is issued while tile kt is multiplied, so up to
 // STAGES - 1 tiles are in flight.  PER_TILE is the number of DMA
 // instructions per tile and wave; 0 means "wait for everything" (register
-// staged operands already wait in land).
-template <class C, int PER_TILE, bool F8 = false, class Fill, class Land>
+// staged operands already wait in land).  MODE: 0 bf16, 1 fp8, 2 MXFP8,
+// whose stages carry EXTRA more chunks (the block scales) after the tiles.
+template <class C, int PER_TILE, int MODE = 0, int EXTRA = 0, class Fill, class Land>
 __device__ __forceinline__ void kloop(int nk, Fill&& fill, Land&& land, u32x4_t* ring,
                                       f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
-    constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS, AOFF = C::BM * C::CPR;
+    constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS + EXTRA, AOFF = C::BM * C::CPR;
     constexpr int MAXAHEAD = PER_TILE > 0 ? S - 2 : 0;
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) {
@@ -283,7 +343,9 @@ __device__ __forceinline__ void kloop(int nk, Fill&& fill, Land&& land, u32x4_t*
         u32x4_t* ns = ring + nxt * STG;
         if (more) fill(kt + S - 1, ns, ns + AOFF);
         u32x4_t* cs = ring + cur * STG;
-        if constexpr (F8)
+        if constexpr (MODE == 2)
+            mma_tile_mx<C>(cs, cs + AOFF, cs + C::STAGE_CHUNKS, acc, wm, wn, lane);
+        else if constexpr (MODE == 1)
             mma_tile_fp8<C>(cs, cs + AOFF, acc, wm, wn, lane);
         else
             mma_tile<C>(cs, cs + AOFF, acc, wm, wn, lane);
@@ -1019,11 +1081,20 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 // [split * nk / splits, (split + 1) * nk / splits) and stores its scaled
 // fp32 partial tile to partial[split][M][ldp]; splitk_reduce_kernel adds the
 // splits in order and applies the epilogue.
-template <class C>
+// MX (MXFP8, OCP microscaling): instead of the per-row fp32 scales applied
+// in the epilogue, each 32-code block of A and B rows carries an E8M0 scale
+// that the scaled MFMA applies.  Each stage then also moves, by one 4-byte
+// DMA instruction per wave, the stage's 32-bit scale word of every A row and
+// every B row (blocks 4 kt .. 4 kt + 3 of the row), into MxWords after the
+// tiles; lanes past the BM + BN rows repeat row 0 of A into the padding.
+template <class C, bool MX>
 __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int tiles_m, int tiles_n, int group_m,
                                                                   int splits, float* partial, int ldp) {
     static_assert(C::DMA && C::CPR == 8, "fp8 tiles: LDS-DMA, 128-byte K step");
-    __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
+    constexpr int MX_WORDS = C::NW * 64;  // one 4-byte DMA lane per wave lane
+    static_assert(!MX || MX_WORDS >= C::BM + C::BN, "a scale word for every A and B row");
+    constexpr int EXTRA = MX ? MX_WORDS / 4 : 0;  // chunks of 16 B
+    __shared__ u32x4_t ring[C::STAGES * (C::STAGE_CHUNKS + EXTRA)];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -1050,6 +1121,18 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
     for (int j = 0; j < SB::N; ++j)
         b_ptr[j] = g.B + (int64_t)min(n0 + SB::row(j, tid), g.N - 1) * g.ldb + SB::lchunk(j, tid) * 16;
 
+    // MX: this lane's scale word source (row q of A, then of B, else A row 0)
+    const uint8_t* mx_src = nullptr;
+    if constexpr (MX) {
+        const int q = wave * 64 + lane;
+        const int64_t bpr = g.K / 32;  // scale bytes per row
+        if (q < C::BM)
+            mx_src = g.a_mx + (int64_t)min(m0 + q, g.M - 1) * bpr;
+        else if (q < C::BM + C::BN)
+            mx_src = g.b_mx + (int64_t)min(n0 + q - C::BM, g.N - 1) * bpr;
+        else
+            mx_src = g.a_mx + (int64_t)min(m0, g.M - 1) * bpr;
+    }
     auto fill = [&](int kt, u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
         const int kk = (kb + kt) * 128;
 #pragma unroll
@@ -1058,24 +1141,30 @@ __global__ __launch_bounds__(C::NT, C::MINB) void fp8_gemm_kernel(Fp8Gemm g, int
 #pragma unroll
         for (int j = 0; j < SB::N; ++j)
             if (SB::active(j, tid)) dma16<C::B_NT ? 2 : 0>(b_ptr[j] + kk, SB::dst(Bs, wave, j));
+        if constexpr (MX) {  // the stage's scale words sit right after its B tile
+            u32x4_t* words = As + C::STAGE_CHUNKS + wave * 16;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(mx_src + (kb + kt) * 4),
+                                             (__attribute__((address_space(3))) void*)words, 4, 0, 0);
+        }
     };
     auto land = [](u32x4_t*, u32x4_t*) {};
 
     f32x16_t acc[C::TM][C::TN];
     zero_acc<C>(acc);
-    kloop<C, SA::N + SB::N, true>(ke - kb, fill, land, ring, acc, wm, wn, lane);
+    kloop<C, SA::N + SB::N + (MX ? 1 : 0), MX ? 2 : 1, EXTRA>(ke - kb, fill, land, ring, acc, wm, wn, lane);
 
     static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
         constexpr int tm = decltype(tmc)::value;
         const int m = m0 + wm * C::WM + tm * 32 + (lane & 31);
         if (m < g.M) {
-            const float sa = g.a_scale[m];
+            const float sa = MX ? 1.0f : g.a_scale[m];
             uint16_t* crow = g.C + (int64_t)m * g.ldc;
             static_for<C::TN * 4>([&](auto tqc) __attribute__((always_inline)) {
                 constexpr int tn = decltype(tqc)::value / 4, q = decltype(tqc)::value % 4;
                 const int n = n0 + wn * C::WN + tn * 32 + q * 8 + (lane >> 5) * 4;
                 if (n < g.N) {  // N % 16 == 0: columns n..n+3 are all inside
-                    const float4 sb = *reinterpret_cast<const float4*>(g.b_scale + n);
+                    const float4 sb = MX ? make_float4(1.f, 1.f, 1.f, 1.f)
+                                         : *reinterpret_cast<const float4*>(g.b_scale + n);
                     float v[4] = {acc[tm][tn][q * 4 + 0] * sa * sb.x, acc[tm][tn][q * 4 + 1] * sa * sb.y,
                                   acc[tm][tn][q * 4 + 2] * sa * sb.z, acc[tm][tn][q * 4 + 3] * sa * sb.w};
                     if (partial) {  // ldp is a multiple of 4: one aligned float4
@@ -1190,6 +1279,66 @@ hipError_t launch_quantize_rows_fp8(const uint16_t* src, int64_t rows, int cols,
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     LMOE_LAUNCH("quantize_fp8", s,
                 quantize_rows_fp8_kernel<<<(unsigned)blocks, 256, 0, s>>>(src, rows, cols, ld, codes, scales));
+    return hipGetLastError();
+}
+
+// MXFP8 quantisation (OCP microscaling) of a bf16 matrix [rows][cols]
+// (cols a multiple of 32, row stride ld), one thread per block of 32
+// consecutive elements: e = floor(log2 max|v|) - 8 (8: the largest E4M3
+// exponent), clamped to [-127, 127] (0 for an all-zero block); the scale is
+// the E8M0 byte e + 127 and each code is E4M3 (nearest, ties to even) of
+// v * 2^-e saturated to +-448.  Scaling by a power of two is exact.
+__global__ __launch_bounds__(256) void quantize_blocks_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                                    int cols, int64_t ld,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    uint8_t* __restrict__ scales) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int bpr = cols / 32;
+    if (i >= rows * bpr) return;
+    const int64_t r = i / bpr;
+    const int b = (int)(i % bpr);
+    const uint16_t* p = src + r * ld + b * 32;
+    u32x4_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const u32x4_t*>(p + 8 * j);
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[j][h] & 0xFFFFu))));
+            amax = fmaxf(amax, fabsf(bf16_to_f32((uint16_t)(v[j][h] >> 16))));
+        }
+    // floor(log2 amax) from the exponent field (a subnormal amax reads -127
+    // and is clamped like every block below 2^-119)
+    int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 8 : 0;
+    e = min(max(e, -127), 127);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e: e <= 119 for finite bf16
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            auto q = [&](uint32_t bits) { return fminf(fmaxf(bf16_to_f32((uint16_t)bits) * inv, -448.f), 448.f); };
+            const uint32_t lo = v[j][2 * h], hi = v[j][2 * h + 1];
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(lo & 0xFFFFu), q(lo >> 16), 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(hi & 0xFFFFu), q(hi >> 16), pk, true);
+            w[2 * j + h] = (uint32_t)pk;
+        }
+    uint8_t* out = codes + r * (int64_t)cols + b * 32;
+    *reinterpret_cast<u32x4_t*>(out) = u32x4_t{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4_t*>(out + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+    scales[r * bpr + b] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_quantize_blocks_mxfp8(const uint16_t* src, int64_t rows, int cols, int64_t ld, uint8_t* codes,
+                                        uint8_t* scales, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (cols % 32 != 0) return hipErrorInvalidValue;
+    const int64_t blocks = (rows * (cols / 32) + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    LMOE_LAUNCH("quantize_mxfp8", s,
+                quantize_blocks_mxfp8_kernel<<<(unsigned)blocks, 256, 0, s>>>(src, rows, cols, ld, codes, scales));
     return hipGetLastError();
 }
 
@@ -1455,15 +1604,15 @@ hipError_t launch_dense_gemm_bf16(const DenseGemm& g, void* splitk_ws, size_t sp
 }
 // FP8 shared expert: 256x256 tiles (64x64 for decode-sized M), one tile per
 // block; N and K are the shared expert's (multiples of 64 and 128).
-template <class C>
+template <class C, bool MX>
 static hipError_t run_fp8(const Fp8Gemm& g, void* ws, size_t ws_bytes, hipStream_t s) {
     const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
     const int ldp = (g.N + 3) / 4 * 4;
     const int splits = splitk_factor(tiles_m * tiles_n, g.K / 128, g.M, ldp, ws_bytes, C::MINB);
     float* partial = splits > 1 ? (float*)ws : nullptr;
     LMOE_LAUNCH("fp8_gemm", s,
-                fp8_gemm_kernel<C><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
-                                                                               partial, ldp));
+                fp8_gemm_kernel<C, MX><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
+                                                                                   partial, ldp));
     if (splits > 1) {  // the reduction's epilogue: one column group writing g.C
         DenseGemm r{};
         r.M = g.M;
@@ -1480,9 +1629,13 @@ static hipError_t run_fp8(const Fp8Gemm& g, void* ws, size_t ws_bytes, hipStream
 hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s) {
     if (g.K % 128 != 0 || g.N % 16 != 0) return hipErrorInvalidValue;
     if (g.epi != EPI_STORE && g.epi != EPI_RELU2 && g.epi != EPI_ADD) return hipErrorInvalidValue;
+    const bool mx = g.a_mx != nullptr;
+    if (mx != (g.b_mx != nullptr)) return hipErrorInvalidValue;
+    using Few = MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>;
+    using Many = MfmaCfg<256, 256, 4, 2, true, 64, 2>;
     if (g.M <= 64)  // weight streaming: split-K over the partial-sum workspace
-        return run_fp8<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, splitk_ws, splitk_bytes, s);
-    return run_fp8<MfmaCfg<256, 256, 4, 2, true, 64, 2>>(g, nullptr, 0, s);
+        return mx ? run_fp8<Few, true>(g, splitk_ws, splitk_bytes, s) : run_fp8<Few, false>(g, splitk_ws, splitk_bytes, s);
+    return mx ? run_fp8<Many, true>(g, nullptr, 0, s) : run_fp8<Many, false>(g, nullptr, 0, s);
 }
 
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to

@@ -105,6 +105,10 @@ struct Fp8Gemm {
     int epi;
     uint16_t* C;
     int64_t ldc;
+    // MXFP8 instead of the per-row scales (both or neither): E8M0 scale bytes
+    // of each 32-code block along K, a_mx [M][K/32], b_mx [N][K/32]
+    const uint8_t* a_mx;
+    const uint8_t* b_mx;
 };
 // The decode-sized first dense GEMM (bf16, split along K) with the router's
 // top-k and gates taken in its reduction, from the logits columns
@@ -114,6 +118,11 @@ bool dense_topk_fusable(const DenseGemm& g, size_t splitk_bytes, int E, int k);
 hipError_t launch_dense_gemm_topk_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, int lc0, int E,
                                        const float* bias, int k, int32_t* idx, float* gate, hipStream_t s);
 hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s);
+
+// MXFP8 quantisation of a bf16 matrix [rows][cols] (cols % 32 == 0, row
+// stride ld): codes [rows][cols], E8M0 scales [rows][cols/32].
+hipError_t launch_quantize_blocks_mxfp8(const uint16_t* src, int64_t rows, int cols, int64_t ld, uint8_t* codes,
+                                        uint8_t* scales, hipStream_t s);
 
 // Per-row FP8 quantisation of a bf16 matrix [rows][cols] (row stride ld):
 // scale = max |v| / 448 (1 for an all-zero row), code = E4M3(v / scale),

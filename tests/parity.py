@@ -17,7 +17,7 @@
   max-norm relative error (max |gpu - ref| / max |ref|) against the
   tolerance of the activation format: 1e-5 fp32, 2e-2 bf16, 3e-2 NVFP4
   experts, 1-D or 2-D blocks (the oracle decodes the same NVFP4 bytes).
-* FP8 up-projection: out is checked twice.  Step-wise, against the oracle's
+* FP8 or MXFP8 up-projection: out is checked twice.  Step-wise, against the oracle's
   fp8 up-projection of the GPU's stored c (the same codes, so only the
   summation differs) within the activation tolerance; end to end, against
   the oracle from x within FP8_PROJ_OUT_TOL (see there).
@@ -221,21 +221,23 @@ def run_and_check(cfg, inp, n_sample: int = 1 << 30, lazy_experts: bool = False,
     errs["z"] = 0.0 if cfg.standard_moe else rel_err(to_f64(dbg["z"][tokens]), ref["z"])
     errs["c"] = rel_err(to_f64(dbg["c"][tokens]), ref["c"])
     errs["out"] = rel_err(to_f64(out[tokens]), ref["out"])
-    if cfg.proj_fp8:  # step-wise: the oracle's fp8 up-projection of the GPU's c as stored
+    proj8 = cfg.proj_fp8 or cfg.proj_mxfp8
+    if proj8:  # step-wise: the oracle's 8-bit up-projection of the GPU's c as stored
         step = O.project(to_f64(dbg["c"][tokens]), h, "W_up")
         if h.get("W_s1") is not None:
             step = step + O.shared_expert(h["x"][tokens], h)
         errs["out_from_gpu_c"] = rel_err(to_f64(out[tokens]), step)
         # share of c's E4M3 codes that differ between the two sides (reported)
-        qg, _ = O.quantize_rows_fp8(to_f64(dbg["c"][tokens]))
-        qo, _ = O.quantize_rows_fp8(O.round_to_bf16(ref["c"]))
+        quant = O.quantize_blocks_mxfp8 if cfg.proj_mxfp8 else O.quantize_rows_fp8
+        qg, _ = quant(to_f64(dbg["c"][tokens]))
+        qo, _ = quant(O.round_to_bf16(ref["c"]))
         errs["c_code_flips"] = float(np.mean(qg != qo))
     errs["tokens_checked"] = int(len(tokens))
     if report is not None:
         report(errs)
     assert errs["z"] <= zt, errs
     assert errs["c"] <= tol, errs
-    if cfg.proj_fp8:
+    if proj8:
         assert errs["out_from_gpu_c"] <= tol, errs
         assert errs["out"] <= FP8_PROJ_OUT_TOL, errs
     else:

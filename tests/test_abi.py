@@ -222,6 +222,33 @@ def test_fp8_projection_rules():
                              need - 1, None) == B.LMOE_ERR_WORKSPACE
 
 
+def test_mxfp8_projection_rules():
+    d = dims(proj_mxfp8=True)
+    assert d.proj_dtype == B.LMOE_MXFP8 and B.validate_dims(d) == B.LMOE_OK
+    f = B.dims_of(synth.CONFIGS["tiny_f32"])
+    f.proj_dtype = B.LMOE_MXFP8  # 8-bit projections need bf16 activations
+    assert B.validate_dims(f) == B.LMOE_ERR_DTYPE
+    assert B.validate_dims(dims(standard_moe=True, l=4096, proj_mxfp8=True)) == B.LMOE_ERR_DTYPE
+    assert B.validate_dims(dims(d=256, l=64, proj_mxfp8=True)) == B.LMOE_ERR_SHAPE
+    good = B.Fp8Matrix(FAKE, FAKE)
+    bad = B.Fp8Matrix(FAKE, MIS)
+    pg = ctypes.cast(ctypes.pointer(good), ctypes.c_void_p)
+    pb = ctypes.cast(ctypes.pointer(bad), ctypes.c_void_p)
+    assert _forward(d, W_down=pg, W_up=pg) == B.LMOE_ERR_WORKSPACE
+    assert _forward(d, W_down=pg, W_up=pb) == B.LMOE_ERR_ALIGN
+    L = B.lib()
+    assert L.lmoe_workspace_bytes(ctypes.byref(d)) > L.lmoe_workspace_bytes(ctypes.byref(dims()))
+
+
+def test_quantize_rows_mxfp8_error_paths():
+    L = B.lib()
+    assert L.lmoe_quantize_rows_mxfp8(0, 64, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_quantize_rows_mxfp8(4, 48, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE  # not a multiple of 32
+    assert L.lmoe_quantize_rows_mxfp8(4, 1 << 21, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE
+    assert L.lmoe_quantize_rows_mxfp8(4, 64, FAKE, None, FAKE, None) == B.LMOE_ERR_NULL
+    assert L.lmoe_quantize_rows_mxfp8(4, 64, FAKE, FAKE, MIS, None) == B.LMOE_ERR_ALIGN
+
+
 def test_quantize_rows_error_paths():
     L = B.lib()
     assert L.lmoe_quantize_rows_fp8(0, 64, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE

@@ -33,6 +33,8 @@ CASES = {
     "f32_ragged": TINY.with_(name="f32_ragged", T=77, d=256, l=64, E=9, k=3, f=192, f_s=128),
     "nvfp4_2d_few_wide": TINY.with_(name="nvfp4_2d_few_wide", T=16, d=4096, l=1024, E=16, k=2, f=1280, f_s=0,
                                     act="bf16", experts="nvfp4_2d"),
+    "mxfp8_proj_few": TINY.with_(name="mxfp8_proj_few", T=20, d=1024, l=256, E=8, k=2, f=128, f_s=256,
+                                 act="bf16", experts="nvfp4", proj_mxfp8=True, shared_fp8=True, router_latent=True),
     # split-K fp8 GEMMs (fp8 projections and shared expert at few rows)
     "fp8_proj_few": TINY.with_(name="fp8_proj_few", T=20, d=1024, l=256, E=8, k=2, f=128, f_s=256,
                                act="bf16", experts="nvfp4", proj_fp8=True, shared_fp8=True, router_latent=True),

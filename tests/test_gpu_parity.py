@@ -86,6 +86,14 @@ SMALL = {
                                 act="bf16", experts="nvfp4_2d"),
     "nvfp4_2d_few_wide": TINY.with_(name="nvfp4_2d_few_wide", T=16, d=4096, l=1024, E=16, k=2, f=1280, f_s=0,
                                     act="bf16", experts="nvfp4_2d"),
+    # MXFP8 projections (E4M3 with E8M0 scales per 32 elements, applied by
+    # the scaled MFMA): many rows, few rows (split-K), skewed routing
+    "mxfp8_proj": TINY.with_(name="mxfp8_proj", T=150, d=512, l=128, E=16, k=3, f=192, f_s=128,
+                             act="bf16", experts="bf16", proj_mxfp8=True),
+    "mxfp8_proj_few": TINY.with_(name="mxfp8_proj_few", T=20, d=1024, l=256, E=8, k=2, f=128, f_s=256,
+                                 act="bf16", experts="nvfp4", proj_mxfp8=True, shared_fp8=True, router_latent=True),
+    "mxfp8_proj_zipf": TINY.with_(name="mxfp8_proj_zipf", T=64, d=2048, l=512, E=64, k=6, f=256, f_s=0,
+                                  act="bf16", experts="bf16", proj_mxfp8=True, zipf_bias=True),
     "E1_f32": TINY.with_(name="E1_f32", T=33, E=1, k=1),
     "E1_bf16": TINY.with_(name="E1_bf16", T=150, E=1, k=1, act="bf16", experts="bf16", f_s=64),
 }
@@ -156,7 +164,7 @@ def test_exact_logit_ties_break_to_lower_id(T, d):
 
 def test_staged_entry_points_compose_to_forward():
     for name in ("bf16_deep", "nvfp4_sparse", "f32_ragged", "few_rows_wide", "latent_bf16", "fp8_shared",
-                 "standard_bf16", "fp8_proj", "fp8_proj_few"):
+                 "standard_bf16", "fp8_proj", "fp8_proj_few", "mxfp8_proj", "mxfp8_proj_few"):
         cfg = SMALL[name]
         log(f"case staged {name}")
         inp = small_inputs(cfg)
@@ -246,6 +254,39 @@ def test_quantize_rows_fp8_matches_oracle(rows, cols):
     codes, scales = B.quantize_rows_fp8(src.cuda())
     torch.cuda.synchronize()
     rc, rs = O.quantize_rows_fp8(O.as_f64(synth.host_view(src)))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("name", ["mxfp8_proj", "mxfp8_proj_few"])
+def test_mxfp8_projections_with_varied_block_scales(name):
+    # x scaled per 32-element block by 2^-6 .. 2^6 (exact in bf16), so
+    # neighbouring blocks of every row carry different E8M0 scales and a
+    # scale applied to the wrong block of the MFMA shows
+    cfg = SMALL[name]
+    inp = small_inputs(cfg)
+    g = torch.Generator().manual_seed(23)
+    f = torch.exp2(torch.randint(-6, 7, (cfg.T, cfg.d // 32), generator=g).float()).repeat_interleave(32, dim=1)
+    inp["x"] = (inp["x"].float().cpu() * f).to(torch.bfloat16).cuda()
+    log(f"case {name} with varied block scales")
+    P.run_and_check(cfg, inp, report=log)
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 1024), (1100, 256)])
+def test_quantize_rows_mxfp8_matches_oracle(rows, cols):
+    # blocks of very different magnitudes (2^-40 .. 2^40), an all-zero
+    # block, a saturating block and values near the E4M3 subnormal range
+    g = torch.Generator().manual_seed(17)
+    v = torch.randn(rows, cols, generator=g)
+    v = v * torch.exp2(torch.randint(-40, 40, (rows, cols // 32), generator=g).float()).repeat_interleave(32, dim=1)
+    v[2, 32:64] = 0.0
+    v[3, :32] = torch.linspace(-1, 1, 32) * 0.99
+    v[3, 7] = 1.97  # 1.97 * 2^8 = 504: saturates to 448
+    v[5, :32] *= 1e-3
+    src = v.to(torch.bfloat16)
+    codes, scales = B.quantize_rows_mxfp8(src.cuda())
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_blocks_mxfp8(O.as_f64(synth.host_view(src)))
     assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(codes.cpu().numpy(), rc)
 
@@ -367,6 +408,23 @@ def test_decode_fp8_projections_full_size():
 @pytest.mark.timeout(900)
 def test_prefill_fp8_projections_sampled():
     cfg = CFG["prefill_bf16"].with_(name="prefill_fp8_proj", T=2048, proj_fp8=True, shared_fp8=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    P.run_and_check(cfg, inp, n_sample=12, lazy_experts=True, report=log)
+
+
+@pytest.mark.timeout(900)
+def test_decode_mxfp8_projections_full_size():
+    cfg = CFG["decode_bf16_zipf"].with_(name="decode_mxfp8_proj", proj_mxfp8=True)
+    log(f"case {cfg}")
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    errs, _, dbg = P.run_and_check(cfg, inp, lazy_experts=True, report=log)
+    assert int(dbg["counts"].cpu()[0]) == cfg.T
+
+
+@pytest.mark.timeout(900)
+def test_prefill_mxfp8_projections_sampled():
+    cfg = CFG["prefill_bf16"].with_(name="prefill_mxfp8_proj", T=2048, proj_mxfp8=True, shared_fp8=True)
     log(f"case {cfg}")
     inp = synth.make_inputs(cfg, 0, "cuda")
     P.run_and_check(cfg, inp, n_sample=12, lazy_experts=True, report=log)
