@@ -282,6 +282,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replays (profiling runs: every launch is then an eager one)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (NVFP4 and mid prefill, latent router)")
     ap.add_argument("--expert-layout", choices=("tiled", "rowmajor"), default="tiled",
@@ -314,7 +316,7 @@ def main():
     B.lib()
     cfg = synth.CONFIGS[args.workload]
     inp, out, ms, wall, kernels, graph = prefill(cfg, args.steps, args.warmup, torch, B, synth,
-                                                 args.expert_layout, graph=True)
+                                                 args.expert_layout, graph=not args.no_graph)
     tokens_per_s = cfg.T / (ms * 1e-3)
     layer_tflops = cfg.flops / (ms * 1e-3) / 1e12
 
@@ -359,7 +361,7 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = decode(synth.CONFIGS["decode_bf16_zipf"], args.decode_steps, torch, B, synth,
-                                  args.expert_layout, graph=True)
+                                  args.expert_layout, graph=not args.no_graph)
     if not args.no_extra:
         C = synth.CONFIGS
         extra = [C[n] for n in ("prefill_nvfp4", "mid_bf16") if n != args.workload]
