@@ -24,6 +24,9 @@ CASES = {
     # 64x256 expert tiles with split-K items finished by the last block
     "few_rows_wide": TINY.with_(name="few_rows_wide", T=24, d=4096, l=1024, E=32, k=4, f=1280, f_s=0,
                                 act="bf16", experts="bf16"),
+    # full rounds of expert items, then tail items split along K
+    "few_rows_rounds": TINY.with_(name="few_rows_rounds", T=64, d=5120, l=1280, E=64, k=8, f=2304, f_s=0,
+                                    act="bf16", experts="bf16"),
     "latent_nvfp4_zipf": TINY.with_(name="latent_nvfp4_zipf", T=40, d=256, l=64, E=32, k=5, f=128, f_s=0,
                                     act="bf16", experts="nvfp4", zipf_bias=True, router_latent=True),
     "fp8_shared": TINY.with_(name="fp8_shared", T=150, d=512, l=128, E=16, k=3, f=192, f_s=256,

@@ -46,6 +46,11 @@ SMALL = {
     # N = 1280 not a multiple of 256
     "few_rows_wide": TINY.with_(name="few_rows_wide", T=24, d=4096, l=1024, E=32, k=4, f=1280, f_s=0,
                                 act="bf16", experts="bf16"),
+    # more 64 x 256 expert items than blocks, not in whole rounds (576 items
+    # in GEMM1, 320 in GEMM2 over 256 blocks): full rounds, then the tail
+    # items split along K
+    "few_rows_rounds": TINY.with_(name="few_rows_rounds", T=64, d=5120, l=1280, E=64, k=8, f=2304, f_s=0,
+                                    act="bf16", experts="bf16"),
     "nvfp4_few_wide": TINY.with_(name="nvfp4_few_wide", T=16, d=4096, l=1024, E=16, k=2, f=1280, f_s=0,
                                  act="bf16", experts="nvfp4"),
     # top-k beyond one register slot per lane: k = 100 of E = 256, and E = 1024
@@ -179,7 +184,7 @@ def test_staged_entry_points_compose_to_forward():
         assert torch.equal(o["out"], fused), name
 
 
-@pytest.mark.parametrize("name", ["bf16_deep", "few_rows_wide"])
+@pytest.mark.parametrize("name", ["bf16_deep", "few_rows_wide", "few_rows_rounds"])
 def test_repeated_runs_are_bit_identical(name):
     # few_rows_wide: expert GEMMs with split-K items, whose partial sums are
     # added by whichever block finishes last
