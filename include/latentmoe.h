@@ -225,6 +225,42 @@ const char* lmoe_strerror(int status);
 /* hipError_t of the last failed launch in this thread (0 if none). */
 int lmoe_last_hip_error(void);
 
+/* ---- optional context: a workspace the library owns ------------------ */
+
+/*
+ * For callers that would rather not manage the workspace.  A context holds
+ * one device buffer, grown by lmoe_ctx_reserve (hipMalloc, outside any
+ * forward call) and used by lmoe_ctx_forward, which never allocates.  One
+ * context per stream; a context is not thread-safe.
+ */
+typedef struct lmoe_ctx lmoe_ctx;
+
+/* *ctx = a new context for device `device` (the device must exist;
+ * LMOE_ERR_HIP otherwise, LMOE_ERR_NULL for ctx == NULL).  No device memory
+ * is allocated yet. */
+int lmoe_create(lmoe_ctx** ctx, int device);
+
+/* Frees the context and its workspace (the device must be idle for it);
+ * NULL is a no-op. */
+int lmoe_destroy(lmoe_ctx* ctx);
+
+/* Grows the context's workspace to lmoe_workspace_bytes(dims) if it is
+ * smaller, on the context's device.  Validation errors as for
+ * lmoe_validate_dims; LMOE_ERR_HIP if the allocation fails. */
+int lmoe_ctx_reserve(lmoe_ctx* ctx, const lmoe_dims* dims);
+
+/* Bytes of the context's workspace (0 before the first reserve). */
+size_t lmoe_ctx_workspace_bytes(const lmoe_ctx* ctx);
+
+/* latentmoe_forward on the context's workspace.  LMOE_ERR_WORKSPACE if the
+ * context was not reserved for dims; LMOE_ERR_HIP if the caller's current
+ * device is not the context's (nothing is launched then). */
+int lmoe_ctx_forward(lmoe_ctx* ctx, const lmoe_dims* dims, const void* x, const void* W_down,
+                     const void* W_router, const float* router_bias,
+                     const lmoe_experts* experts, const void* W_up,
+                     const lmoe_shared* shared, int k, void* out,
+                     const lmoe_debug* dbg, void* stream);
+
 /* ---- per-kernel timing (optional) ------------------------------------ */
 
 /* One timed kernel launch: the kernel's name and its duration between two

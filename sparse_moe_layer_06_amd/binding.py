@@ -31,7 +31,8 @@ DTYPE_CODE = {"f32": LMOE_F32, "bf16": LMOE_BF16, "nvfp4": LMOE_NVFP4, "bf16_til
 EXPORTED = ["lmoe_workspace_bytes", "lmoe_validate_dims", "lmoe_strerror", "lmoe_last_hip_error",
             "latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
             "lmoe_combine_up", "lmoe_timing_start", "lmoe_timing_stop", "lmoe_pack_expert_weights",
-            "lmoe_quantize_rows_fp8", "lmoe_quantize_rows_mxfp8"]
+            "lmoe_quantize_rows_fp8", "lmoe_quantize_rows_mxfp8", "lmoe_create", "lmoe_destroy",
+            "lmoe_ctx_reserve", "lmoe_ctx_workspace_bytes", "lmoe_ctx_forward"]
 
 
 class Dims(ctypes.Structure):
@@ -112,6 +113,13 @@ def lib() -> ctypes.CDLL:
         L.lmoe_pack_expert_weights.restype = ctypes.c_int
         L.lmoe_quantize_rows_fp8.argtypes = [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, vp]
         L.lmoe_quantize_rows_mxfp8.argtypes = [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, vp]
+        L.lmoe_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int]
+        L.lmoe_destroy.argtypes = [vp]
+        L.lmoe_ctx_reserve.argtypes = [vp, pd]
+        L.lmoe_ctx_workspace_bytes.argtypes = [vp]
+        L.lmoe_ctx_workspace_bytes.restype = sz
+        L.lmoe_ctx_forward.argtypes = [vp, pd, vp, vp, vp, vp, ctypes.POINTER(Experts), vp,
+                                       ctypes.POINTER(Shared), ctypes.c_int, vp, ctypes.POINTER(Debug), vp]
         L.lmoe_quantize_rows_fp8.restype = ctypes.c_int
         for n in ("latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
                   "lmoe_combine_up"):
@@ -230,6 +238,37 @@ def _byref_opt(s):
 
 def act_dtype(cfg: LayerDims) -> torch.dtype:
     return torch.bfloat16 if cfg.act == "bf16" else torch.float32
+
+
+class Context:
+    """An lmoe_ctx: a workspace the library owns (grown by reserve, outside
+    any forward call)."""
+
+    def __init__(self, device: int = 0):
+        self.h = ctypes.c_void_p()
+        _check(lib().lmoe_create(ctypes.byref(self.h), device), "lmoe_create")
+
+    def reserve(self, cfg: LayerDims, T: Optional[int] = None):
+        d = dims_of(cfg, T)
+        _check(lib().lmoe_ctx_reserve(self.h, ctypes.byref(d)), "lmoe_ctx_reserve")
+
+    def workspace_bytes(self) -> int:
+        return int(lib().lmoe_ctx_workspace_bytes(self.h))
+
+    def forward(self, cfg: LayerDims, inp, out: torch.Tensor, debug=None, stream=None) -> torch.Tensor:
+        d = dims_of(cfg, inp["x"].shape[0])
+        ex, sh = experts_struct(inp), shared_struct(inp)
+        wd, wu = _Proj(cfg, inp, "W_down"), _Proj(cfg, inp, "W_up")
+        dbg = Debug(**{n: _p(debug.get(n)) for n, _ in Debug._fields_}) if debug else None
+        _check(lib().lmoe_ctx_forward(self.h, ctypes.byref(d), _p(inp["x"]), wd.arg, _p(inp["W_r"]),
+                                      _p(inp.get("b_r")), ctypes.byref(ex), wu.arg, _byref_opt(sh), cfg.k,
+                                      _p(out), _byref_opt(dbg), _stream(stream)), "lmoe_ctx_forward")
+        return out
+
+    def close(self):
+        if self.h:
+            _check(lib().lmoe_destroy(self.h), "lmoe_destroy")
+            self.h = ctypes.c_void_p()
 
 
 def quantize_rows_mxfp8(src: torch.Tensor, stream=None):

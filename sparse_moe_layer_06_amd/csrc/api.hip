@@ -16,6 +16,8 @@
 // fp8 GEMMs of their own, each after a per-token quantisation of its input.
 #include <string.h>
 
+#include <new>
+
 #include "lmoe_internal.hpp"
 
 namespace lmoe {
@@ -666,6 +668,70 @@ int lmoe_combine_up(const lmoe_dims* dims, const void* Y, const int32_t* inv, co
     char* ws = (char*)workspace;
     const Layout L = plan(d);
     return hip_status(run_combine_up(d, Y, inv, topk_gate, W_up, shared, hs, c, out, ws, L, (hipStream_t)stream));
+}
+
+struct lmoe_ctx {
+    int device;
+    void* ws;
+    size_t bytes;
+};
+
+int lmoe_create(lmoe_ctx** ctx, int device) {
+    if (!ctx) return LMOE_ERR_NULL;
+    *ctx = nullptr;
+    int count = 0;
+    const hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess) return hip_status(e);
+    if (device < 0 || device >= count) return hip_status(hipErrorInvalidDevice);
+    lmoe_ctx* c = new (std::nothrow) lmoe_ctx{device, nullptr, 0};
+    if (!c) return hip_status(hipErrorOutOfMemory);
+    *ctx = c;
+    return LMOE_OK;
+}
+
+int lmoe_destroy(lmoe_ctx* ctx) {
+    if (!ctx) return LMOE_OK;
+    hipError_t e = hipSuccess;
+    if (ctx->ws) e = hipFree(ctx->ws);
+    delete ctx;
+    return hip_status(e);
+}
+
+int lmoe_ctx_reserve(lmoe_ctx* ctx, const lmoe_dims* dims) {
+    if (!ctx) return LMOE_ERR_NULL;
+    LMOE_TRY(lmoe_validate_dims(dims));
+    const size_t need = plan(*dims).total;
+    if (need <= ctx->bytes) return LMOE_OK;
+    int prev = 0;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != ctx->device) e = hipSetDevice(ctx->device);
+    if (e == hipSuccess && ctx->ws) {
+        e = hipFree(ctx->ws);
+        ctx->ws = nullptr;
+        ctx->bytes = 0;
+    }
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipMalloc(&p, need);
+    if (e == hipSuccess) {
+        ctx->ws = p;
+        ctx->bytes = need;
+    }
+    if (prev != ctx->device) (void)hipSetDevice(prev);
+    return hip_status(e);
+}
+
+size_t lmoe_ctx_workspace_bytes(const lmoe_ctx* ctx) { return ctx ? ctx->bytes : 0; }
+
+int lmoe_ctx_forward(lmoe_ctx* ctx, const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,
+                     const float* router_bias, const lmoe_experts* experts, const void* W_up,
+                     const lmoe_shared* shared, int k, void* out, const lmoe_debug* dbg, void* stream) {
+    if (!ctx) return LMOE_ERR_NULL;
+    int cur = -1;
+    const hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (cur != ctx->device) return hip_status(hipErrorInvalidDevice);
+    return latentmoe_forward(dims, x, W_down, W_router, router_bias, experts, W_up, shared, k, out, ctx->ws,
+                             ctx->bytes, dbg, stream);
 }
 
 }  // extern "C"

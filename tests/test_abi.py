@@ -256,3 +256,19 @@ def test_quantize_rows_error_paths():
     assert L.lmoe_quantize_rows_fp8(4, 1 << 21, FAKE, FAKE, FAKE, None) == B.LMOE_ERR_SHAPE
     assert L.lmoe_quantize_rows_fp8(4, 64, None, FAKE, FAKE, None) == B.LMOE_ERR_NULL
     assert L.lmoe_quantize_rows_fp8(4, 64, FAKE, FAKE, MIS, None) == B.LMOE_ERR_ALIGN
+
+
+def test_context_error_paths():
+    # host-side argument checks; creating a context needs the device to exist
+    # (on a machine without one, or for device -1, LMOE_ERR_HIP)
+    L = B.lib()
+    assert L.lmoe_create(None, 0) == B.LMOE_ERR_NULL
+    assert L.lmoe_destroy(None) == B.LMOE_OK
+    assert L.lmoe_ctx_reserve(None, ctypes.byref(dims())) == B.LMOE_ERR_NULL
+    assert L.lmoe_ctx_workspace_bytes(None) == 0
+    h = ctypes.c_void_p()
+    assert L.lmoe_create(ctypes.byref(h), -1) == B.LMOE_ERR_HIP and not h.value
+    ex = B.Experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    d = dims()
+    assert L.lmoe_ctx_forward(None, ctypes.byref(d), FAKE, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, d.k,
+                              FAKE, None, None) == B.LMOE_ERR_NULL

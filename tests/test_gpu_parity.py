@@ -198,6 +198,32 @@ def test_repeated_runs_are_bit_identical(name):
         assert torch.equal(a, b)
 
 
+def test_context_owned_workspace():
+    # the optional context: reserved for 8 tokens it refuses a 500-token call
+    # (it never allocates in the forward), reserved again it grows and gives
+    # the same bytes as a caller-provided workspace; it does not shrink
+    cfg = SMALL["bf16_deep"]
+    inp = small_inputs(cfg)
+    ref = B.forward(cfg, inp).clone()
+    ctx = B.Context(0)
+    try:
+        ctx.reserve(cfg, 8)
+        small = ctx.workspace_bytes()
+        out = torch.empty_like(ref)
+        with pytest.raises(B.LatentMoEError):
+            ctx.forward(cfg, inp, out)
+        ctx.reserve(cfg)
+        assert ctx.workspace_bytes() > small
+        ctx.forward(cfg, inp, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        big = ctx.workspace_bytes()
+        ctx.reserve(cfg, 8)
+        assert ctx.workspace_bytes() == big
+    finally:
+        ctx.close()
+
+
 def test_invalid_expert_ids_are_left_out_of_the_permutation():
     cfg = SMALL["bf16_ragged"]
     ws = B.alloc_workspace(cfg)
