@@ -257,11 +257,12 @@ def test_permutation_matches_oracle_on_both_paths(T, k, E):
     assert np.array_equal(p["inv"].cpu().numpy(), ri)
 
 
-@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "few_rows_wide", "k100_E256",
-                                  "E1_bf16"])
+@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "few_rows_wide", "few_rows_rounds",
+                                  "k100_E256", "E1_bf16"])
 def test_tiled_expert_weights(name):
     # the packed layout holds the same values: outputs bit-identical to the
     # row-major stacks, and the oracle (row-major weights) agrees
+    # (few_rows_wide, few_rows_rounds: 64 x 256 tiles with the split tail)
     cfg = SMALL[name]
     log(f"case tiled {name}")
     inp = small_inputs(cfg)
