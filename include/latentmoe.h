@@ -245,8 +245,10 @@ int lmoe_create(lmoe_ctx** ctx, int device);
 int lmoe_destroy(lmoe_ctx* ctx);
 
 /* Grows the context's workspace to lmoe_workspace_bytes(dims) if it is
- * smaller, on the context's device.  Validation errors as for
- * lmoe_validate_dims; LMOE_ERR_HIP if the allocation fails. */
+ * smaller, on the context's device (the old buffer is freed after the new
+ * one is allocated; hipFree waits for the device).  Validation errors as
+ * for lmoe_validate_dims; LMOE_ERR_HIP if the allocation fails, and the
+ * context then keeps its previous workspace. */
 int lmoe_ctx_reserve(lmoe_ctx* ctx, const lmoe_dims* dims);
 
 /* Bytes of the context's workspace (0 before the first reserve). */

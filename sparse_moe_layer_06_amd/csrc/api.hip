@@ -702,21 +702,19 @@ int lmoe_ctx_reserve(lmoe_ctx* ctx, const lmoe_dims* dims) {
     LMOE_TRY(lmoe_validate_dims(dims));
     const size_t need = plan(*dims).total;
     if (need <= ctx->bytes) return LMOE_OK;
+    // the new buffer first: if it cannot be had, the context keeps the old one
     int prev = 0;
     hipError_t e = hipGetDevice(&prev);
-    if (e == hipSuccess && prev != ctx->device) e = hipSetDevice(ctx->device);
-    if (e == hipSuccess && ctx->ws) {
-        e = hipFree(ctx->ws);
-        ctx->ws = nullptr;
-        ctx->bytes = 0;
-    }
+    const bool other = e == hipSuccess && prev != ctx->device;
+    if (other) e = hipSetDevice(ctx->device);
     void* p = nullptr;
     if (e == hipSuccess) e = hipMalloc(&p, need);
     if (e == hipSuccess) {
+        if (ctx->ws) e = hipFree(ctx->ws);
         ctx->ws = p;
         ctx->bytes = need;
     }
-    if (prev != ctx->device) (void)hipSetDevice(prev);
+    if (other) (void)hipSetDevice(prev);
     return hip_status(e);
 }
 
