@@ -270,6 +270,12 @@ class Context:
             _check(lib().lmoe_destroy(self.h), "lmoe_destroy")
             self.h = ctypes.c_void_p()
 
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
 
 def quantize_rows_mxfp8(src: torch.Tensor, stream=None):
     """(codes uint8 [rows][cols], E8M0 scales uint8 [rows][cols/32]) of a

@@ -205,8 +205,7 @@ def test_context_owned_workspace():
     cfg = SMALL["bf16_deep"]
     inp = small_inputs(cfg)
     ref = B.forward(cfg, inp).clone()
-    ctx = B.Context(0)
-    try:
+    with B.Context(0) as ctx:
         ctx.reserve(cfg, 8)
         small = ctx.workspace_bytes()
         out = torch.empty_like(ref)
@@ -220,8 +219,7 @@ def test_context_owned_workspace():
         big = ctx.workspace_bytes()
         ctx.reserve(cfg, 8)
         assert ctx.workspace_bytes() == big
-    finally:
-        ctx.close()
+    assert not ctx.h  # closed on leaving the block
 
 
 def test_invalid_expert_ids_are_left_out_of_the_permutation():
