@@ -584,15 +584,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseGemm g, int spl
     }
 }
 
-// The decode-sized first GEMM's reduction with the router folded in: one
-// block per token row sums the row's split partials in split order and
-// stores them through the column groups' epilogues, as splitk_reduce_kernel
-// does, and keeps the row's logits (columns [lc0, lc0 + E), bias added: the
-// values the logits epilogue stores) in LDS; its first wave then selects the
-// token's top-k and gates from there, as the router kernel does from the
-// stored logits.  This saves the router kernel's launch and its re-read.
-// 1024 threads, so a decode row's 2560 columns take one pass of float4
-// chunks, with up to 16 splits' loads in flight per thread.
+// The decode-sized first GEMM's reduction with the router folded in.  Two
+// blocks per token row sum the row's split partials in split order and
+// store them through the column groups' epilogues, as splitk_reduce_kernel
+// does: block m < M the float4 chunks holding the logits (columns [lc0,
+// lc0 + E)), block M + m the other columns, so that the first finishes its
+// loads early.  Block m keeps the row's logits (bias added: the values the
+// logits epilogue stores) in LDS; its first wave then selects the token's
+// top-k and gates from there, as the router kernel does from the stored
+// logits.  This saves the router kernel's launch and its re-read.  1024
+// threads, so each part of a decode row takes one pass of float4 chunks,
+// with up to 16 splits' loads in flight per thread.
 template <int S>
 __global__ __launch_bounds__(1024) void splitk_reduce_topk_kernel(DenseGemm g, int splits,
                                                                  const float* __restrict__ partial, int ldp,
@@ -601,8 +603,11 @@ __global__ __launch_bounds__(1024) void splitk_reduce_topk_kernel(DenseGemm g, i
                                                                  float* __restrict__ gate) {
     __shared__ float s_l[S * kWave];
     __shared__ uint64_t by_id[kWave], by_rank[kWave];
-    const int m = blockIdx.x;
-    for (int n = threadIdx.x * 4; n < g.N; n += 1024 * 4) {
+    const bool sel = (int)blockIdx.x < g.M;  // this block selects the row's top-k
+    const int m = sel ? blockIdx.x : blockIdx.x - g.M;
+    const int lo = lc0 & ~3, hi = lc0 + E;  // float4 chunks starting in [lo, hi) hold logits
+    for (int n = (sel ? lo : 0) + threadIdx.x * 4; n < (sel ? hi : g.N); n += 1024 * 4) {
+        if (!sel && n >= lo && n < hi) continue;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         constexpr int kBatch = 16;
         for (int sp0 = 0; sp0 < splits; sp0 += kBatch) {
@@ -631,6 +636,7 @@ __global__ __launch_bounds__(1024) void splitk_reduce_topk_kernel(DenseGemm g, i
             if (e >= 0 && e < E) s_l[e] = v[c] + (bias ? bias[e] : 0.f);
         }
     }
+    if (!sel) return;
     __syncthreads();
     if (threadIdx.x < kWave) topk_select_row<S>(s_l, E, k, m, by_id, by_rank, idx, gate);
 }
@@ -1564,8 +1570,8 @@ hipError_t launch_dense_gemm_topk_bf16(const DenseGemm& g, void* splitk_ws, size
                                                                                   partial, ldp));
 #define LMOE_REDUCE_TOPK(S_)                                                                                  \
     LMOE_LAUNCH("splitk_reduce_topk", s,                                                                      \
-                splitk_reduce_topk_kernel<S_><<<g.M, 1024, 0, s>>>(g, splits, partial, ldp, lc0, E, bias, k, idx, \
-                                                                 gate))
+                splitk_reduce_topk_kernel<S_><<<2 * g.M, 1024, 0, s>>>(g, splits, partial, ldp, lc0, E, bias, k, \
+                                                                     idx, gate))
     if (E <= 64)
         LMOE_REDUCE_TOPK(1);
     else if (E <= 128)
