@@ -213,13 +213,18 @@ def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, tensor_scale: float) ->
     """w[r][c] = E2M1(code[r][c]) * E4M3(scale[r][c // 16]) * tensor_scale,
     or with 2-D blocks (one scale per 16 rows x 16 columns, scales
     [R/16][K/16]; the Ultra release news describes the pretrained weights as
-    quantised in two-dimensional blocks) E4M3(scale[r // 16][c // 16])."""
+    quantised in two-dimensional blocks) E4M3(scale[r // 16][c // 16]).
+    The codes and scale bytes are decoded through tables of e2m1_value over
+    the 16 codes and e4m3_value over the 256 bytes: the same values, looked
+    up instead of recomputed per element."""
     codes = np.asarray(codes)
     scales = np.asarray(scales)
+    e2m1_table = e2m1_value(np.arange(16))
+    e4m3_table = e4m3_value(np.arange(256))
     q = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.float64)
-    q[..., 0::2] = e2m1_value(codes & 0x0F)
-    q[..., 1::2] = e2m1_value(codes >> 4)
-    s = np.repeat(e4m3_value(scales), 16, axis=-1)
+    q[..., 0::2] = e2m1_table[codes & 0x0F]
+    q[..., 1::2] = e2m1_table[codes >> 4]
+    s = np.repeat(e4m3_table[scales], 16, axis=-1)
     if scales.shape[-2] != codes.shape[-2]:
         if scales.shape[-2] * 16 != codes.shape[-2]:
             raise ValueError("block scales neither per row nor per 16 rows")
@@ -357,13 +362,18 @@ def route(inp: dict, k: int):
     return s, idx, gate_weights(s, idx)
 
 
-def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> dict:
+def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None, idx=None) -> dict:
     """The layer forward for the given token rows (all rows by default).
 
     Returns float64 z [n][l], c [n][l], out [n][d], and the routing of those
     rows: logits (float32) [n][E], idx [n][k], gate [n][k].  Tokens are
     independent (no capacity limit, every routed pair is computed), so any
     subset of rows gives the same values as the full call for those rows.
+
+    idx, if given ([n][k] expert ids of those rows), replaces the top-k
+    selection of step 3: the rows are evaluated with those experts, gated by
+    the softmax over their own logits (step 4).  This evaluates a row with
+    another valid selection of its top-k where logits tie or nearly tie.
     """
     x = np.asarray(inp["x"])
     if tokens is not None:
@@ -372,7 +382,7 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
     # a standard MoE (no W_down / W_up, experts in d) routes and computes on x
     z = project(x, inp, "W_down") if inp.get("W_down") is not None else as_f64(x)
     s = router_logits(router_input(x, inp), inp["W_r"], inp.get("b_r"))
-    idx = select_topk(s, k)
+    idx = select_topk(s, k) if idx is None else np.asarray(idx, dtype=np.int32).reshape(len(x), k)
     g = gate_weights(s, idx)
     n, l = z.shape
     c = np.zeros((n, l), dtype=np.float64)
@@ -380,15 +390,45 @@ def forward(inp: dict, k: int, tokens=None, experts: ExpertWeights = None) -> di
         for j in range(k):
             W1_e, W2_e = experts(idx[t, j])
             c[t] += g[t, j] * expert_ffn(z[t], W1_e, W2_e)
+    return dict(z=z, logits=s, idx=idx, gate=g, c=c, out=up_project(c, x, inp))
+
+
+def forward_batched(inp: dict, k: int, idx=None, experts: ExpertWeights = None) -> dict:
+    """forward() for every token, with step 5 taken one expert at a time over
+    all the rows routed to it: H = max(0, Z_e W1_e^T)^2 and Y = H W2_e^T for
+    the stacked latent rows Z_e of that expert's tokens, then each row added
+    into its token's c with its gate.  The same arithmetic as forward(),
+    grouped by expert instead of by token (a token holds each expert at
+    most once), so only the order of the float64 additions into c differs.
+    idx, if given ([T][k]), replaces the top-k selection as in forward()."""
+    x = np.asarray(inp["x"])
+    experts = experts or ExpertWeights(inp, cache_size=1)
+    z = project(x, inp, "W_down") if inp.get("W_down") is not None else as_f64(x)
+    s = router_logits(router_input(x, inp), inp["W_r"], inp.get("b_r"))
+    idx = select_topk(s, k) if idx is None else np.asarray(idx, dtype=np.int32).reshape(len(x), k)
+    g = gate_weights(s, idx)
+    c = np.zeros(z.shape, dtype=np.float64)
+    for e in np.unique(idx):
+        t, j = np.nonzero(idx == e)
+        W1_e, W2_e = experts(e)
+        H = np.maximum(z[t] @ W1_e.T, 0.0) ** 2
+        c[t] += g[t, j][:, None] * (H @ W2_e.T)
+    return dict(z=z, logits=s, idx=idx, gate=g, c=c, out=up_project(c, x, inp))
+
+
+def up_project(c: np.ndarray, x: np.ndarray, inp: dict) -> np.ndarray:
+    """Step 6's up-projection out = W_up c (c itself without W_up: the
+    standard MoE layer), plus the shared expert of step 7 if there is one.
+    An E4M3 W_up reads c as stored (rounded to x's format)."""
     if inp.get("W_up") is None:
         out = c.copy()
-    elif np.asarray(inp["W_up"]).dtype == np.uint8:  # E4M3 W_up reads c as stored
+    elif np.asarray(inp["W_up"]).dtype == np.uint8:
         out = project(store_round(c, x), inp, "W_up")
     else:
         out = project(c, inp, "W_up")
     if inp.get("W_s1") is not None:
         out = out + shared_expert(x, inp)
-    return dict(z=z, logits=s, idx=idx, gate=g, c=c, out=out)
+    return out
 
 
 def shared_expert(x: np.ndarray, inp: dict) -> np.ndarray:

@@ -671,3 +671,154 @@ def test_fp8_projections_against_torch_casts(latent, fmt):
     assert rel_err(got["z"], z.numpy()) <= 1e-12
     assert rel_err(got["c"], c) <= 1e-12
     assert rel_err(got["out"], out.numpy()) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Router bias (the skewed decode workload: b_e = 2 ln(1/(e+1)) is added to
+# the logits and used for both the top-k selection and the gate)
+# ---------------------------------------------------------------------------
+
+def _torch_values(a):
+    """A host array of bf16 bit patterns or float32 values as torch float64,
+    decoded by torch itself."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)
+    return torch.from_numpy(a.astype(np.float32)).to(torch.float64)
+
+
+def route_by_torch(x, W_r, b, k):
+    """Routing re-derived in torch, without the oracle's functions: logits
+    x W_r^T + b in float64 kept as float32; expert e is selected iff fewer
+    than k experts precede it in the order (logit desc, id asc), counted
+    pairwise; gates = torch.softmax over the selected logits in that order."""
+    s = (_torch_values(x) @ _torch_values(W_r).T + _torch_values(b)[None, :]).to(torch.float32)
+    sv = s.to(torch.float64)
+    ids = torch.arange(s.shape[1])
+    ahead = (sv[:, None, :] > sv[:, :, None]) | ((sv[:, None, :] == sv[:, :, None]) & (ids[None, None, :] < ids[None, :, None]))
+    rank = ahead.sum(-1)
+    idx = torch.argsort(rank, dim=1)[:, :k]
+    gate = torch.softmax(torch.gather(sv, 1, idx), dim=1)
+    return s.numpy(), idx.numpy().astype(np.int32), gate.numpy()
+
+
+def _check_route_against_torch(inp, k, with_forward=True):
+    s, idx, gate = O.route(inp, k)
+    ts, tidx, tgate = route_by_torch(inp["x"], inp["W_r"], inp["b_r"], k)
+    srt = -np.sort(-ts.astype(np.float64), axis=1)
+    assert np.min(srt[:, k - 1] - srt[:, k]) > 1e-5  # no near tie: the selection is unique
+    assert rel_err(s, ts) <= 1e-6
+    assert np.array_equal(idx, tidx)
+    assert np.max(np.abs(gate - tgate)) <= 1e-6
+    if not with_forward:
+        return
+    f = O.forward(inp, k)
+    assert np.array_equal(f["idx"], tidx) and np.max(np.abs(f["gate"] - tgate)) <= 1e-6
+
+
+def test_router_bias_worked_example():
+    # one token x = e_0 and router rows whose first column gives the raw
+    # logits (0, 0.5, 1, 3); with b_e = -2 ln(e+1) the logits are
+    # (0, 0.5 - 2 ln 2, 1 - 2 ln 3, 3 - 2 ln 4) = (0, -0.886, -1.197, 0.227):
+    # top-2 is (3, 0) and the gates are 1 / (1 + 16 e^-3) and its complement.
+    # Without the bias it would be (3, 2); with the bias negated (3, 2); with
+    # the bias in the selection only the gates would be softmax(3, 0).
+    bf = lambda v: torch.tensor(v, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    W = np.zeros((4, 8))
+    W[:, 0] = [0.0, 0.5, 1.0, 3.0]
+    x = np.zeros((1, 8))
+    x[0, 0] = 1.0
+    b = (-2.0 * np.log(np.arange(1, 5))).astype(np.float32)
+    inp = {"x": bf(x), "W_r": bf(W), "b_r": b}
+    s, idx, gate = O.route(inp, 2)
+    assert idx.tolist() == [[3, 0]]
+    g0 = 1.0 / (1.0 + 16.0 * math.exp(-3.0))
+    assert abs(gate[0, 0] - g0) <= 1e-6 and abs(gate[0, 1] - (1.0 - g0)) <= 1e-6
+    _check_route_against_torch(inp, 2, with_forward=False)
+
+
+def test_router_bias_matches_torch_rederivation():
+    inp = host_inputs(SMALL_ZIPF)
+    assert np.max(np.abs(inp["b_r"])) > 4.0  # the bias spans several logit units
+    _check_route_against_torch(inp, SMALL_ZIPF.k)
+
+
+@pytest.mark.parametrize("which", ["bias_dropped", "bias_negated", "bias_in_selection_only"])
+def test_planted_bias_mistake_is_caught(monkeypatch, which):
+    inp = host_inputs(SMALL_ZIPF)
+    b = np.asarray(inp["b_r"], dtype=np.float64)
+    orig_logits, orig_gates = O.router_logits, O.gate_weights
+    if which == "bias_dropped":
+        monkeypatch.setattr(O, "router_logits", lambda x, W, b_r=None: orig_logits(x, W, None))
+    elif which == "bias_negated":
+        monkeypatch.setattr(O, "router_logits",
+                            lambda x, W, b_r=None: orig_logits(x, W, None if b_r is None else -np.asarray(b_r)))
+    else:  # the gate taken from the logits without the bias
+        monkeypatch.setattr(O, "gate_weights", lambda s, idx: orig_gates(np.asarray(s, np.float64) - b[None, :], idx))
+    with pytest.raises(AssertionError):
+        _check_route_against_torch(inp, SMALL_ZIPF.k)
+
+
+# ---------------------------------------------------------------------------
+# The expert-batched evaluation and the selection override
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16, SMALL_NVFP4, SMALL_NVFP4_2D, SMALL_ZIPF, SMALL_LATENT, TINY_LATENT,
+                                 SMALL_FP8, SMALL_STANDARD, SMALL_FP8_PROJ, SMALL_MXFP8_PROJ, TINY.with_(E=5, k=5)],
+                         ids=lambda c: f"{c.name}-E{c.E}k{c.k}")
+def test_expert_batched_forward_equals_per_token_forward(cfg):
+    inp = host_inputs(cfg)
+    a = O.forward(inp, cfg.k)
+    b = O.forward_batched(inp, cfg.k)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["logits"], b["logits"])
+    for name in ("z", "gate", "c", "out"):
+        assert rel_err(b[name], a[name]) <= 1e-12, name
+
+
+def dense_with_selection(inp, sel):
+    """Every expert on every token, weighted by the full-E softmax masked to
+    the given selection sel [T][k] and renormalised (the dense pin with an
+    arbitrary set in place of the top-k)."""
+    x = O.as_f64(inp["x"])
+    z = x @ O.as_f64(inp["W_down"]).T
+    s = O.router_logits(O.router_input(inp["x"], inp), inp["W_r"], inp.get("b_r")).astype(np.float64)
+    W_up = O.as_f64(inp["W_up"])
+    ew = O.ExpertWeights(inp)
+    out = np.zeros((x.shape[0], x.shape[1]))
+    for t in range(x.shape[0]):
+        mask = np.zeros(s.shape[1])
+        mask[sel[t]] = 1.0
+        p = np.exp(s[t] - s[t].max()) * mask
+        p /= p.sum()
+        for e in range(s.shape[1]):
+            if p[e] > 0.0:
+                W1, W2 = ew(e)
+                out[t] += p[e] * (W_up @ (W2 @ (np.maximum(W1 @ z[t], 0) ** 2)))
+    return out
+
+
+def test_selection_override_equals_dense_pin_with_that_selection():
+    cfg = SMALL_BF16.with_(f_s=0)
+    inp = host_inputs(cfg)
+    rng = np.random.default_rng(11)
+    # another valid-looking selection per token: k distinct ids in random order
+    sel = np.stack([rng.permutation(cfg.E)[:cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    ref = dense_with_selection(inp, sel)
+    assert rel_err(O.forward(inp, cfg.k, idx=sel)["out"], ref) <= 1e-12
+    assert rel_err(O.forward_batched(inp, cfg.k, idx=sel)["out"], ref) <= 1e-12
+    # the same sets in another order give the same outputs
+    rev = sel[:, ::-1].copy()
+    assert rel_err(O.forward(inp, cfg.k, idx=rev)["out"], ref) <= 1e-12
+
+
+@pytest.mark.parametrize("rows_per_scale", [1, 16], ids=["blocks_1x16", "blocks_16x16"])
+def test_nvfp4_table_decode_equals_elementwise_decode(rows_per_scale):
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, size=(3, 32, 24), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(3, 32 // rows_per_scale, 3), dtype=np.uint8)
+    got = O.nvfp4_dequant(codes, scales, 0.375)
+    q = np.empty((3, 32, 48))
+    q[..., 0::2] = O.e2m1_value(codes & 0x0F)
+    q[..., 1::2] = O.e2m1_value(codes >> 4)
+    s = np.repeat(np.repeat(O.e4m3_value(scales), 16, axis=-1), rows_per_scale, axis=-2)
+    assert np.array_equal(got, q * s * 0.375)
