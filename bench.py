@@ -243,14 +243,17 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     return res
 
 
-def cpu_baseline(cfg, inp, n_tokens, synth):
+def oracle_seconds(cfg, inp, tokens, synth, threads=None):
+    """Wall time of the CPU oracle on the given token rows of a layer (their
+    routing, experts, up-projection and shared expert), with numpy's BLAS
+    limited to `threads` threads (all by default).  The experts those rows
+    use are copied to the host first: device-to-host copies are not oracle
+    work."""
+    import contextlib
+
     import numpy as np
     from oracle import latentmoe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        cores = 1
+    from threadpoolctl import threadpool_limits
     h = {}
     for k, v in inp.items():
         if v is None:
@@ -259,17 +262,45 @@ def cpu_baseline(cfg, inp, n_tokens, synth):
             h[k] = synth.LazyExperts(v)
         else:
             h[k] = synth.host_view(v)
-    tokens = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int64)
-    # copy the experts these tokens use to the host first: device->host copies are not oracle work
-    _, idx, _ = O.route({"x": h["x"][tokens], "W_r": h["W_r"], "b_r": h.get("b_r")}, cfg.k)
+    _, idx, _ = O.route({"x": h["x"][tokens], "W_r": h["W_r"], "b_r": h.get("b_r"),
+                         "W_down": h.get("W_down")}, cfg.k)
     for e in np.unique(idx):
         h["W1"][e], h["W2"][e]
-    t0 = time.perf_counter()
-    O.forward(h, cfg.k, tokens=tokens, experts=O.ExpertWeights(h))
-    dt = time.perf_counter() - t0
-    return dict(value=n_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
+    limit = threadpool_limits(limits=threads) if threads else contextlib.nullcontext()
+    with limit:
+        t0 = time.perf_counter()
+        O.forward(h, cfg.k, tokens=tokens, experts=O.ExpertWeights(h, cache_size=len(np.unique(idx))))
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, inp, n_tokens, synth, torch):
+    """The oracle timed on the host: the headline workload on a bounded token
+    sample with every host core, and single-threaded on the tiny workload
+    (all 64 tokens), the mid-size one (a 32-token sample) and the decode
+    workload (all 64 tokens)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    tokens = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int64)
+    dt = oracle_seconds(cfg, inp, tokens, synth)
+    single = {}
+    for name, n in (("tiny_f32", 64), ("mid_bf16", 32), ("decode_bf16_zipf", 64)):
+        c = synth.CONFIGS[name]
+        sub = synth.make_inputs(c, 0, "cuda")
+        t = np.linspace(0, c.T - 1, min(n, c.T)).astype(np.int64)
+        s1 = oracle_seconds(c, sub, t, synth, threads=1)
+        single[name] = dict(tokens=int(len(t)), seconds=s1, tokens_per_s=len(t) / s1)
+        del sub
+        torch.cuda.empty_cache()
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=cores, blas_threads=blas_threads, kind="oracle",
                 sample=f"{n_tokens} evenly spaced tokens of {cfg.name} (routing, experts, up-projection "
-                       f"and shared expert of those tokens), {dt:.1f} s, float64 numpy")
+                       f"and shared expert of those tokens), {dt:.1f} s, float64 numpy on {cores} host cores "
+                       f"(BLAS threads {blas_threads})",
+                single_thread=single)
 
 
 def main():
@@ -392,7 +423,7 @@ def main():
                 args.decode_steps, torch, B, synth, args.expert_layout)
     if not args.no_cpu:
         log("bench: cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens, synth)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens, synth, torch)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

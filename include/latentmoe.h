@@ -328,13 +328,21 @@ int lmoe_quantize_rows_mxfp8(int64_t rows, int64_t cols, const void* src, uint8_
 /* ---- the layer ------------------------------------------------------- */
 
 /*
- * The whole forward: out [T][d] = LatentMoE(x).  router_bias [E] fp32 may be
+ * The whole forward of the LatentMoE layer (Nemotron 3 overview, section 2.2
+ * "LatentMoE", steps 1-3: project the hidden vector down to the latent width
+ * l = d/4, route it and run the selected experts in the latent space, then
+ * project the combined result back up to d; the shared expert stays in d per
+ * the paragraph after that section's table; Ultra release news: 512 experts,
+ * top-22): out [T][d] = LatentMoE(x).  router_bias [E] fp32 may be
  * NULL (no bias); shared may be NULL (then dims.f_s must be 0); dbg may be
  * NULL.  W_down and W_up are device arrays in the activation dtype, or
  * host pointers to lmoe_fp8_matrix with dims.proj_dtype = LMOE_FP8_E4M3, or
- * to lmoe_mxfp8_matrix with dims.proj_dtype = LMOE_MXFP8.  workspace must hold lmoe_workspace_bytes(dims) bytes.  The result
- * equals running lmoe_project_route, lmoe_permute, lmoe_experts_ffn and
- * lmoe_combine_up in that order.
+ * to lmoe_mxfp8_matrix with dims.proj_dtype = LMOE_MXFP8.  workspace (device,
+ * caller-owned, 256-byte aligned) must hold lmoe_workspace_bytes(dims) bytes.
+ * The result equals running lmoe_project_route, lmoe_permute,
+ * lmoe_experts_ffn and lmoe_combine_up in that order.  Errors are returned
+ * before the first launch (out untouched); the call is asynchronous on
+ * stream.
  */
 int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down,
                       const void* W_router, const float* router_bias,
@@ -363,7 +371,9 @@ int lmoe_project_route(const lmoe_dims* dims, const void* x, const void* W_down,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Token permutation: counts[e] = number of (t, j) with topk_idx[t][j] = e;
+ * Token permutation.  The pages do not describe how the routed tokens are
+ * grouped by expert; this stable counting sort is this layer's own
+ * specification of that step: counts[e] = number of (t, j) with topk_idx[t][j] = e;
  * offsets[e] = sum of counts below e, offsets[E] = T*k; perm[p] = the flat
  * pair index t*k + j at sorted position p, stable (pairs ascend within each
  * expert); inv = perm^-1.  Integer results are exact and deterministic.

@@ -659,9 +659,10 @@ __device__ __forceinline__ void e4m3_parts(uint32_t b, float& pw, float& mt) {
 
 // 8 E2M1 codes (one 32-bit word, element i in bits 4i..4i+3, so byte j holds
 // elements 2j and 2j+1) -> 8 bf16.  The hardware conversion scales by the
-// power of two exactly; the product with mt has at most 5 significant bits
-// (an E2M1 value has 2, an E4M3 factor 4), so it is exact in fp32 and its
-// upper half is the exact bf16.
+// power of two exactly; the product with mt has at most 6 significant bits
+// (an E2M1 value has up to 2, an E4M3 factor up to 4: 1.5 x 1.875 =
+// 10.1101b), so it is exact in fp32 and its upper half (8 bits) is the exact
+// bf16.
 __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float pw, float mt) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     u32x4_t r;
@@ -1537,7 +1538,6 @@ size_t dense_tail_split_bytes(const DenseGemm& g) {
     return bytes;
 }
 
-#ifndef LMOE_GEMM_VARIANTS
 // Dense: 256x256 tiles over 8 waves (2 per SIMD), each wave 64 x 128, the
 // fastest shape measured for the 8192-wide projections; 256x192 where that
 // fills the GPU better (narrow N, few M tiles).  Decode-sized M uses 64x64
@@ -1656,6 +1656,5 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
     if (g.tt.bm == 64) return run_grouped<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, s);
     return hipErrorInvalidValue;
 }
-#endif
 
 }  // namespace lmoe

@@ -46,3 +46,14 @@ def test_source_digest_covers_the_gemm_sources(tmp_path, monkeypatch):
     assert bench.kernel_source_digest() == d0
     (csrc / "device_common.hpp").write_bytes((csrc / "device_common.hpp").read_bytes() + b"\n")
     assert bench.kernel_source_digest() != d0
+
+
+def test_oracle_timing_runs_single_threaded_on_host_inputs():
+    # the CPU-baseline leg: the oracle on a token sample, BLAS limited to one thread
+    import numpy as np
+
+    from sparse_moe_layer_06_amd import synth
+    cfg = synth.CONFIGS["tiny_f32"]
+    inp = synth.make_inputs(cfg, 0, "cpu")
+    dt = bench.oracle_seconds(cfg, inp, np.arange(8), synth, threads=1)
+    assert dt > 0.0
