@@ -43,8 +43,9 @@ struct DenseGemm {
 };
 
 // Device tile table of a grouped GEMM: M-tiles of BM sorted rows per expert.
-// tiles[i] = {expert, first sorted row, rows, 0}; expert_tile_start/ntiles
-// give each expert's tile range.  Built on the device from the offsets.
+// tiles[i] = {expert, first sorted row, rows, m | nt << 16} for the m-th of
+// the expert's nt tiles; expert_tile_start/ntiles give each expert's tile
+// range.  Built on the device from the offsets.
 struct TileTable {
     const int* tile_count;
     const int4* tiles;

@@ -76,7 +76,7 @@ __device__ void write_tiles(int e, int E, int count, int offset, const TileTable
     if (e < E) {
         int4* tiles = const_cast<int4*>(tt.tiles);
         for (int m = 0; m < nt; ++m)
-            tiles[ts + m] = make_int4(e, offset + m * bm, min(bm, count - m * bm), 0);
+            tiles[ts + m] = make_int4(e, offset + m * bm, min(bm, count - m * bm), m | (nt << 16));
         const_cast<int*>(tt.expert_tile_start)[e] = ts;
         const_cast<int*>(tt.expert_ntiles)[e] = nt;
     }
