@@ -351,6 +351,29 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down,
                       void* workspace, size_t workspace_bytes,
                       const lmoe_debug* dbg, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * forward of latentmoe_forward without a workspace argument.  Its workspace
+ * is a library-owned array of LMOE_STATIC_SCRATCH_BYTES (128 MiB) per GPU,
+ * allocated when the library's code is loaded on that GPU and held until
+ * the process ends; the call allocates and frees nothing.  The array of the
+ * current device is used (stream must belong to it).  Returns
+ * LMOE_ERR_WORKSPACE before any launch when lmoe_workspace_bytes(dims)
+ * exceeds LMOE_STATIC_SCRATCH_BYTES (decode-sized layers fit: 76 MiB at
+ * T = 64, d = 8192, E = 512, k = 22); other arguments and errors as for
+ * latentmoe_forward.  Every call on one GPU shares that GPU's array and
+ * finds it holding the previous call's data (nothing in it needs to start
+ * at zero): calls that overlap in time on one GPU (other streams or host
+ * threads) race, so serialise them.
+ */
+#define LMOE_STATIC_SCRATCH_BYTES (128u << 20)
+int lmoe_static_forward(const lmoe_dims* dims, const void* x, const void* W_down,
+                        const void* W_router, const float* router_bias,
+                        const lmoe_experts* experts, const void* W_up,
+                        const lmoe_shared* shared, int k, void* out,
+                        const lmoe_debug* dbg, void* stream);
+
 /* ---- staged entry points (same conventions) -------------------------- */
 
 /*

@@ -32,7 +32,8 @@ EXPORTED = ["lmoe_workspace_bytes", "lmoe_validate_dims", "lmoe_strerror", "lmoe
             "latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
             "lmoe_combine_up", "lmoe_timing_start", "lmoe_timing_stop", "lmoe_pack_expert_weights",
             "lmoe_quantize_rows_fp8", "lmoe_quantize_rows_mxfp8", "lmoe_create", "lmoe_destroy",
-            "lmoe_ctx_reserve", "lmoe_ctx_workspace_bytes", "lmoe_ctx_forward"]
+            "lmoe_ctx_reserve", "lmoe_ctx_workspace_bytes", "lmoe_ctx_forward", "lmoe_static_forward"]
+LMOE_STATIC_SCRATCH_BYTES = 128 << 20
 
 
 class Dims(ctypes.Structure):
@@ -120,6 +121,9 @@ def lib() -> ctypes.CDLL:
         L.lmoe_ctx_workspace_bytes.restype = sz
         L.lmoe_ctx_forward.argtypes = [vp, pd, vp, vp, vp, vp, ctypes.POINTER(Experts), vp,
                                        ctypes.POINTER(Shared), ctypes.c_int, vp, ctypes.POINTER(Debug), vp]
+        L.lmoe_static_forward.argtypes = [pd, vp, vp, vp, vp, ctypes.POINTER(Experts), vp,
+                                          ctypes.POINTER(Shared), ctypes.c_int, vp, ctypes.POINTER(Debug), vp]
+        L.lmoe_static_forward.restype = ctypes.c_int
         L.lmoe_quantize_rows_fp8.restype = ctypes.c_int
         for n in ("latentmoe_forward", "lmoe_project_route", "lmoe_permute", "lmoe_experts_ffn",
                   "lmoe_combine_up"):
@@ -323,6 +327,24 @@ def forward(cfg: LayerDims, inp, out: Optional[torch.Tensor] = None,
     if workspace is None:
         workspace = alloc_workspace(cfg, x.device, x.shape[0])
     Call(cfg, inp, out, workspace, debug, stream)()
+    return out
+
+
+def static_forward(cfg: LayerDims, inp, out: Optional[torch.Tensor] = None, debug=None,
+                   stream=None) -> torch.Tensor:
+    """out [T][d] = LatentMoE(inp['x']) through lmoe_static_forward: the
+    library's own per-GPU scratch array as workspace (no allocation by the
+    library; out is allocated here when not given)."""
+    x = inp["x"]
+    if out is None:
+        out = torch.empty((x.shape[0], cfg.d), dtype=act_dtype(cfg), device=x.device)
+    d = dims_of(cfg, x.shape[0])
+    ex, sh = experts_struct(inp), shared_struct(inp)
+    wd, wu = _Proj(cfg, inp, "W_down"), _Proj(cfg, inp, "W_up")
+    dbg = Debug(**{n: _p(debug.get(n)) for n, _ in Debug._fields_}) if debug else None
+    _check(lib().lmoe_static_forward(ctypes.byref(d), _p(x), wd.arg, _p(inp["W_r"]), _p(inp.get("b_r")),
+                                     ctypes.byref(ex), wu.arg, _byref_opt(sh), cfg.k, _p(out), _byref_opt(dbg),
+                                     _stream(stream)), "lmoe_static_forward")
     return out
 
 

@@ -16,6 +16,7 @@
 // fp8 GEMMs of their own, each after a per-token quantisation of its input.
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "lmoe_internal.hpp"
@@ -470,6 +471,37 @@ static hipError_t run_combine_up(const lmoe_dims& d, const void* Y, const int32_
 
 using namespace lmoe;
 
+// ---- the allocation-free forward's workspace ------------------------------
+// One array per GPU the library runs on, held until the process ends.  In
+// host code its name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[LMOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (hipGetSymbolAddress on its first use
+// on that device).
+hipError_t static_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
 extern "C" {
 
 int lmoe_validate_dims(const lmoe_dims* d) {
@@ -719,6 +751,18 @@ int lmoe_ctx_reserve(lmoe_ctx* ctx, const lmoe_dims* dims) {
 }
 
 size_t lmoe_ctx_workspace_bytes(const lmoe_ctx* ctx) { return ctx ? ctx->bytes : 0; }
+
+int lmoe_static_forward(const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,
+                        const float* router_bias, const lmoe_experts* experts, const void* W_up,
+                        const lmoe_shared* shared, int k, void* out, const lmoe_debug* dbg, void* stream) {
+    LMOE_TRY(lmoe_validate_dims(dims));
+    if (plan(*dims).total > (size_t)LMOE_STATIC_SCRATCH_BYTES) return LMOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+    return latentmoe_forward(dims, x, W_down, W_router, router_bias, experts, W_up, shared, k, out, ws,
+                             (size_t)LMOE_STATIC_SCRATCH_BYTES, dbg, stream);
+}
 
 int lmoe_ctx_forward(lmoe_ctx* ctx, const lmoe_dims* dims, const void* x, const void* W_down, const void* W_router,
                      const float* router_bias, const lmoe_experts* experts, const void* W_up,

@@ -272,3 +272,26 @@ def test_context_error_paths():
     d = dims()
     assert L.lmoe_ctx_forward(None, ctypes.byref(d), FAKE, FAKE, FAKE, None, ctypes.byref(ex), FAKE, None, d.k,
                               FAKE, None, None) == B.LMOE_ERR_NULL
+
+
+def test_static_forward_rejects_layers_beyond_its_scratch_before_any_launch():
+    # the allocation-free entry point: a layer whose workspace exceeds the
+    # library's per-GPU scratch array is refused on the host
+    big = synth.CONFIGS["prefill_bf16"]
+    assert B.workspace_bytes(big) > B.LMOE_STATIC_SCRATCH_BYTES
+    d = B.dims_of(big)
+    rc = B.lib().lmoe_static_forward(ctypes.byref(d), None, None, None, None, None, None, None, big.k, None,
+                                     None, None)
+    assert rc == B.LMOE_ERR_WORKSPACE
+    # the decode workloads fit
+    for name in ("decode_bf16_zipf",):
+        c = synth.CONFIGS[name]
+        for v in (c, c.with_(router_latent=True), c.with_(proj_fp8=True), c.with_(proj_mxfp8=True),
+                  c.with_(l=c.d, E=128, k=6, standard_moe=True)):
+            assert B.workspace_bytes(v) <= B.LMOE_STATIC_SCRATCH_BYTES
+
+
+def test_static_scratch_size_matches_header():
+    with open(os.path.join(ROOT, "include", "latentmoe.h")) as fh:
+        m = re.search(r"#define LMOE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", fh.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == B.LMOE_STATIC_SCRATCH_BYTES
