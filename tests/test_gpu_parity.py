@@ -24,11 +24,17 @@ TINY = CFG["tiny_f32"]
 SMALL = {
     "bf16_ragged": TINY.with_(name="bf16_ragged", T=193, d=256, l=64, E=12, k=3, f=192, f_s=192,
                               act="bf16", experts="bf16"),
-    # >= 96 rows per expert on average: the 192-row expert tiles
+    # >= 96 rows per expert on average: the 192-row expert tiles, each expert
+    # in one partly filled tile
     "bf16_deep": TINY.with_(name="bf16_deep", T=500, d=512, l=128, E=8, k=2, f=256, f_s=320,
                             act="bf16", experts="bf16"),
     "nvfp4_deep": TINY.with_(name="nvfp4_deep", T=300, d=512, l=128, E=4, k=2, f=256, f_s=0,
                              act="bf16", experts="nvfp4"),
+    # more than 192 rows per expert: full and partly filled 192-row tiles
+    "bf16_deep192": TINY.with_(name="bf16_deep192", T=450, d=512, l=128, E=4, k=2, f=320, f_s=192,
+                               act="bf16", experts="bf16"),
+    "nvfp4_deep192": TINY.with_(name="nvfp4_deep192", T=400, d=512, l=128, E=4, k=2, f=256, f_s=0,
+                                act="bf16", experts="nvfp4"),
     "nvfp4_sparse": TINY.with_(name="nvfp4_sparse", T=70, d=256, l=64, E=16, k=3, f=128, f_s=0,
                                act="bf16", experts="nvfp4"),
     "zipf_small": TINY.with_(name="zipf_small", T=64, d=512, l=128, E=64, k=6, f=256, f_s=0,
@@ -91,6 +97,8 @@ SMALL = {
     # tiles with a ragged N = 1280
     "nvfp4_2d_deep": TINY.with_(name="nvfp4_2d_deep", T=300, d=512, l=128, E=4, k=2, f=256, f_s=0,
                                 act="bf16", experts="nvfp4_2d"),
+    "nvfp4_2d_deep192": TINY.with_(name="nvfp4_2d_deep192", T=400, d=512, l=128, E=4, k=2, f=256, f_s=0,
+                                   act="bf16", experts="nvfp4_2d"),
     "nvfp4_2d_few_wide": TINY.with_(name="nvfp4_2d_few_wide", T=16, d=4096, l=1024, E=16, k=2, f=1280, f_s=0,
                                     act="bf16", experts="nvfp4_2d"),
     # MXFP8 projections (E4M3 with E8M0 scales per 32 elements, applied by
@@ -150,7 +158,8 @@ def test_all_tokens_to_one_expert():
     assert counts[3] == counts[7] == counts[1] == cfg.T and counts.sum() == cfg.T * cfg.k
 
 
-@pytest.mark.parametrize("name", ["bf16_deep", "nvfp4_deep", "nvfp4_2d_deep"])
+@pytest.mark.parametrize("name", ["bf16_deep", "nvfp4_deep", "nvfp4_2d_deep", "bf16_deep192", "nvfp4_deep192",
+                                  "nvfp4_2d_deep192"])
 def test_experts_spanning_several_tiles(name):
     # every token routed to the same two experts (a large bias on them): 500
     # rows each, so each expert takes two full 192-row tiles and a 116-row
