@@ -7,7 +7,8 @@
 //   1. dense MFMA GEMM  x [W_down; W_r; W_s1]^T -> z, logits (+bias), hs
 //   2. top-k + softmax gate                     -> idx, gate
 //      (with few tokens: in step 1's split-K reduction)
-//   3. permutation (hist, scan + tile table, stable scatter)
+//   3. permutation (hist, scan + tile table, stable scatter; with few tokens
+//      in the last token block of step 2's reduction)
 //   4. grouped GEMM  H = relu(z[perm] W1_e^T)^2
 //   5. grouped GEMM  Y = H W2_e^T
 //   6. combine       c_t = sum_j gate_tj Y[inv(t, j)]
@@ -140,7 +141,7 @@ static DenseGemm gemm_out(const lmoe_dims& d, const void* c, const void* hs, con
 struct Layout {
     size_t z, logits, idx, gate, counts, offsets, perm, inv, hist, tiles, tile_count, tile_start, ntiles, H, Y,
         c, hs, splitk, splitk_bytes, sk_part, sk_count, sk_count_len, q_x, s_x, q_h, s_h, q_c, s_c, mq_x, ms_x, mq_c,
-        ms_c, total;
+        ms_c, arrive, total;
 };
 
 // Whether the few-rows expert GEMMs may take the split-K 64 x 256 tiles
@@ -175,6 +176,7 @@ static Layout plan(const lmoe_dims& d) {
     L.tile_count = take(4);
     L.tile_start = take((size_t)d.E * 4);
     L.ntiles = take((size_t)d.E * 4);
+    L.arrive = take(4);  // arrival counter of the decode router reduction that also permutes
     L.H = take(n * d.f * es);
     L.Y = take(n * d.l * es);
     L.c = take(d.standard_moe ? 0 : (size_t)d.T * d.l * es);
@@ -298,10 +300,13 @@ static TileTable tile_table(const lmoe_dims& d, char* ws, const Layout& L) {
 
 // ---- the steps, shared by the fused and the staged entry points --------
 
+// pf (the fused forward's permutation outputs, or null): with few tokens the
+// router reduction also permutes the pairs, and *perm_done says so.
 static hipError_t run_project_route(const lmoe_dims& d, const void* x, const void* W_down, const void* W_r,
                                     const float* bias, const lmoe_shared* sh, void* z, float* logits,
                                     int32_t* idx, float* gate, void* hs, char* ws, const Layout& L,
-                                    hipStream_t s) {
+                                    hipStream_t s, const PermFused* pf = nullptr, bool* perm_done = nullptr) {
+    if (perm_done) *perm_done = false;
     const DenseGemm g = gemm_in(d, x, W_down, W_r, bias, sh ? sh->W_s1 : nullptr, z, logits, hs);
     hipError_t e = hipSuccess;
     // Few tokens with the router in d: the top-k is taken in this GEMM's
@@ -311,7 +316,8 @@ static hipError_t run_project_route(const lmoe_dims& d, const void* x, const voi
     if (route_fused) {
         const int lc0 = (d.standard_moe || proj_8bit(d)) ? 0 : (int)d.l;
         e = launch_dense_gemm_topk_bf16(g, ws + L.splitk, L.splitk_bytes, lc0, (int)d.E, bias, (int)d.k, idx, gate,
-                                        s);
+                                        pf, s);
+        if (pf && perm_done) *perm_done = e == hipSuccess;
     } else if (g.N > 0) {
         e = launch_dense_gemm(g, d.act_dtype, (int)d.T, ws + L.splitk, L.splitk_bytes, s);
     }
@@ -629,9 +635,11 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down, 
     void* hs = ws + L.hs;
     const TileTable tt = tile_table(d, ws, L);
 
+    const PermFused pf{counts, offsets, perm, inv, tt, (int*)(ws + L.arrive)};
+    bool perm_done = false;
     hipError_t e = run_project_route(d, x, W_down, W_router, router_bias, shared, (void*)z, logits, idx, gate, hs,
-                                     ws, L, s);
-    if (e == hipSuccess)
+                                     ws, L, s, &pf, &perm_done);
+    if (e == hipSuccess && !perm_done)
         e = launch_permute(idx, d.T * d.k, (int)d.E, (int32_t*)(ws + L.hist), counts, offsets, perm, inv, &tt, s);
     if (e == hipSuccess) e = run_experts(d, z, perm, experts, ws + L.H, ws + L.Y, tt, ws, L, s);
     if (e == hipSuccess) e = run_combine_up(d, ws + L.Y, inv, gate, W_up, shared, hs, dv.c, out, ws, L, s);

@@ -31,6 +31,7 @@
 
 #include "device_common.hpp"
 #include "lmoe_internal.hpp"
+#include "perm_block.hpp"
 #include "topk_row.hpp"
 
 namespace lmoe {
@@ -451,9 +452,10 @@ __device__ __forceinline__ void dense_store4(const DenseGemm& g, int m, int n, c
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MINB) void dense_gemm_kernel(DenseGemm g, int tiles_m, int tiles_n,
                                                               int group_m, int splits, float* partial,
-                                                              int ldp) {
+                                                              int ldp, int* clear) {
     __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
     const int tid = threadIdx.x, lane = tid & 63;
+    if (clear && blockIdx.x == 0 && tid == 0) *clear = 0;  // a counter of the kernel that follows
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
@@ -584,6 +586,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseGemm g, int spl
     }
 }
 
+// Pairs the fused permutation sorts at most (up to 64 rows of top-64).
+constexpr int kMaxFusedPairs = 64 * kWave;
+
 // The decode-sized first GEMM's reduction with the router folded in.  Two
 // blocks per token row sum the row's split partials in split order and
 // store them through the column groups' epilogues, as splitk_reduce_kernel
@@ -595,12 +600,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(DenseGemm g, int spl
 // logits.  This saves the router kernel's launch and its re-read.  1024
 // threads, so each part of a decode row takes one pass of float4 chunks,
 // with up to 16 splits' loads in flight per thread.
-template <int S>
+//
+// PERM (the fused forward): the row's ids are stored device-coherently, and
+// each selecting block counts itself in once they have completed; the last
+// of the M token blocks reads every id back (device-coherent loads) and runs
+// the permutation's single-block counting sort, so that kernel's launch
+// goes.  Every block's ids are complete before its arrival is counted, so
+// the last one reads all of them.
+template <int S, bool PERM>
 __global__ __launch_bounds__(1024) void splitk_reduce_topk_kernel(DenseGemm g, int splits,
                                                                  const float* __restrict__ partial, int ldp,
                                                                  int lc0, int E, const float* __restrict__ bias,
                                                                  int k, int32_t* __restrict__ idx,
-                                                                 float* __restrict__ gate) {
+                                                                 float* __restrict__ gate, PermFused pf) {
     __shared__ float s_l[S * kWave];
     __shared__ uint64_t by_id[kWave], by_rank[kWave];
     const bool sel = (int)blockIdx.x < g.M;  // this block selects the row's top-k
@@ -638,7 +650,24 @@ __global__ __launch_bounds__(1024) void splitk_reduce_topk_kernel(DenseGemm g, i
     }
     if (!sel) return;
     __syncthreads();
-    if (threadIdx.x < kWave) topk_select_row<S>(s_l, E, k, m, by_id, by_rank, idx, gate);
+    if (threadIdx.x < kWave) topk_select_row<S, PERM>(s_l, E, k, m, by_id, by_rank, idx, gate);
+    if constexpr (PERM) {
+        __shared__ int s_last;
+        __shared__ int32_t s_idx[kMaxFusedPairs];
+        __shared__ int h[kSmallWaves][kMaxExperts];
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's id stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(pf.arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g.M - 1;
+        __syncthreads();
+        if (!s_last) return;
+        const int n = g.M * k;
+        for (int p = threadIdx.x; p < n; p += 1024)
+            s_idx[p] = __hip_atomic_load(idx + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        perm_block(s_idx, n, E, pf.counts, pf.offsets, pf.perm, pf.inv, pf.tt, 1, h);
+        if (threadIdx.x == 0) *pf.arrive = 0;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1432,7 +1461,7 @@ static hipError_t run_dense(const DenseGemm& g, void* ws, size_t ws_bytes, hipSt
     float* partial = splits > 1 ? (float*)ws : nullptr;
     LMOE_LAUNCH("dense_gemm", s,
                 dense_gemm_kernel<C><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
-                                                                                  partial, ldp));
+                                                                                  partial, ldp, nullptr));
     if (splits > 1) {
         const int64_t threads = (int64_t)g.M * (ldp / 4);
         LMOE_LAUNCH("splitk_reduce", s,
@@ -1573,20 +1602,32 @@ bool dense_topk_fusable(const DenseGemm& g, size_t splitk_bytes, int E, int k) {
 }
 
 hipError_t launch_dense_gemm_topk_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, int lc0, int E,
-                                       const float* bias, int k, int32_t* idx, float* gate, hipStream_t s) {
+                                       const float* bias, int k, int32_t* idx, float* gate, const PermFused* pf,
+                                       hipStream_t s) {
     using C = DecodeDenseCfg;
     if (!dense_topk_fusable(g, splitk_bytes, E, k) || lc0 < 0 || lc0 + E > g.N) return hipErrorInvalidValue;
+    if (pf && (!pf->arrive || g.M * k > kMaxFusedPairs || E > kMaxExperts)) return hipErrorInvalidValue;
     const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
     const int ldp = (g.N + 3) / 4 * 4;
     const int splits = decode_dense_splits(g, splitk_bytes);
     float* partial = (float*)splitk_ws;
+    const PermFused none{};
     LMOE_LAUNCH("dense_gemm", s,
                 dense_gemm_kernel<C><<<tiles_m * tiles_n * splits, C::NT, 0, s>>>(g, tiles_m, tiles_n, 8, splits,
-                                                                                  partial, ldp));
-#define LMOE_REDUCE_TOPK(S_)                                                                                  \
-    LMOE_LAUNCH("splitk_reduce_topk", s,                                                                      \
-                splitk_reduce_topk_kernel<S_><<<2 * g.M, 1024, 0, s>>>(g, splits, partial, ldp, lc0, E, bias, k, \
-                                                                     idx, gate))
+                                                                                  partial, ldp,
+                                                                                  pf ? pf->arrive : nullptr));
+#define LMOE_REDUCE_TOPK(S_)                                                                                   \
+    do {                                                                                                       \
+        if (pf)                                                                                                \
+            LMOE_LAUNCH("splitk_reduce_topk_perm", s,                                                          \
+                        splitk_reduce_topk_kernel<S_, true><<<2 * g.M, 1024, 0, s>>>(g, splits, partial, ldp, lc0, \
+                                                                                   E, bias, k, idx, gate, *pf)); \
+        else                                                                                                   \
+            LMOE_LAUNCH("splitk_reduce_topk", s,                                                               \
+                        splitk_reduce_topk_kernel<S_, false><<<2 * g.M, 1024, 0, s>>>(g, splits, partial, ldp,   \
+                                                                                    lc0, E, bias, k, idx, gate, \
+                                                                                    none));                    \
+    } while (0)
     if (E <= 64)
         LMOE_REDUCE_TOPK(1);
     else if (E <= 128)

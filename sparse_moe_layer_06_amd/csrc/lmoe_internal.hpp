@@ -116,8 +116,20 @@ struct Fp8Gemm {
 // [lc0, lc0 + E) (+ bias): dense_topk_fusable says whether a call takes
 // that path (at most 64 rows, k <= 64, a split, E <= 1024).
 bool dense_topk_fusable(const DenseGemm& g, size_t splitk_bytes, int E, int k);
+// The permutation's outputs when the last token block of that reduction
+// also sorts the pairs (the fused forward): arrive is a workspace counter
+// the GEMM clears before the reduction counts its token blocks in.
+struct PermFused {
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv;
+    TileTable tt;
+    int* arrive;
+};
 hipError_t launch_dense_gemm_topk_bf16(const DenseGemm& g, void* splitk_ws, size_t splitk_bytes, int lc0, int E,
-                                       const float* bias, int k, int32_t* idx, float* gate, hipStream_t s);
+                                       const float* bias, int k, int32_t* idx, float* gate, const PermFused* pf,
+                                       hipStream_t s);
 hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_bytes, hipStream_t s);
 
 // MXFP8 quantisation of a bf16 matrix [rows][cols] (cols % 32 == 0, row

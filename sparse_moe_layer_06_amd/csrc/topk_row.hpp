@@ -22,14 +22,20 @@ __device__ __forceinline__ float unordered_value(uint32_t o) {
 }
 
 // Gates of the k (<= 64) selections held by lanes 0..k-1, in rank order:
-// softmax with the rank-0 logit as the shift.
+// softmax with the rank-0 logit as the shift.  COHERENT_IDX stores the ids
+// with device-coherent (agent-scope) stores, for a reader on another XCD
+// within the same kernel.
+template <bool COHERENT_IDX = false>
 __device__ __forceinline__ void write_gates(float v, int e, int lane, int64_t t, int k, int32_t* __restrict__ idx,
                                             float* __restrict__ gate) {
     const float vmax = __shfl(v, 0, kWave);
     const float w = lane < k ? expf(v - vmax) : 0.f;
     const float inv_sum = 1.0f / wave_sum(w);
     if (lane < k) {
-        idx[t * k + lane] = e;
+        if constexpr (COHERENT_IDX)
+            __hip_atomic_store(idx + t * k + lane, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            idx[t * k + lane] = e;
         gate[t * k + lane] = w * inv_sum;
     }
 }
@@ -41,7 +47,7 @@ __device__ __forceinline__ void write_gates(float v, int e, int lane, int64_t t,
 // every logit above X plus the lowest ids among those equal to X; the k
 // selected (logit, id) keys are ranked against each other in the wave's LDS
 // scratch (by_id, by_rank: 64 keys each) and lane j writes the key of rank j.
-template <int S>
+template <int S, bool COHERENT_IDX = false>
 __device__ __forceinline__ void topk_select_row(const float* s, int E, int k, int64_t t, uint64_t* by_id,
                                                 uint64_t* by_rank, int32_t* __restrict__ idx,
                                                 float* __restrict__ gate) {
@@ -94,7 +100,7 @@ __device__ __forceinline__ void topk_select_row(const float* s, int E, int k, in
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint64_t key = lane < k ? by_rank[lane] : 0ull;
-    write_gates(unordered_value((uint32_t)(key >> 32)), (int)(~(uint32_t)key), lane, t, k, idx, gate);
+    write_gates<COHERENT_IDX>(unordered_value((uint32_t)(key >> 32)), (int)(~(uint32_t)key), lane, t, k, idx, gate);
 }
 
 }  // namespace lmoe

@@ -190,8 +190,12 @@ def test_exact_logit_ties_break_to_lower_id(T, d):
         torch.cuda.synchronize()
     idx = dbg["topk_idx"].cpu().numpy()
     assert np.all(idx == np.array([6, 1, 2])), idx[:2]
-    fused = "splitk_reduce_topk" in kt.by_kernel()
-    assert fused == (T == 64) and fused != ("topk_softmax" in kt.by_kernel())
+    ran = kt.by_kernel()
+    # 64 tokens: the reduction also permutes (its last token block), so no
+    # router or permutation kernel of its own runs
+    fused = "splitk_reduce_topk_perm" in ran
+    assert fused == (T == 64) and fused != ("topk_softmax" in ran)
+    assert fused != any(n.startswith("perm_") for n in ran)
 
 
 def test_staged_entry_points_compose_to_forward():
