@@ -144,7 +144,7 @@ struct Layout {
         ms_c, arrive, total;
 };
 
-// Whether the few-rows expert GEMMs may take the split-K 64 x 256 tiles
+// Whether the few-rows expert GEMMs may take the split-K 64 x 128 tiles
 // (64-row expert tiles, outputs at least 1024 wide): they then need the
 // partial-sum buffer and one counter per work item.
 static bool expert_split_k(const lmoe_dims& d) {

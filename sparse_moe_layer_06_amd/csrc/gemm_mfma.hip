@@ -1510,7 +1510,7 @@ static void launch_grouped_any(const GroupedGemm& g, int grid, int nN, hipStream
         launch_grouped_fmt<C, LMOE_BF16, SK>(g, grid, nN, s);
 }
 
-// Split-K scheduling for the 64 x 256 few-rows tiles when the caller gave
+// Split-K scheduling for the 64 x 128 few-rows tiles when the caller gave
 // the partial-sum buffer and enough counters; whole items otherwise.
 template <class C>
 static hipError_t run_grouped(const GroupedGemm& g, hipStream_t s) {
@@ -1703,12 +1703,14 @@ hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_byte
 // Grouped: 192-row expert tiles (about 352 rows per expert at prefill pad to
 // 384) by 256 columns over 8 waves, each wave 96 x 64.  Few-row experts
 // (decode) stream their weights with the non-temporal hint (each call reads
-// them once): 64x256 tiles, 3 LDS stages, for wide outputs (each activation
-// row fetched per K step then feeds 256 weight rows, not 64), else 64x64
-// tiles, 4 stages, two blocks per CU.
+// them once), two blocks per CU: 64x128 tiles, 3 LDS stages, for wide
+// outputs (each activation row fetched per K step then feeds 128 weight rows,
+// not 64), else 64x64 tiles, 4 stages.  A plain weight stream through LDS-DMA
+// with two 4-wave blocks per CU reached 6.8 TB/s; one 8-wave block per CU with
+// the same bytes in flight, 5.6.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
     if (g.tt.bm == 192) return run_grouped<MfmaCfg<192, 256, 2, 4, true, 64, 2>>(g, s);
-    if (g.tt.bm == 64 && g.N >= 1024) return run_grouped<MfmaCfg<64, 256, 2, 4, true, 64, 3, 1, true>>(g, s);
+    if (g.tt.bm == 64 && g.N >= 1024) return run_grouped<MfmaCfg<64, 128, 2, 2, true, 64, 3, 2, true>>(g, s);
     if (g.tt.bm == 64) return run_grouped<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, s);
     return hipErrorInvalidValue;
 }

@@ -63,7 +63,7 @@ struct TileTable {
 // full rounds of the blocks as they can; each item of the last, partial
 // round is split along K over up to kSkMaxParts blocks, and the block that
 // finishes last sums the parts in part order.  One partial-sum slot per block.
-constexpr int kSkBM = 64, kSkBN = 256;
+constexpr int kSkBM = 64, kSkBN = 128;
 constexpr int kSkMaxBlocks = 512, kSkMaxParts = 4;
 constexpr size_t kSkPartialBytes = (size_t)kSkMaxBlocks * kSkBM * kSkBN * sizeof(float);
 
