@@ -151,6 +151,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt with vmcnt(N) and lgkmcnt(0): also this wave's LDS writes done.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 // Waits until at most `ahead` K tiles of this wave's DMA are still in flight
 // (`per_tile` instructions each), then the workgroup barrier.  The empty asm
 // statements keep the compiler from moving memory accesses across.
@@ -734,7 +741,13 @@ enum Gather : int { GATHER_NONE = 0, GATHER_SCALAR = 1, GATHER_LANE = 2 };
 //               otherwise be streamed by one block while the rest idle.
 template <class C, int BFMT, int GATHER, bool SK = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGemm g, int nN) {
-    __shared__ u32x4_t ring[C::STAGES * C::STAGE_CHUNKS];
+    // NVFP4 prefill tiles with 3 stages (SPLITB): the A ring has 3 stages,
+    // the decoded weight tiles a 2-slot ring of their own, and the raw codes
+    // and scale words (RAW chunks per step) a 2-slot ring; see the K loop.
+    constexpr bool SPLITB = (BFMT == LMOE_NVFP4 || BFMT == LMOE_NVFP4_2D) && !SK && C::STAGES == 3 && C::BM >= 128;
+    constexpr int RAW = C::NT + C::NT / 4;  // a 16-byte chunk of codes and a 4-byte scale word per thread
+    __shared__ u32x4_t ring[SPLITB ? (C::STAGES * C::BM + 2 * C::BN) * C::CPR + 2 * RAW
+                                   : C::STAGES * C::STAGE_CHUNKS];
     __shared__ int sk_last;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -873,9 +886,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             const int64_t n = (int64_t)e * N + min(n0 + tid / LPR, N - 1);
             c_ptr = g.B_codes + n * (K / 2) + (tid % LPR) * (EPL / 2);
             // 2-D blocks: N is a multiple of 16, so weight row n of the stack
-            // has scale row n / 16 of [E][N/16][K/16]
+            // has scale row n / 16 of [E][N/16][K/16].  A lane loads the
+            // row's whole 4-byte scale word of a K step (4-byte aligned: K is
+            // a multiple of 64 and the stack 16-byte aligned) and uses its
+            // own EPL/16 bytes of it.
             const int64_t srow = BFMT == LMOE_NVFP4_2D ? n >> 4 : n;
-            s_ptr = g.B_scales + srow * (K / 16) + (tid % LPR) * (EPL / 16);
+            s_ptr = g.B_scales + srow * (K / 16);
         } else if constexpr (BFMT == LMOE_BF16_TILED) {
             // 64-row slabs of 64x64 tiles, each stored in the swizzled order of
             // the LDS tile (the swizzle repeats every 16 rows and n0 is a
@@ -897,9 +913,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     setup(fdesc);
 
     u32x4_t ra[C::DMA ? 1 : SA::N], rb[B_DMA || FP4 ? 1 : SB::N];
-    code_words_t rc;  // NVFP4: EPL codes
-    uint32_t rs = 0;  // NVFP4: EPL/16 scale bytes
-    // issues the next K step of the fill item into stage (As, Bs)
+    code_words_t rc;   // NVFP4: EPL codes
+    uint32_t rs = 0;   // NVFP4: the weight row's 4 scale bytes of a K step
+    // issues the next K step of the fill item into stage (As, Bs); with
+    // SPLITB, Bs is the raw slot the NVFP4 codes and scale words go to
     auto fill_next = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
         if (f_kt == nk) {  // next item: its descriptor was fetched one item ahead
             ++f_item;
@@ -912,11 +929,18 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         const int kk = kt * C::BK;
         if constexpr (FP4) {
             // register loads first, so waiting for them does not wait for the DMA
-            rc = *reinterpret_cast<const code_words_t*>(c_ptr + kt * (C::BK / 2));
-            if constexpr (EPL == 32)
-                rs = *reinterpret_cast<const uint16_t*>(s_ptr + kt * (C::BK / 16));
-            else
-                rs = s_ptr[kt * (C::BK / 16)];
+            if constexpr (SPLITB) {
+                // this thread's 16 code bytes to chunk tid, the row's scale word
+                // to word tid of the slot: each wave stages exactly the rows it
+                // decodes, so its own vmcnt orders the staging and the decode
+                static_assert(EPL == 32, "SPLITB: 16 code bytes per thread");
+                dma16(c_ptr + kt * (C::BK / 2), Bs + wave * 64);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(s_ptr + kt * (C::BK / 16)),
+                                                 (__attribute__((address_space(3))) void*)(Bs + C::NT + wave * 16), 4, 0, 0);
+            } else {
+                rc = *reinterpret_cast<const code_words_t*>(c_ptr + kt * (C::BK / 2));
+                rs = *reinterpret_cast<const uint32_t*>(s_ptr + kt * (C::BK / 16));
+            }
         } else if constexpr (B_DMA) {
             // tiled weights: K step kt is the kt-th 64x64 tile of the slab
             const int bk = BFMT == LMOE_BF16_TILED ? kt * 64 * 64 : kk;
@@ -936,17 +960,26 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             for (int j = 0; j < SA::N; ++j) ra[j] = *reinterpret_cast<const u32x4_t*>(a_ptr[j] + kk);
         }
     };
-    auto land = [&](u32x4_t* As, u32x4_t* Bs) __attribute__((always_inline)) {
+    // finishes the move of a K step: staged registers to LDS; NVFP4 decoded
+    // into the weight tile Bs (with SPLITB from the raw slot Raw)
+    auto land = [&](u32x4_t* As, u32x4_t* Bs, const u32x4_t* Raw = nullptr) __attribute__((always_inline)) {
         if constexpr (!C::DMA) {
 #pragma unroll
             for (int j = 0; j < SA::N; ++j) As[lds_idx<C>(SA::row(j, tid), SA::lchunk(j, tid))] = ra[j];
         }
         if constexpr (FP4) {
+            code_words_t codes = rc;
+            uint32_t sw = rs;
+            if constexpr (SPLITB) {
+                const u32x4_t v = Raw[tid];
+                codes = code_words_t{v[0], v[1], v[2], v[3]};
+                sw = reinterpret_cast<const uint32_t*>(Raw + C::NT)[tid];
+            }
             static_for<EPL / 8>([&](auto wc) __attribute__((always_inline)) {
                 constexpr int w = decltype(wc)::value;  // 8 elements; scale block w / 2
                 float pw, mt;
-                e4m3_parts((rs >> (8 * (w / 2))) & 0xFFu, pw, mt);
-                Bs[lds_idx<C>(tid / LPR, (tid % LPR) * (EPL / 8) + w)] = decode_e2m1x8(rc[w], pw, mt);
+                e4m3_parts((sw >> (8 * ((tid % LPR) * (EPL / 16) + w / 2))) & 0xFFu, pw, mt);
+                Bs[lds_idx<C>(tid / LPR, (tid % LPR) * (EPL / 8) + w)] = decode_e2m1x8(codes[w], pw, mt);
             });
         } else if constexpr (!B_DMA) {
 #pragma unroll
@@ -1081,6 +1114,54 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     constexpr int MAXAHEAD = PER_TILE > 0 ? S - 2 : 0;
     f32x16_t acc[C::TM][C::TN];
     zero_acc<C>(acc);
+    if constexpr (SPLITB) {
+        // NVFP4, three A stages.  Step q multiplies A stage q % 3 and decoded
+        // weight slot q % 2.  Its iteration waits for A stage q, issues step
+        // q + 2 (A by DMA; the raw codes and scale words by DMA into raw slot
+        // q % 2, the one step q's decode has finished with), multiplies, then
+        // waits for step q + 1's staging (issued an iteration earlier) and
+        // decodes it into weight slot (q + 1) % 2, last read by step q - 1,
+        // which every wave finished before this iteration's barrier.  A
+        // thread issues the same PT DMA instructions per step (A, codes,
+        // scales), so waiting for vmcnt(PT) leaves exactly the newest step in
+        // flight.  Every iteration issues a step, also past the end (the fill
+        // side then re-reads the block's last item, at valid addresses, into
+        // stages nothing multiplies), so the count never changes.
+        constexpr int ACH = C::BM * C::CPR, BCH = C::BN * C::CPR, PT = SA::N + 2;
+        u32x4_t* const bring = ring + S * ACH;
+        u32x4_t* const raw = bring + 2 * BCH;
+        fill_next(ring, raw);
+        fill_next(ring + ACH, raw + RAW);
+        wait_vmcnt<PT>();
+        land(nullptr, bring, raw);
+        int m_item = 0, m_kt = 0;
+        for (int q = 0; q < total; ++q) {
+            asm volatile("" ::: "memory");
+            if (q + 1 < total)
+                wait_vmcnt_lgkm0<PT>();
+            else
+                __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            fill_next(ring + ((q + 2) % S) * ACH, raw + (q & 1) * RAW);
+            mma_tile<C>(ring + (q % S) * ACH, bring + (q & 1) * BCH, acc, wm, wn, lane);
+            if (q + 1 < total) {
+                wait_vmcnt<PT>();
+                asm volatile("" ::: "memory");
+                land(nullptr, bring + ((q + 1) & 1) * BCH, raw + ((q + 1) & 1) * RAW);
+            }
+            if (++m_kt == nk) {
+                epilogue(mdesc, acc);
+                zero_acc<C>(acc);
+                ++m_item;
+                m_kt = 0;
+                mdesc = nk >= S - 1 ? fdesc : load_item(m_item);
+                fetch_scale(mdesc);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the steps issued past the end have landed
+        return;
+    }
 #pragma unroll
     for (int st = 0; st < S - 1; ++st) {
         if (st < total) {
@@ -1709,6 +1790,16 @@ hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_byte
 // with two 4-wave blocks per CU reached 6.8 TB/s; one 8-wave block per CU with
 // the same bytes in flight, 5.6.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
+    if (g.tt.bm == 192 && (g.b_fmt == LMOE_NVFP4 || g.b_fmt == LMOE_NVFP4_2D)) {
+        // NVFP4: three A stages and the decoded weights in a ring of their own
+        using C = MfmaCfg<192, 256, 2, 4, true, 64, 3>;
+        const int grid = persistent_grid() * C::MINB, nN = (g.N + C::BN - 1) / C::BN;
+        if (g.b_fmt == LMOE_NVFP4)
+            launch_grouped_fmt<C, LMOE_NVFP4, false>(g, grid, nN, s);
+        else
+            launch_grouped_fmt<C, LMOE_NVFP4_2D, false>(g, grid, nN, s);
+        return hipGetLastError();
+    }
     if (g.tt.bm == 192) return run_grouped<MfmaCfg<192, 256, 2, 4, true, 64, 2>>(g, s);
     if (g.tt.bm == 64 && g.N >= 1024) return run_grouped<MfmaCfg<64, 128, 2, 2, true, 64, 3, 2, true>>(g, s);
     if (g.tt.bm == 64) return run_grouped<MfmaCfg<64, 64, 2, 2, true, 64, 4, 2, true>>(g, s);
