@@ -175,6 +175,19 @@ def test_experts_spanning_several_tiles(name):
     assert counts[2] == counts[1] == cfg.T and errs["tokens_checked"] == cfg.T
 
 
+@pytest.mark.parametrize("experts", ["nvfp4", "nvfp4_2d"])
+def test_nvfp4_items_of_one_k_step(experts):
+    # l = 64: the NVFP4 expert GEMM1 has a single K step per item (its fill
+    # side moves to the next item on every step) and GEMM2 two; 100 rows per
+    # expert, so the 192-row tiles (three A stages) run, one item per block
+    cfg = TINY.with_(name=f"{experts}_one_k_step", T=400, d=256, l=64, E=4, k=1, f=128, f_s=0, act="bf16",
+                     experts=experts)
+    inp = small_inputs(cfg)
+    log(f"case {cfg.name}")
+    errs, _, _ = P.run_and_check(cfg, inp, report=log)
+    assert errs["tokens_checked"] == cfg.T
+
+
 @pytest.mark.parametrize("T,d", [(193, 256), (64, 1024)], ids=["router_kernel", "in_gemm_reduction"])
 def test_exact_logit_ties_break_to_lower_id(T, d):
     # x = 0 makes every logit equal to its bias; equal biases must pick the
