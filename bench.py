@@ -45,11 +45,39 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments, whitespace runs folded to one space
+    (string and character literals kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
+    """sha256 of the GEMM kernel sources' code (comments and layout left
+    out, so re-wording a comment does not void counters taken on the same
+    kernels)."""
     h = hashlib.sha256()
     for f in ("gemm_mfma.hip", "device_common.hpp", "lmoe_internal.hpp"):
-        with open(os.path.join(ROOT, "sparse_moe_layer_06_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_moe_layer_06_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -928,7 +928,6 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         const int kt = f_kt++;
         const int kk = kt * C::BK;
         if constexpr (FP4) {
-            // register loads first, so waiting for them does not wait for the DMA
             if constexpr (SPLITB) {
                 // this thread's 16 code bytes to chunk tid, the row's scale word
                 // to word tid of the slot: each wave stages exactly the rows it
@@ -938,6 +937,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
                 __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(s_ptr + kt * (C::BK / 16)),
                                                  (__attribute__((address_space(3))) void*)(Bs + C::NT + wave * 16), 4, 0, 0);
             } else {
+                // register loads first, so waiting for them does not wait for the DMA
                 rc = *reinterpret_cast<const code_words_t*>(c_ptr + kt * (C::BK / 2));
                 rs = *reinterpret_cast<const uint32_t*>(s_ptr + kt * (C::BK / 16));
             }

@@ -34,8 +34,9 @@ def test_traffic_reported_only_for_the_profiled_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic() is None
 
 
-def test_source_digest_covers_the_gemm_sources(tmp_path, monkeypatch):
-    # the digest changes with any byte of the GEMM kernel sources
+def test_source_digest_covers_the_gemm_code(tmp_path, monkeypatch):
+    # the digest changes with the code of the GEMM kernel sources, not with
+    # their comments or layout
     d0 = bench.kernel_source_digest()
     csrc = tmp_path / "sparse_moe_layer_06_amd" / "csrc"
     csrc.mkdir(parents=True)
@@ -44,8 +45,19 @@ def test_source_digest_covers_the_gemm_sources(tmp_path, monkeypatch):
             (csrc / name).write_bytes(fh.read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.kernel_source_digest() == d0
-    (csrc / "device_common.hpp").write_bytes((csrc / "device_common.hpp").read_bytes() + b"\n")
+    f = csrc / "device_common.hpp"
+    base = f.read_bytes()
+    f.write_bytes(base + b"\n// a comment\n/* another */\n")
+    assert bench.kernel_source_digest() == d0
+    f.write_bytes(base + b"\nconstexpr int kOneMore = 1;\n")
     assert bench.kernel_source_digest() != d0
+    f.write_bytes(base.replace(b"static_for", b"static_for_", 1))
+    assert bench.kernel_source_digest() != d0
+
+
+def test_code_only_keeps_literals_and_drops_comments():
+    src = 'int a = 1; // x\n/* y\n z */ const char* s = "//not a comment"; char c = \'"\';\n'
+    assert bench.code_only(src) == 'int a = 1; const char* s = "//not a comment"; char c = \'"\';'
 
 
 def test_oracle_timing_runs_single_threaded_on_host_inputs():
