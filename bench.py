@@ -240,6 +240,23 @@ def decode(cfg, steps, torch, B, synth, layout="tiled", graph=False):
                 **({"hipgraph": graph} if graph else {}))
 
 
+def grouped_bytes_per_launch(cfg):
+    """Algorithmic HBM bytes of one expert GEMM, the two launches averaged:
+    every expert's weights once (bf16, or NVFP4 codes plus one E4M3 scale
+    byte per 16 weights or per 16 x 16 block), the T k gathered input rows
+    and the T k output rows.  Only for unbiased routing, where T k >= 16 E
+    leaves no expert without rows (the chance is below e^-16 per expert);
+    None otherwise."""
+    if cfg.zipf_bias or cfg.T * cfg.k < 16 * cfg.E:
+        return None
+    per_weight = {"bf16": 2.0, "nvfp4": 0.5 + 1 / 16, "nvfp4_2d": 0.5 + 1 / 256}.get(cfg.experts)
+    if per_weight is None:
+        return None
+    weights = cfg.E * cfg.l * cfg.f * per_weight
+    rows = cfg.T * cfg.k * (cfg.l + cfg.f) * 2
+    return weights + rows
+
+
 def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
     """The other MFMA-bound workloads (same metric, reported beside the headline)."""
     inp, out, ms, _, kernels, _ = prefill(cfg, steps, warmup, torch, B, synth, layout)
@@ -257,6 +274,10 @@ def secondary(cfg, steps, warmup, torch, B, synth, layout="tiled"):
         ach = 2.0 * cfg.T * cfg.k * cfg.l * cfg.f / (g["avg_ms"] * 1e-3)
         res["grouped"] = dict(kernel=gname, avg_launch_ms=g["avg_ms"], achieved_tflops=ach / 1e12,
                               mfma_frac=ach / PEAK_BF16_FLOPS)
+        nbytes = grouped_bytes_per_launch(cfg)
+        if nbytes:
+            res["grouped"].update(alg_bytes_per_launch=nbytes,
+                                  hbm_frac=nbytes / (g["avg_ms"] * 1e-3) / PEAK_HBM_BYTES)
     f8 = kernels.get("fp8_gemm")
     # the fp8 products: the shared expert's two (2 T d f_s FLOPs each) and
     # the two projections (2 T d l each)
