@@ -710,13 +710,13 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float pw, float
     return r;
 }
 
-// Persistent grouped GEMM.  One block per CU walks a list of work items,
-// each one M tile of one expert (tiles[i] = {expert, first sorted row, rows})
-// times one BN-wide N tile, in M-tile-major order: item w is M tile w / nN,
-// N tile w % nN.  An XCD's blocks (block b runs on XCD b % 8) take its
-// contiguous range of items round-robin, so in each round they cover
-// consecutive items: all N tiles of an M tile (shared A rows) and the M
-// tiles of an expert (shared weights) are in L2 together.
+// Persistent grouped GEMM.  A grid of MINB blocks per CU walks a list of
+// work items, each one M tile of one expert (tiles[i] = {expert, first
+// sorted row, rows}) times one BN-wide N tile.  The list holds an expert's
+// items together (its M tiles times the nN N tiles); an XCD's blocks (block
+// b runs on XCD b % 8) take the XCD's contiguous range of the list
+// round-robin, so each round covers consecutive items, and within an expert
+// the M tiles that share a weight tile are neighbours (see load_item).
 //
 // The K steps of all the block's items form one flattened loop through the
 // LDS ring: the first stages of the next item are in flight while the
@@ -725,8 +725,9 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float pw, float
 // pay a pipeline fill each.
 //
 // A (gathered activation rows) always uses the tile's loader policy; B is a
-// dense bf16 expert stack (same policy) or NVFP4 codes (always through
-// registers, decoded on the way to LDS).
+// dense bf16 expert stack (same policy) or NVFP4 codes decoded into the LDS
+// weight tile, the codes staged through LDS-DMA (SPLITB, the prefill tiles)
+// or through registers (the other tiles).
 // A-row gather modes of the grouped GEMM.
 enum Gather : int { GATHER_NONE = 0, GATHER_SCALAR = 1, GATHER_LANE = 2 };
 
