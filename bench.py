@@ -21,6 +21,8 @@ Prints one JSON line:
   cpu_baseline  the CPU oracle on a bounded token sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-extra]
+       python bench.py --vendor-gemm-calibration   (the vendor library's GEMMs on the prefill shapes,
+                                                    and this library's kernels in isolation)
 """
 from __future__ import annotations
 
@@ -352,6 +354,82 @@ def cpu_baseline(cfg, inp, n_tokens, synth, torch):
                 single_thread=single)
 
 
+def vendor_gemm_calibration(torch, steps):
+    """torch's bf16 GEMMs on the prefill layer's products, random operands,
+    all contiguous: the two dense projections as plain GEMMs, and the expert
+    GEMM as a batched GEMM of 512 experts with 352 rows each (the mean rows
+    per expert at T = 8192, top-22; the same FLOPs, without the row gather
+    and the ragged tiles).  Not part of the layer: a measure of what the
+    vendor library sustains on this chip under the same clocks."""
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, dtype=bf, generator=g)
+
+    cases = {
+        "down_projection_router_shared": (lambda a, b: torch.matmul(a, b), (8192, 8192), (8192, 10752)),
+        "up_projection_shared": (lambda a, b: torch.matmul(a, b), (8192, 10240), (10240, 8192)),
+        "experts_batched": (lambda a, b: torch.bmm(a, b), (512, 352, 2048), (512, 2048, 2048)),
+    }
+    out = {}
+    for name, (fn, sa, sb) in cases.items():
+        a, b = rnd(*sa), rnd(*sb)
+        flops = 2.0 * a.numel() * sb[-1]
+        for _ in range(3):
+            fn(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[name] = dict(a=list(sa), b=list(sb), ms=ms, tflops=flops / (ms * 1e-3) / 1e12,
+                         mfma_frac=flops / (ms * 1e-3) / PEAK_BF16_FLOPS)
+        del a, b
+    torch.cuda.empty_cache()
+    return {"vendor_gemm_calibration": out, "own_kernels_in_isolation": own_kernels_in_isolation(torch, steps)}
+
+
+def own_kernels_in_isolation(torch, steps):
+    """The library's staged calls on the prefill workload, each repeated back
+    to back as the vendor GEMMs are above: the per-launch time of every
+    kernel of one call, in launch order (the layer's own timing runs them in
+    sequence, where the clock follows the whole step's power draw)."""
+    from sparse_moe_layer_06_amd import binding as B
+    from sparse_moe_layer_06_amd import synth
+    cfg = synth.CONFIGS["prefill_bf16"]
+    inp = synth.make_inputs(cfg, 0, "cuda")
+    ws = B.alloc_workspace(cfg)
+    pcfg, pinp = prepared(cfg, inp, "tiled", B)
+    r = B.project_route(pcfg, pinp, ws)
+    pm = B.permute(pcfg, r["idx"], ws)
+    Y = B.experts_ffn(pcfg, pinp, r["z"], pm["offsets"], pm["perm"], ws)
+    stages = {
+        "project_route": lambda: B.project_route(pcfg, pinp, ws),
+        "experts_ffn": lambda: B.experts_ffn(pcfg, pinp, r["z"], pm["offsets"], pm["perm"], ws),
+        "combine_up": lambda: B.combine_up(pcfg, pinp, Y, pm["inv"], r["gate"], r["hs"], ws, cfg.T),
+    }
+    res = {}
+    for name, fn in stages.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        with B.KernelTimer(capacity=16 * steps) as kt:
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+        recs = kt.records
+        n = len(recs) // steps
+        res[name] = [dict(kernel=recs[i][0], avg_ms=sum(recs[i + j * n][1] for j in range(steps)) / steps)
+                     for i in range(n)]
+    del inp, ws, pinp, r, pm, Y
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +448,9 @@ def main():
                     help="bf16 expert weights as packed by lmoe_pack_expert_weights (default) or row-major")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (scale for HBM byte counters) and exit")
+    ap.add_argument("--vendor-gemm-calibration", action="store_true",
+                    help="only time torch's bf16 GEMMs (the ROCm BLAS libraries) on the prefill layer's "
+                         "product shapes and exit: what the vendor library sustains on this chip")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer is benchmarked on a single MI355X "
@@ -388,6 +469,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+
+    if args.vendor_gemm_calibration:
+        print(json.dumps(vendor_gemm_calibration(torch, args.steps)), flush=True)
         return
 
     from sparse_moe_layer_06_amd import binding as B
