@@ -360,7 +360,7 @@ int latentmoe_forward(const lmoe_dims* dims, const void* x, const void* W_down,
  * the process ends; the call allocates and frees nothing.  The array of the
  * current device is used (stream must belong to it).  Returns
  * LMOE_ERR_WORKSPACE before any launch when lmoe_workspace_bytes(dims)
- * exceeds LMOE_STATIC_SCRATCH_BYTES (decode-sized layers fit: 76 MiB at
+ * exceeds LMOE_STATIC_SCRATCH_BYTES (decode-sized layers fit: 60 MiB at
  * T = 64, d = 8192, E = 512, k = 22); other arguments and errors as for
  * latentmoe_forward.  Every call on one GPU shares that GPU's array and
  * finds it holding the previous call's data (nothing in it needs to start
