@@ -21,7 +21,7 @@ TINY = synth.CONFIGS["tiny_f32"]
 CASES = {
     "bf16_deep": TINY.with_(name="bf16_deep", T=500, d=512, l=128, E=8, k=2, f=256, f_s=320,
                             act="bf16", experts="bf16"),
-    # 64x256 expert tiles with split-K items finished by the last block
+    # 64 x 128 expert tiles with split-K items finished by the last block
     "few_rows_wide": TINY.with_(name="few_rows_wide", T=24, d=4096, l=1024, E=32, k=4, f=1280, f_s=0,
                                 act="bf16", experts="bf16"),
     # full rounds of expert items, then tail items split along K
@@ -96,7 +96,7 @@ def test_graph_replays_match_eager(name):
 
 @pytest.mark.timeout(900)
 def test_graph_replays_match_eager_decode_full_size():
-    # 64 tokens, 512 experts, top-22 with the skewed bias: the 64x256 expert
+    # 64 tokens, 512 experts, top-22 with the skewed bias: the 64 x 128 expert
     # tiles with the split last round, expert weights in the tiled layout
     cfg = synth.CONFIGS["decode_bf16_zipf"]
     log(f"case graph {cfg}")

@@ -50,17 +50,24 @@ SMALL = {
                                   act="bf16", experts="bf16"),
     "few_rows_deepK": TINY.with_(name="few_rows_deepK", T=20, d=2048, l=512, E=16, k=4, f=512, f_s=0,
                                  act="bf16", experts="bf16"),
-    # few rows per expert and outputs >= 1024 wide (the 64x256 expert tiles),
-    # N = 1280 not a multiple of 256
+    # few rows per expert and outputs >= 1024 wide (the 64 x 128 expert
+    # tiles, two blocks per CU): fewer items than blocks, so GEMM1 runs whole
+    # items and GEMM2 splits them along K
     "few_rows_wide": TINY.with_(name="few_rows_wide", T=24, d=4096, l=1024, E=32, k=4, f=1280, f_s=0,
                                 act="bf16", experts="bf16"),
-    # more 64 x 256 expert items than blocks, not in whole rounds (576 items
-    # in GEMM1, 320 in GEMM2 over 256 blocks): full rounds, then the tail
-    # items split along K
+    # the same with both expert GEMMs' outputs (f = 1216, l = 1088) ending in
+    # a partly filled 128-wide N tile
+    "few_rows_wide_ragged": TINY.with_(name="few_rows_wide_ragged", T=24, d=4352, l=1088, E=32, k=4, f=1216,
+                                       f_s=0, act="bf16", experts="bf16"),
+    # more 64 x 128 expert items than blocks, not in whole rounds (about 1150
+    # items in GEMM1 and 640 in GEMM2 over 512 blocks on 256 CUs): full
+    # rounds, then the tail items split along K
     "few_rows_rounds": TINY.with_(name="few_rows_rounds", T=64, d=5120, l=1280, E=64, k=8, f=2304, f_s=0,
                                     act="bf16", experts="bf16"),
     "nvfp4_few_wide": TINY.with_(name="nvfp4_few_wide", T=16, d=4096, l=1024, E=16, k=2, f=1280, f_s=0,
                                  act="bf16", experts="nvfp4"),
+    "nvfp4_few_wide_ragged": TINY.with_(name="nvfp4_few_wide_ragged", T=16, d=4352, l=1088, E=16, k=2, f=1216,
+                                        f_s=0, act="bf16", experts="nvfp4"),
     # top-k beyond one register slot per lane: k = 100 of E = 256, and E = 1024
     "k100_E256": TINY.with_(name="k100_E256", T=16, d=256, l=64, E=256, k=100, f=64, act="bf16",
                             experts="bf16"),
@@ -93,8 +100,8 @@ SMALL = {
                                act="bf16", experts="nvfp4", proj_fp8=True, shared_fp8=True, router_latent=True),
     "fp8_proj_zipf": TINY.with_(name="fp8_proj_zipf", T=64, d=2048, l=512, E=64, k=6, f=256, f_s=0,
                                 act="bf16", experts="bf16", proj_fp8=True, zipf_bias=True),
-    # NVFP4 with 16 x 16 scale blocks: 192-row tiles, and the split-K 64 x 256
-    # tiles with a ragged N = 1280
+    # NVFP4 with 16 x 16 scale blocks: 192-row tiles, and the 64 x 128 tiles
+    # of few rows (split along K in GEMM2)
     "nvfp4_2d_deep": TINY.with_(name="nvfp4_2d_deep", T=300, d=512, l=128, E=4, k=2, f=256, f_s=0,
                                 act="bf16", experts="nvfp4_2d"),
     "nvfp4_2d_deep192": TINY.with_(name="nvfp4_2d_deep192", T=400, d=512, l=128, E=4, k=2, f=256, f_s=0,
@@ -299,12 +306,12 @@ def test_permutation_matches_oracle_on_both_paths(T, k, E):
     assert np.array_equal(p["inv"].cpu().numpy(), ri)
 
 
-@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "few_rows_wide", "few_rows_rounds",
-                                  "k100_E256", "E1_bf16"])
+@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "few_rows_wide", "few_rows_wide_ragged",
+                                  "few_rows_rounds", "k100_E256", "E1_bf16"])
 def test_tiled_expert_weights(name):
     # the packed layout holds the same values: outputs bit-identical to the
     # row-major stacks, and the oracle (row-major weights) agrees
-    # (few_rows_wide, few_rows_rounds: 64 x 256 tiles with the split tail)
+    # (few_rows_wide, few_rows_wide_ragged, few_rows_rounds: 64 x 128 tiles with the split tail)
     cfg = SMALL[name]
     log(f"case tiled {name}")
     inp = small_inputs(cfg)
