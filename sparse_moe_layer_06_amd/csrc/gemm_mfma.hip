@@ -1113,6 +1113,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     constexpr int S = C::STAGES, STG = C::STAGE_CHUNKS, AOFF = C::BM * C::CPR;
     constexpr int PER_TILE = (C::DMA && B_DMA) ? SA::N + SB::N : 0;
     constexpr int MAXAHEAD = PER_TILE > 0 ? S - 2 : 0;
+    // whole items through two DMA stages (the 192-row tiles): the late-barrier loop below
+    constexpr bool LATE = !SPLITB && !SK && S == 2 && PER_TILE > 0;
     f32x16_t acc[C::TM][C::TN];
     zero_acc<C>(acc);
     if constexpr (SPLITB) {
@@ -1161,6 +1163,95 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             }
         }
         __builtin_amdgcn_s_waitcnt(0);  // the steps issued past the end have landed
+        return;
+    }
+    if constexpr (LATE) {
+        // Two stages, both operands by DMA, the barrier late: step q's last
+        // 16-wide sub-step waits for step q + 1's tile (the only DMA in
+        // flight), then the barrier, after which every wave holds step q's
+        // last fragments in registers, so stage q % 2 takes step q + 2's
+        // DMA; step q + 1's first fragments are read under the last
+        // sub-step's MFMAs instead of after the next barrier.
+        constexpr int KS = C::BK / 16, NM = C::TM * C::TN, NR = C::TM + C::TN;
+        bf16x8_t af[2][C::TM], bfr[2][C::TN];
+        // A fragment row starts at a multiple of 32, so the swizzle of every
+        // row this lane reads is that of lane & 31: one address per operand
+        // and sub-step, the 32-row blocks at constant offsets from it
+        static_assert(C::CPR == 8 && C::WM % 32 == 0 && C::WN % 32 == 0, "late-barrier loop: K step 64");
+        const int l31 = lane & 31, hi = lane >> 5, sw = swz_bits<C::CPR>(l31);
+        const int arow = (wm * C::WM + l31) * C::CPR, brow = (wn * C::WN + l31) * C::CPR;
+        auto read = [&](const u32x4_t* As, const u32x4_t* Bs, int ks, int b) __attribute__((always_inline)) {
+            const int c = (ks * 2 + hi) ^ sw;
+            const u32x4_t* pa = As + arow + c;
+            const u32x4_t* pb = Bs + brow + c;
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = as_bf16x8(pa[tm * 32 * C::CPR]);
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn) bfr[b][tn] = as_bf16x8(pb[tn * 32 * C::CPR]);
+        };
+        auto mfmas = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn) acc[tm][tn] = mfma32x32x16(bfr[b][tn], af[b][tm], acc[tm][tn]);
+        };
+        auto interleave = [&]() __attribute__((always_inline)) {  // MFMA m, then its share of the reads
+            static_for<NM>([&](auto mc) __attribute__((always_inline)) {
+                constexpr int m = decltype(mc)::value, r = (m + 1) * NR / NM - m * NR / NM;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+            });
+        };
+        fill_next(ring, ring + AOFF);
+        if (total > 1) {
+            fill_next(ring + STG, ring + STG + AOFF);
+            wait_vmcnt<PER_TILE>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        read(ring, ring + AOFF, 0, 0);
+        int m_item = 0, m_kt = 0;
+        for (int q = 0; q < total; ++q) {
+            u32x4_t* const cs = ring + (q & 1) * STG;
+            const u32x4_t* const ns = ring + ((q + 1) & 1) * STG;
+            static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int ks = decltype(kc)::value, b = ks & 1;
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this sub-step's fragments
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (ks + 1 < KS) {
+                    read(cs, cs + AOFF, ks + 1, b ^ 1);
+                    mfmas(b);
+                    interleave();
+                } else {
+                    // also on the block's last step (the reads then fetch a
+                    // stage nothing multiplies): no branch around the MFMAs
+                    asm volatile("" ::: "memory");
+                    wait_vmcnt<0>();  // step q + 1 (and any epilogue stores) complete
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    // stage q % 2 is free: every wave holds step q's last
+                    // fragments in registers
+                    if (q + 2 < total) fill_next(cs, cs + AOFF);
+                    __builtin_amdgcn_sched_barrier(0);
+                    read(ns, ns + AOFF, 0, b ^ 1);
+                    mfmas(b);
+                    interleave();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if (++m_kt == nk) {
+                epilogue(mdesc, acc);
+                zero_acc<C>(acc);
+                ++m_item;
+                m_kt = 0;
+                // the fill side is on the next item already unless items
+                // are one K step long (it is two steps ahead here)
+                mdesc = nk >= 2 ? fdesc : load_item(m_item);
+                fetch_scale(mdesc);
+            }
+        }
         return;
     }
 #pragma unroll
