@@ -49,9 +49,10 @@ paragraph):
 
 Precision: all arithmetic in float64 on the exact values of the stored
 inputs; the one intermediate taken at its stored precision is the latent z
-a latent router reads (the layer stores z before the router reads it).  The one place floating point decides an integer (the top-k) takes
-the decision on float32 logits, the precision the layer stores its logits in;
-ties in float32 are broken by the lower expert id.
+a latent router reads (the layer stores z before the router reads it).  The
+one place floating point decides an integer (the top-k) takes the decision
+on float32 logits, the precision the layer stores its logits in; ties in
+float32 are broken by the lower expert id.
 
 Data format: bf16 tensors are numpy uint16 arrays of bf16 bit patterns;
 fp32 tensors are float32 arrays.  NVFP4 expert weights are byte arrays of
