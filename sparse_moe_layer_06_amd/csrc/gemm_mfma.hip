@@ -1293,6 +1293,241 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     }
 }
 
+// Prefill NVFP4 expert GEMM with the weights decoded in registers.
+//
+// 192 x 256 tiles over 8 waves of 96 x 64 (2 x 4).  Each K step moves by
+// LDS-DMA into a ring of NB = D + 1 stages: the gathered activation rows
+// (24 KB) and the tile's raw weight codes and scale words (thread t stages
+// 16 code bytes of weight row t / 2, half t % 2, and that row's 4-byte
+// scale word: 10 KB).  A lane then reads from LDS the 32 codes of its own
+// weight row that its MFMA fragments of the step hold, with the row's
+// scale word, and decodes a sub-step's 8 codes to bf16 in registers right
+// before the MFMAs that take them: no decoded weight tile is written to or
+// read from LDS.  The K positions inside a step are renumbered (sub-step s
+// of lane half h takes k = 32 h + 8 s .. +8, the activation fragments
+// read from LDS take the same k), which leaves the product unchanged and
+// makes a lane's codes of a step one 16-byte chunk.  Step q's iteration
+// waits for its own DMA, passes the barrier, issues step q + D into the
+// stage step q - 1 used, then multiplies.  Every thread issues the same PT
+// DMA instructions per step, also past the block's last step (the fill
+// side then re-reads the last item at valid addresses into stages nothing
+// uses), so waiting for vmcnt((D - 1) PT) leaves exactly steps q + 1 ..
+// q + D - 1 in flight (epilogue stores issued since can only make that
+// wait longer).  The work list and the items' order are the persistent
+// grouped GEMM's (whole items, N-tile-major within an expert).
+template <int BFMT, int GATHER, int D>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedGemm g, int nN) {
+    using C = MfmaCfg<192, 256, 2, 4, true, 64, D + 1>;
+    using SA = Slots<C, C::BM>;
+    constexpr int NB = D + 1, ACH = C::BM * C::CPR, KS = C::BK / 16;
+    // raw slot: a 16-byte code chunk per thread, then a scale word per thread
+    constexpr int RAWC = C::NT + C::NT / 4;
+    constexpr int PT = SA::N + 2;  // DMA instructions per step and thread
+    static_assert(BFMT == LMOE_NVFP4 || BFMT == LMOE_NVFP4_2D, "NVFP4 weights");
+    static_assert(C::TM == 3 && C::TN == 2 && KS == 4 && SA::CPW % 64 == 0 && C::NT == 2 * C::BN,
+                  "8 waves of 96 x 64, two threads per weight row");
+    static_assert(D >= 1 && (D - 1) * PT < 64, "vmcnt range");
+    __shared__ u32x4_t ring[NB * (ACH + RAWC)];
+    const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, hi = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int N = g.N, K = g.K, nk = K / C::BK;
+
+    const int W = *g.tt.tile_count * nN;
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+    const int per = W >> 3, rem = W & 7;
+    const int first = x * per + min(x, rem);
+    const int end = first + per + (x < rem ? 1 : 0);
+    if (first + slot >= end) return;
+    const int n_items = (end - 1 - first - slot) / nbx + 1;
+    const int total = n_items * nk;
+    const int w_first = first + slot;
+    // descriptor {expert, first sorted row, rows, n0} of this block's item i
+    // (clamped to the last), the expert's items taken N-tile-major
+    auto load_item = [&](int i) __attribute__((always_inline)) {
+        const int w = __builtin_amdgcn_readfirstlane(w_first + min(i, n_items - 1) * nbx);
+        const int t = w / nN;
+        const i32x4_t d = sload4(g.tt.tiles + t);
+        const int nt = d.w >> 16, t0 = t - (d.w & 0xFFFF);
+        const int local = w - t0 * nN;
+        const i32x4_t e = sload4(g.tt.tiles + t0 + local % nt);
+        return make_int4(e.x, e.y, e.z, (local / nt) * C::BN);
+    };
+
+    // ---- fill side
+    constexpr int RPI = SA::RPI;
+    static_assert(GATHER != GATHER_SCALAR || RPI == 8, "scalar gather: 8 rows per DMA instruction");
+    auto a_row = [&](int j, int row0, int rows) __attribute__((always_inline)) {
+        const int p = row0 + min(SA::row(j, tid), rows - 1);
+        if constexpr (GATHER == GATHER_NONE) {
+            return p;
+        } else if constexpr (GATHER == GATHER_SCALAR) {
+            const int rb = __builtin_amdgcn_readfirstlane((wave * SA::CPW + j * 64) / C::CPR);
+            const int q0 = __builtin_amdgcn_readfirstlane(min(row0 + rb, g.n_rows - RPI));
+            const int idx = min(max(p - q0, 0), RPI - 1);
+            const i32x8_t r = sload8(g.a_row_map + q0);
+            int v = r[0];
+#pragma unroll
+            for (int t = 1; t < 8; ++t) v = (idx == t) ? r[t] : v;
+            return v / g.a_row_div;
+        } else {
+            return g.a_row_map[p] / g.a_row_div;
+        }
+    };
+    const uint16_t* a_ptr[SA::N];
+    const uint8_t* c_ptr;  // this thread's 16 code bytes of K step 0: weight row tid / 2, half tid % 2
+    const uint8_t* s_ptr;  // that row's scale words
+    auto setup = [&](const int4& d) __attribute__((always_inline)) {
+        const int e = d.x, row0 = d.y, rows = d.z, n0 = d.w;
+#pragma unroll
+        for (int j = 0; j < SA::N; ++j) {
+            const int ar = a_row(j, row0, rows);
+            a_ptr[j] = (const uint16_t*)g.A + (int64_t)ar * g.lda + SA::lchunk(j, tid) * 8;
+        }
+        const int64_t n = (int64_t)e * N + min(n0 + (tid >> 1), N - 1);
+        c_ptr = g.B_codes + n * (K / 2) + 16 * (tid & 1);
+        // 2-D blocks: N is a multiple of 16, so weight row n of the stack
+        // has scale row n / 16 of [E][N/16][K/16]
+        s_ptr = g.B_scales + (BFMT == LMOE_NVFP4_2D ? n >> 4 : n) * (K / 16);
+    };
+    int4 fdesc = load_item(0);
+    int4 fnext = load_item(1);
+    int f_item = 0, f_kt = 0;
+    setup(fdesc);
+    // issues the next K step of the fill item by DMA: the activation rows
+    // into stage As, the codes and scale words into raw slot Raw
+    auto fill = [&](u32x4_t* As, u32x4_t* Raw) __attribute__((always_inline)) {
+        if (f_kt == nk) {  // next item: its descriptor was fetched one item ahead
+            ++f_item;
+            f_kt = 0;
+            fdesc = fnext;
+            setup(fdesc);
+            fnext = load_item(f_item + 1);
+        }
+        const int kt = f_kt++;
+#pragma unroll
+        for (int j = 0; j < SA::N; ++j) dma16(a_ptr[j] + kt * C::BK, SA::dst(As, wave, j));
+        dma16(c_ptr + kt * (C::BK / 2), Raw + wave * 64);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(s_ptr + kt * (C::BK / 16)),
+                                         (__attribute__((address_space(3))) void*)(Raw + C::NT + wave * 16), 4, 0, 0);
+    };
+
+    // ---- multiply side
+    f32x16_t acc[C::TM][C::TN];
+    zero_acc<C>(acc);
+    bf16x8_t af[2][C::TM], bfr[2][C::TN];
+    const int arow = (wm * C::WM + l31) * C::CPR, asw = swz_bits<8>(l31);  // rows tm * 32 + l31: l31's swizzle
+    // sub-step ks of lane half h: logical chunk 4 h + ks, k = 32 h + 8 ks .. +8
+    auto read = [&](const u32x4_t* As, int ks, int b) __attribute__((always_inline)) {
+        const u32x4_t* pa = As + arow + ((4 * hi + ks) ^ asw);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = as_bf16x8(pa[tm * 32 * C::CPR]);
+    };
+    // the same k of the lane's weight row: code word ks, scale block 2 h + ks / 2
+    auto decode = [&](const u32x4_t (&bc)[C::TN], const uint32_t (&bs)[C::TN], int ks, int b)
+                      __attribute__((always_inline)) {
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+            float pw, mt;
+            e4m3_parts((bs[tn] >> (8 * (2 * hi + (ks >> 1)))) & 0xFFu, pw, mt);
+            bfr[b][tn] = as_bf16x8(decode_e2m1x8(bc[tn][ks], pw, mt));
+        }
+    };
+    // the lane's weight row of group tn: wn * 64 + tn * 32 + l31, its chunk
+    // (and scale word) 2 row + half in the raw slot
+    const int rraw = 2 * (wn * C::WN + l31) + hi;
+    auto mma = [&](const u32x4_t* As, const u32x4_t* Raw) __attribute__((always_inline)) {
+        u32x4_t bc[C::TN];
+        uint32_t bs[C::TN];
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+            bc[tn] = Raw[rraw + 64 * tn];
+            bs[tn] = reinterpret_cast<const uint32_t*>(Raw + C::NT)[rraw + 64 * tn];
+        }
+        read(As, 0, 0);
+        decode(bc, bs, 0, 0);
+        static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int ks = decltype(kc)::value, b = ks & 1;
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this sub-step's activation fragments
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ks + 1 < KS) {
+                read(As, ks + 1, b ^ 1);
+                decode(bc, bs, ks + 1, b ^ 1);
+            }
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn)
+                    acc[tm][tn] = mfma32x32x16(bfr[b][tn], af[b][tm], acc[tm][tn]);
+            if constexpr (ks + 1 < KS) {  // MFMA m, then a fragment read and a share of the decode
+                static_for<C::TM * C::TN>([&](auto mc) __attribute__((always_inline)) {
+                    constexpr int m = decltype(mc)::value;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (m < C::TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    float mscale = 1.0f;
+    auto epilogue = [&](const int4& d) __attribute__((always_inline)) {
+        const int row0 = d.y, rows = d.z, n0 = d.w;
+        static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
+            constexpr int tm = decltype(tmc)::value;
+            const int ml = wm * C::WM + tm * 32 + l31;
+            if (ml < rows) {
+                uint16_t* crow = (uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc;
+                static_for<C::TN * 4>([&](auto tqc) __attribute__((always_inline)) {
+                    constexpr int tn = decltype(tqc)::value / 4, q = decltype(tqc)::value % 4;
+                    const int n = n0 + wn * C::WN + tn * 32 + q * 8 + hi * 4;
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[i] = acc[tm][tn][q * 4 + i] * mscale;
+                        if (g.epi == EPI_RELU2) {
+                            v[i] = fmaxf(v[i], 0.f);
+                            v[i] *= v[i];
+                        }
+                    }
+                    uint2 o;
+                    o.x = pack_bf16x2(v[0], v[1]);
+                    o.y = pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<uint2*>(crow + n) = o;
+                });
+            }
+        });
+    };
+
+    u32x4_t* const raw = ring + NB * ACH;
+    static_for<D>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        fill(ring + u * ACH, raw + u * RAWC);
+    });
+    int4 mdesc = fdesc;
+    mscale = sload_f32(g.B_ts + mdesc.x);
+    int m_kt = 0;
+    for (int q0 = 0; q0 < total; q0 += NB) {  // total is a multiple of NB (nk is)
+        static_for<NB>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value, un = (u + D) % NB;
+            asm volatile("" ::: "memory");
+            wait_vmcnt<(D - 1) * PT>();    // this thread's loads of step q
+            __builtin_amdgcn_s_barrier();  // everyone's; and step q - 1 is done
+            asm volatile("" ::: "memory");
+            fill(ring + un * ACH, raw + un * RAWC);
+            mma(ring + u * ACH, raw + u * RAWC);
+            if (++m_kt == nk) {
+                epilogue(mdesc);
+                zero_acc<C>(acc);
+                m_kt = 0;
+                mdesc = fdesc;  // the fill side is D < nk steps ahead, in the next item
+                mscale = sload_f32(g.B_ts + mdesc.x);
+            }
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the steps issued past the end have landed
+}
+
 // ---------------------------------------------------------------------------
 // FP8 dense GEMM (the shared expert with E4M3 weights and activations)
 // ---------------------------------------------------------------------------
@@ -1683,6 +1918,22 @@ static void launch_grouped_any(const GroupedGemm& g, int grid, int nN, hipStream
         launch_grouped_fmt<C, LMOE_BF16, SK>(g, grid, nN, s);
 }
 
+// Steps in flight of the register-decode NVFP4 expert GEMM.
+constexpr int kFp4RegD = 3;
+
+template <int BFMT>
+static void launch_grouped_fp4reg(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
+    if (!g.a_row_map)
+        LMOE_LAUNCH("grouped_gemm_nvfp4", s,
+                    grouped_gemm_nvfp4_reg_kernel<BFMT, GATHER_NONE, kFp4RegD><<<grid, 512, 0, s>>>(g, nN));
+    else if (g.n_rows >= 8)
+        LMOE_LAUNCH("grouped_gemm_nvfp4", s,
+                    grouped_gemm_nvfp4_reg_kernel<BFMT, GATHER_SCALAR, kFp4RegD><<<grid, 512, 0, s>>>(g, nN));
+    else
+        LMOE_LAUNCH("grouped_gemm_nvfp4", s,
+                    grouped_gemm_nvfp4_reg_kernel<BFMT, GATHER_LANE, kFp4RegD><<<grid, 512, 0, s>>>(g, nN));
+}
+
 // Split-K scheduling for the 64 x 128 few-rows tiles when the caller gave
 // the partial-sum buffer and enough counters; whole items otherwise.
 template <class C>
@@ -1882,6 +2133,16 @@ hipError_t launch_fp8_gemm(const Fp8Gemm& g, void* splitk_ws, size_t splitk_byte
 // with two 4-wave blocks per CU reached 6.8 TB/s; one 8-wave block per CU with
 // the same bytes in flight, 5.6.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
+    if (g.tt.bm == 192 && (g.b_fmt == LMOE_NVFP4 || g.b_fmt == LMOE_NVFP4_2D) && g.N % 256 == 0 &&
+        (g.K / 64) % (kFp4RegD + 1) == 0 && g.K / 64 > kFp4RegD) {
+        // NVFP4 decoded in registers
+        const int grid = persistent_grid(), nN = g.N / 256;
+        if (g.b_fmt == LMOE_NVFP4)
+            launch_grouped_fp4reg<LMOE_NVFP4>(g, grid, nN, s);
+        else
+            launch_grouped_fp4reg<LMOE_NVFP4_2D>(g, grid, nN, s);
+        return hipGetLastError();
+    }
     if (g.tt.bm == 192 && (g.b_fmt == LMOE_NVFP4 || g.b_fmt == LMOE_NVFP4_2D)) {
         // NVFP4: three A stages and the decoded weights in a ring of their own
         using C = MfmaCfg<192, 256, 2, 4, true, 64, 3>;

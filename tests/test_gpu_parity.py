@@ -35,6 +35,22 @@ SMALL = {
                                act="bf16", experts="bf16"),
     "nvfp4_deep192": TINY.with_(name="nvfp4_deep192", T=400, d=512, l=128, E=4, k=2, f=256, f_s=0,
                                 act="bf16", experts="nvfp4"),
+    # the register-weight expert GEMM (192-row tiles, N a multiple of 256, K
+    # steps a multiple of 4): ragged experts in one or two tiles, one item per
+    # block; and 64 experts over 3 N tiles with K of 4 and 12 steps, several
+    # items per block
+    "bf16_regw": TINY.with_(name="bf16_regw", T=600, d=1024, l=256, E=4, k=2, f=512, f_s=256,
+                            act="bf16", experts="bf16"),
+    "bf16_regw_items": TINY.with_(name="bf16_regw_items", T=4096, d=1024, l=256, E=64, k=6, f=768, f_s=0,
+                                  act="bf16", experts="bf16"),
+    # the register-decode NVFP4 expert GEMM (192-row tiles, N a multiple of
+    # 256, K steps a multiple of 4), 1-D and 2-D scale blocks
+    "nvfp4_regw": TINY.with_(name="nvfp4_regw", T=600, d=1024, l=256, E=4, k=2, f=512, f_s=0,
+                             act="bf16", experts="nvfp4"),
+    "nvfp4_2d_regw": TINY.with_(name="nvfp4_2d_regw", T=600, d=1024, l=256, E=4, k=2, f=512, f_s=0,
+                                act="bf16", experts="nvfp4_2d"),
+    "nvfp4_regw_items": TINY.with_(name="nvfp4_regw_items", T=4096, d=1024, l=256, E=64, k=6, f=768, f_s=0,
+                                   act="bf16", experts="nvfp4"),
     "nvfp4_sparse": TINY.with_(name="nvfp4_sparse", T=70, d=256, l=64, E=16, k=3, f=128, f_s=0,
                                act="bf16", experts="nvfp4"),
     "zipf_small": TINY.with_(name="zipf_small", T=64, d=512, l=128, E=64, k=6, f=256, f_s=0,
@@ -166,7 +182,7 @@ def test_all_tokens_to_one_expert():
 
 
 @pytest.mark.parametrize("name", ["bf16_deep", "nvfp4_deep", "nvfp4_2d_deep", "bf16_deep192", "nvfp4_deep192",
-                                  "nvfp4_2d_deep192"])
+                                  "nvfp4_2d_deep192", "bf16_regw", "nvfp4_regw", "nvfp4_2d_regw"])
 def test_experts_spanning_several_tiles(name):
     # every token routed to the same two experts (a large bias on them): 500
     # rows each, so each expert takes two full 192-row tiles and a 116-row
@@ -306,7 +322,7 @@ def test_permutation_matches_oracle_on_both_paths(T, k, E):
     assert np.array_equal(p["inv"].cpu().numpy(), ri)
 
 
-@pytest.mark.parametrize("name", ["bf16_deep", "zipf_small", "few_rows_ragged", "few_rows_wide", "few_rows_wide_ragged",
+@pytest.mark.parametrize("name", ["bf16_deep", "bf16_regw", "bf16_regw_items", "zipf_small", "few_rows_ragged", "few_rows_wide", "few_rows_wide_ragged",
                                   "few_rows_rounds", "k100_E256", "E1_bf16"])
 def test_tiled_expert_weights(name):
     # the packed layout holds the same values: outputs bit-identical to the
