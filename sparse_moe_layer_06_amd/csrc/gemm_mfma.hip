@@ -693,6 +693,19 @@ __device__ __forceinline__ void e4m3_parts(uint32_t b, float& pw, float& mt) {
     if (b & 0x80u) mt = -mt;
 }
 
+// The same split of an E4M3 scale already converted to fp32 (exactly, by the
+// hardware's OCP E4M3 conversion): pw keeps its exponent bits, mt takes its
+// sign and mantissa with the exponent of 1, so pw * mt is the scale for every
+// nonzero finite value (an E4M3 subnormal is a normal fp32).  A zero scale
+// gives pw = 1, mt = 0; a NaN one mt = NaN.
+__device__ __forceinline__ void e4m3_split_f32(float s, float& pw, float& mt) {
+    const uint32_t u = __float_as_uint(s);
+    const bool zero = (u & 0x7FFFFFFFu) == 0u;
+    pw = zero ? 1.f : __uint_as_float(u & 0x7F800000u);
+    mt = zero ? 0.f : __uint_as_float((u & 0x807FFFFFu) | 0x3F800000u);
+    if (s != s) mt = s;
+}
+
 // 8 E2M1 codes (one 32-bit word, element i in bits 4i..4i+3, so byte j holds
 // elements 2j and 2j+1) -> 8 bf16.  The hardware conversion scales by the
 // power of two exactly; the product with mt has at most 6 significant bits
@@ -1424,12 +1437,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
         for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = as_bf16x8(pa[tm * 32 * C::CPR]);
     };
     // the same k of the lane's weight row: code word ks, scale block 2 h + ks / 2
-    auto decode = [&](const u32x4_t (&bc)[C::TN], const uint32_t (&bs)[C::TN], int ks, int b)
+    // (byte ks / 2 of the scale word shifted right by 16 h)
+    auto decode = [&](const u32x4_t (&bc)[C::TN], const uint32_t (&bsh)[C::TN], int ks, int b)
                       __attribute__((always_inline)) {
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn) {
+            const float sc = (ks >> 1) ? __builtin_amdgcn_cvt_f32_fp8((int)bsh[tn], 1)
+                                       : __builtin_amdgcn_cvt_f32_fp8((int)bsh[tn], 0);
             float pw, mt;
-            e4m3_parts((bs[tn] >> (8 * (2 * hi + (ks >> 1)))) & 0xFFu, pw, mt);
+            e4m3_split_f32(sc, pw, mt);
             bfr[b][tn] = as_bf16x8(decode_e2m1x8(bc[tn][ks], pw, mt));
         }
     };
@@ -1442,7 +1458,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn) {
             bc[tn] = Raw[rraw + 64 * tn];
-            bs[tn] = reinterpret_cast<const uint32_t*>(Raw + C::NT)[rraw + 64 * tn];
+            bs[tn] = reinterpret_cast<const uint32_t*>(Raw + C::NT)[rraw + 64 * tn] >> (16 * hi);
         }
         read(As, 0, 0);
         decode(bc, bs, 0, 0);
