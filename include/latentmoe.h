@@ -288,10 +288,13 @@ int lmoe_timing_stop(lmoe_kernel_time* out, int capacity, int* count);
 /*
  * Repacks one routed-expert bf16 weight stack W [E][rows][cols] (row-major:
  * W1 with rows = f, cols = l; W2 with rows = l, cols = f) into the
- * LMOE_BF16_TILED layout: 64-row slabs of 64x64 tiles, each tile stored in
- * the order the expert GEMMs keep it in LDS, so that weight streaming reads
- * whole contiguous kilobytes.  A one-time preparation of static weights, not
- * part of the forward.  packed must hold E*rows*cols*2 bytes, may not
+ * LMOE_BF16_TILED layout, the order of the expert GEMMs' matrix-core
+ * fragments: in 16-byte chunks,
+ *   packed[e][rb][kt][s][l] = W[e][32 rb + l % 32][64 kt + 16 s + 8 (l / 32) .. +8]
+ * for 32-row blocks rb, 64-wide K steps kt, 16-wide sub-steps s < 4 and
+ * lanes l < 64, so that each sub-step of a block is one contiguous kilobyte
+ * that a wave loads in one instruction, into registers or into LDS.  A
+ * one-time preparation of static weights, not part of the forward.  packed must hold E*rows*cols*2 bytes, may not
  * overlap W, and both must be 16-byte aligned.  rows and cols must be
  * positive multiples of 64 (LMOE_ERR_SHAPE).  Asynchronous on stream.
  */

@@ -189,7 +189,10 @@ __device__ __forceinline__ void wait_tiles_barrier(int ahead) {
 // issued one group earlier (lgkmcnt(0) while only those are in flight: they
 // have landed by then); the compiler would otherwise wait for all reads
 // right before the MFMAs, including the ones just issued.
-template <class C>
+// BFRAG: the B tile is in fragment order (packed expert weights): the 32-row
+// block rb's fragment of sub-step ks is the 64 chunks at (4 rb + ks) * 64,
+// lane l's at + l.
+template <class C, bool BFRAG = false>
 __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u32x4_t* __restrict__ Bs,
                                          f32x16_t (&acc)[C::TM][C::TN], int wm, int wn, int lane) {
     constexpr int KS = C::BK / 16, NM = C::TM * C::TN, NR = C::TM + C::TN;
@@ -201,7 +204,8 @@ __device__ __forceinline__ void mma_tile(const u32x4_t* __restrict__ As, const u
             af[b][tm] = as_bf16x8(As[lds_idx<C>(wm * C::WM + tm * 32 + (lane & 31), ch)]);
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn)
-            bfr[b][tn] = as_bf16x8(Bs[lds_idx<C>(wn * C::WN + tn * 32 + (lane & 31), ch)]);
+            bfr[b][tn] = as_bf16x8(BFRAG ? Bs[((wn * C::WN / 32 + tn) * KS + ks) * 64 + lane]
+                                         : Bs[lds_idx<C>(wn * C::WN + tn * 32 + (lane & 31), ch)]);
     };
     read(0, 0);
     static_for<KS>([&](auto kc) __attribute__((always_inline)) {
@@ -840,7 +844,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     constexpr bool FP4 = BFMT == LMOE_NVFP4 || BFMT == LMOE_NVFP4_2D;
     constexpr bool B_DMA = C::DMA && !FP4;
     static_assert(BFMT != LMOE_BF16_TILED || (C::DMA && C::BK == 64 && C::BN % 64 == 0),
-                  "tiled weights: LDS-DMA, K step 64, whole 64-row slabs");
+                  "packed weights: LDS-DMA, K step 64, whole 64-row tiles");
     using SA = Slots<C, C::BM>;
     using SB = Slots<C, C::BN>;
     // NVFP4 weights: each weight row's K step is split over LPR lanes, EPL
@@ -907,14 +911,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
             const int64_t srow = BFMT == LMOE_NVFP4_2D ? n >> 4 : n;
             s_ptr = g.B_scales + srow * (K / 16);
         } else if constexpr (BFMT == LMOE_BF16_TILED) {
-            // 64-row slabs of 64x64 tiles, each stored in the swizzled order of
-            // the LDS tile (the swizzle repeats every 16 rows and n0 is a
-            // multiple of 64): LDS chunk q comes from tile chunk q of its slab
+            // packed weights: the 4 KB fragment-ordered K step of each 32-row
+            // block, the K steps of a block consecutive; LDS chunk q of the
+            // tile (block q / 256 of the tile, chunk q % 256 of its K step)
+            // comes from the same chunk of the packed step
 #pragma unroll
             for (int j = 0; j < SB::N; ++j) {
-                const int n = min(n0 + SB::row(j, tid), N - 1);
-                const int pc = SB::chunk(j, tid) % C::CPR;
-                b_ptr[j] = (const uint16_t*)g.B + ((int64_t)e * N + (n & ~63)) * K + (n & 63) * 64 + pc * 8;
+                const int q = min(SB::chunk(j, tid), C::BN * C::CPR - 1);
+                const int rb = min(n0 / 32 + q / 256, N / 32 - 1);
+                b_ptr[j] = (const uint16_t*)g.B + (((int64_t)e * (N / 32) + rb) * nk * 256 + q % 256) * 8;
             }
         } else {
 #pragma unroll
@@ -956,8 +961,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
                 rs = *reinterpret_cast<const uint32_t*>(s_ptr + kt * (C::BK / 16));
             }
         } else if constexpr (B_DMA) {
-            // tiled weights: K step kt is the kt-th 64x64 tile of the slab
-            const int bk = BFMT == LMOE_BF16_TILED ? kt * 64 * 64 : kk;
+            // packed weights: K step kt of a 32-row block is 4 KB past step kt - 1
+            const int bk = BFMT == LMOE_BF16_TILED ? kt * 32 * 64 : kk;
 #pragma unroll
             for (int j = 0; j < SB::N; ++j)
                 if (SB::active(j, tid)) dma16<C::B_NT ? 2 : 0>(b_ptr[j] + bk, SB::dst(Bs, wave, j));
@@ -1196,11 +1201,17 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         auto read = [&](const u32x4_t* As, const u32x4_t* Bs, int ks, int b) __attribute__((always_inline)) {
             const int c = (ks * 2 + hi) ^ sw;
             const u32x4_t* pa = As + arow + c;
-            const u32x4_t* pb = Bs + brow + c;
 #pragma unroll
             for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = as_bf16x8(pa[tm * 32 * C::CPR]);
+            if constexpr (BFMT == LMOE_BF16_TILED) {  // fragment-ordered weight tile
+                const u32x4_t* pb = Bs + (wn * C::WN / 32 * KS + ks) * 64 + lane;
 #pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn) bfr[b][tn] = as_bf16x8(pb[tn * 32 * C::CPR]);
+                for (int tn = 0; tn < C::TN; ++tn) bfr[b][tn] = as_bf16x8(pb[tn * KS * 64]);
+            } else {
+                const u32x4_t* pb = Bs + brow + c;
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn) bfr[b][tn] = as_bf16x8(pb[tn * 32 * C::CPR]);
+            }
         };
         auto mfmas = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
@@ -1281,7 +1292,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
         u32x4_t* ns = ring + nxt * STG;
         if (more) fill_next(ns, ns + AOFF);
         u32x4_t* cs = ring + cur * STG;
-        mma_tile<C>(cs, cs + AOFF, acc, wm, wn, lane);
+        mma_tile<C, BFMT == LMOE_BF16_TILED>(cs, cs + AOFF, acc, wm, wn, lane);
         if (more) land(ns, ns + AOFF);
         cur = (cur + 1 == S) ? 0 : cur + 1;
         nxt = (nxt + 1 == S) ? 0 : nxt + 1;
@@ -1304,6 +1315,205 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
     if constexpr (SK) {
         if (m_item < n_items && sk_t >= 0) sk_finish(mdesc, acc);
     }
+}
+
+// Prefill expert GEMM with the packed weights streamed into registers.
+//
+// 192 x 256 tiles over 8 waves of 192 x 32: each wave owns one 32-row block
+// of weights (output columns) of the tile and every one of its 192
+// activation rows.  The packed layout keeps each block's K step as four
+// 1 KB sub-step fragments in lane order, so a wave reads its weight
+// fragments straight into the registers the MFMAs take with four contiguous
+// 1 KB loads per K step: the weights need no LDS and no barrier.  (The same
+// fragments read from a row-major stack touch 32 rows per load; measured on
+// L2-resident data that streams 3.4 times slower per byte.)  The gathered
+// activation rows, which all 8 waves read, go through a ring of NB = D + 1
+// LDS stages by DMA (24 KB per K step).  Step q's iteration waits for its
+// own loads, passes the barrier, issues step q + D (A by DMA into the stage
+// step q - 1 used, the weights into the register set step q - 1 used), then
+// multiplies.
+//
+// Every thread issues the same PT loads per step, also past the block's
+// last step (the fill side then re-reads the last item, at valid
+// addresses, into stages and registers nothing uses), so waiting for
+// vmcnt((D - 1) PT) leaves exactly steps q + 1 .. q + D - 1 in flight.
+// Epilogue stores issued since count among the outstanding operations too,
+// so after an epilogue that wait can only be longer than needed, never
+// short.  The work list and the items' order are the persistent grouped
+// GEMM's (whole items, N-tile-major within an expert).
+template <int BFMT, int GATHER, int D>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g, int nN) {
+    using C = MfmaCfg<192, 256, 1, 8, true, 64, D + 1>;
+    using SA = Slots<C, C::BM>;
+    constexpr int NB = D + 1, ACH = C::BM * C::CPR, KS = C::BK / 16;
+    constexpr int PT = SA::N + KS;  // vector-memory instructions per step and thread
+    static_assert(BFMT == LMOE_BF16_TILED, "packed bf16 weights");
+    static_assert(C::TN == 1 && C::WN == 32 && SA::CPW % 64 == 0, "8 waves of 192 x 32");
+    static_assert(D >= 1 && (D - 1) * PT < 64, "vmcnt range");
+    __shared__ u32x4_t ring[NB * ACH];
+    const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, hi = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = g.N, K = g.K, nk = K / C::BK;
+
+    const int W = *g.tt.tile_count * nN;
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+    const int per = W >> 3, rem = W & 7;
+    const int first = x * per + min(x, rem);
+    const int end = first + per + (x < rem ? 1 : 0);
+    if (first + slot >= end) return;
+    const int n_items = (end - 1 - first - slot) / nbx + 1;
+    const int total = n_items * nk;
+    const int w_first = first + slot;
+    // descriptor {expert, first sorted row, rows, n0} of this block's item i
+    // (clamped to the last), the expert's items taken N-tile-major
+    auto load_item = [&](int i) __attribute__((always_inline)) {
+        const int w = __builtin_amdgcn_readfirstlane(w_first + min(i, n_items - 1) * nbx);
+        const int t = w / nN;
+        const i32x4_t d = sload4(g.tt.tiles + t);
+        const int nt = d.w >> 16, t0 = t - (d.w & 0xFFFF);
+        const int local = w - t0 * nN;
+        const i32x4_t e = sload4(g.tt.tiles + t0 + local % nt);
+        return make_int4(e.x, e.y, e.z, (local / nt) * C::BN);
+    };
+
+    // ---- fill side
+    constexpr int RPI = SA::RPI;
+    static_assert(GATHER != GATHER_SCALAR || RPI == 8, "scalar gather: 8 rows per DMA instruction");
+    auto a_row = [&](int j, int row0, int rows) __attribute__((always_inline)) {
+        const int p = row0 + min(SA::row(j, tid), rows - 1);
+        if constexpr (GATHER == GATHER_NONE) {
+            return p;
+        } else if constexpr (GATHER == GATHER_SCALAR) {
+            const int rb = __builtin_amdgcn_readfirstlane((wave * SA::CPW + j * 64) / C::CPR);
+            const int q0 = __builtin_amdgcn_readfirstlane(min(row0 + rb, g.n_rows - RPI));
+            const int idx = min(max(p - q0, 0), RPI - 1);
+            const i32x8_t r = sload8(g.a_row_map + q0);
+            int v = r[0];
+#pragma unroll
+            for (int t = 1; t < 8; ++t) v = (idx == t) ? r[t] : v;
+            return v / g.a_row_div;
+        } else {
+            return g.a_row_map[p] / g.a_row_div;
+        }
+    };
+    // this lane's chunk of the wave's weight block: sub-step ks of K step kt
+    // at b_ptr + kt * 2048 + ks * 512 (bf16 elements)
+    const uint16_t* a_ptr[SA::N];
+    const uint16_t* b_ptr;
+    auto setup = [&](const int4& d) __attribute__((always_inline)) {
+        const int e = d.x, row0 = d.y, rows = d.z, n0 = d.w;
+#pragma unroll
+        for (int j = 0; j < SA::N; ++j) {
+            const int ar = a_row(j, row0, rows);
+            a_ptr[j] = (const uint16_t*)g.A + (int64_t)ar * g.lda + SA::lchunk(j, tid) * 8;
+        }
+        const int rb = min(n0 / 32 + wave, N / 32 - 1);
+        b_ptr = (const uint16_t*)g.B + (((int64_t)e * (N / 32) + rb) * nk * 256 + lane) * 8;
+    };
+    int4 fdesc = load_item(0);
+    int4 fnext = load_item(1);
+    int f_item = 0, f_kt = 0;
+    setup(fdesc);
+    u32x4_t breg[NB][KS];
+    // issues the next K step of the fill item: the weights into registers
+    // br, the activation rows by DMA into stage As
+    auto fill = [&](u32x4_t* As, u32x4_t (&br)[KS]) __attribute__((always_inline)) {
+        if (f_kt == nk) {  // next item: its descriptor was fetched one item ahead
+            ++f_item;
+            f_kt = 0;
+            fdesc = fnext;
+            setup(fdesc);
+            fnext = load_item(f_item + 1);
+        }
+        const int kt = f_kt++;
+        const uint16_t* bp = b_ptr + kt * 2048;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) br[s] = *reinterpret_cast<const u32x4_t*>(bp + s * 512);
+#pragma unroll
+        for (int j = 0; j < SA::N; ++j) dma16(a_ptr[j] + kt * C::BK, SA::dst(As, wave, j));
+    };
+
+    // ---- multiply side
+    f32x16_t acc[C::TM][1];
+    zero_acc<C>(acc);
+    bf16x8_t af[2][C::TM];
+    const int arow = l31 * C::CPR, asw = swz_bits<8>(l31);  // A row tm * 32 + l31 has l31's swizzle
+    auto read = [&](const u32x4_t* As, int ks, int b) __attribute__((always_inline)) {
+        const u32x4_t* pa = As + arow + ((ks * 2 + hi) ^ asw);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = as_bf16x8(pa[tm * 32 * C::CPR]);
+    };
+    auto mma = [&](const u32x4_t* As, const u32x4_t (&br)[KS]) __attribute__((always_inline)) {
+        read(As, 0, 0);
+        static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int ks = decltype(kc)::value, b = ks & 1;
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this sub-step's fragments
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ks + 1 < KS) read(As, ks + 1, b ^ 1);
+            const bf16x8_t bf = as_bf16x8(br[ks]);
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm) acc[tm][0] = mfma32x32x16(bf, af[b][tm], acc[tm][0]);
+            if constexpr (ks + 1 < KS) {  // MFMA tm, then the next sub-step's fragment tm
+                static_for<C::TM>([&](auto) __attribute__((always_inline)) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    auto epilogue = [&](const int4& d) __attribute__((always_inline)) {
+        const int row0 = d.y, rows = d.z, n0 = d.w;
+        static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
+            constexpr int tm = decltype(tmc)::value;
+            const int ml = tm * 32 + l31;
+            if (ml < rows) {
+                uint16_t* crow = (uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc;
+                static_for<4>([&](auto qc) __attribute__((always_inline)) {
+                    constexpr int q = decltype(qc)::value;
+                    const int n = n0 + wave * C::WN + q * 8 + hi * 4;
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[i] = acc[tm][0][q * 4 + i];
+                        if (g.epi == EPI_RELU2) {
+                            v[i] = fmaxf(v[i], 0.f);
+                            v[i] *= v[i];
+                        }
+                    }
+                    uint2 o;
+                    o.x = pack_bf16x2(v[0], v[1]);
+                    o.y = pack_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<uint2*>(crow + n) = o;
+                });
+            }
+        });
+    };
+
+    static_for<D>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        fill(ring + u * ACH, breg[u]);
+    });
+    int4 mdesc = fdesc;
+    int m_kt = 0;
+    for (int q0 = 0; q0 < total; q0 += NB) {  // total is a multiple of NB (nk is)
+        static_for<NB>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value, un = (u + D) % NB;
+            asm volatile("" ::: "memory");
+            wait_vmcnt<(D - 1) * PT>();  // this thread's loads of step q
+            __builtin_amdgcn_s_barrier();  // everyone's; and step q - 1 is done
+            asm volatile("" ::: "memory");
+            fill(ring + un * ACH, breg[un]);
+            mma(ring + u * ACH, breg[u]);
+            if (++m_kt == nk) {
+                epilogue(mdesc);
+                zero_acc<C>(acc);
+                m_kt = 0;
+                mdesc = fdesc;  // the fill side is D < nk steps ahead, in the next item
+            }
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the steps issued past the end have landed
 }
 
 // Prefill NVFP4 expert GEMM with the weights decoded in registers.
@@ -1821,27 +2031,24 @@ hipError_t launch_quantize_blocks_mxfp8(const uint16_t* src, int64_t rows, int c
 // Repacking of bf16 expert weights into the tiled layout
 // ---------------------------------------------------------------------------
 //
-// W [E][rows][cols] row-major -> 64-row slabs of 64x64 tiles,
-// P[e][slab][kt][r][pc] (16-byte chunks) = W[e][64 slab + r][64 kt + 8 (pc ^ swz(r)) ..+8]:
-// each tile is stored exactly as the grouped GEMM's LDS tile holds it (K step
-// 64, 8 chunks per row, the swizzle of those tiles), so one LDS-DMA
-// instruction of the GEMM reads 1 KB of contiguous weights.
-constexpr int kPackTile = 64;
-using PackCfg = MfmaCfg<64, 64, 2, 2, true, kPackTile>;  // the tile geometry (CPR 8) of the packed layout
-
+// W [E][rows][cols] row-major -> MFMA-fragment order (16-byte chunks):
+// P[e][rb][kt][ks][l] = W[e][32 rb + l % 32][64 kt + 16 ks + 8 (l / 32) ..+8]
+// for 32-row blocks rb, 64-wide K steps kt, 16-wide sub-steps ks and lanes
+// l < 64: exactly the 8 values lane l of a 32x32x16 MFMA takes for weight
+// row l % 32, so each sub-step of a block is 1 KB of contiguous weights,
+// one wave-wide 16-byte load (into registers, or by LDS-DMA into a tile
+// that keeps the same order), and a block's K steps follow each other.
 __global__ __launch_bounds__(256) void pack_experts_kernel(const u32x4_t* __restrict__ W, u32x4_t* __restrict__ P,
                                                            int64_t n_chunks, int rows, int cols) {
     const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (o >= n_chunks) return;
-    constexpr int CPR = PackCfg::CPR;
-    const int kts = cols / kPackTile, slabs = rows / kPackTile;
-    const int pc = (int)(o % CPR), r = (int)((o / CPR) % kPackTile);
-    const int64_t tile = o / (CPR * kPackTile);  // (e, slab, kt)
-    const int kt = (int)(tile % kts);
-    const int64_t es = tile / kts;              // e * slabs + slab
-    const int64_t row = (es / slabs) * rows + (es % slabs) * kPackTile + r;
-    const int c = pc ^ swz_bits<CPR>(r);
-    P[o] = W[row * (cols / 8) + kt * CPR + c];
+    const int kts = cols / 64, rbs = rows / 32;
+    const int l = (int)(o % 64), ks = (int)((o / 64) % 4);
+    const int64_t step = o / 256;  // (e, rb, kt)
+    const int kt = (int)(step % kts);
+    const int64_t erb = step / kts;  // e * rbs + rb
+    const int64_t row = (erb / rbs) * rows + (erb % rbs) * 32 + l % 32;
+    P[o] = W[row * (cols / 8) + kt * 8 + 2 * ks + l / 32];
 }
 
 hipError_t launch_pack_experts(const void* W, void* P, int64_t E, int rows, int cols, hipStream_t s) {
@@ -1934,8 +2141,10 @@ static void launch_grouped_any(const GroupedGemm& g, int grid, int nN, hipStream
         launch_grouped_fmt<C, LMOE_BF16, SK>(g, grid, nN, s);
 }
 
-// Steps in flight of the register-decode NVFP4 expert GEMM.
+// Steps in flight of the register-decode NVFP4 expert GEMM and of the
+// register-weight bf16 one.
 constexpr int kFp4RegD = 3;
+constexpr int kBregD = 3;
 
 template <int BFMT>
 static void launch_grouped_fp4reg(const GroupedGemm& g, int grid, int nN, hipStream_t s) {
@@ -2167,6 +2376,21 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, hipStream_t s) {
             launch_grouped_fmt<C, LMOE_NVFP4, false>(g, grid, nN, s);
         else
             launch_grouped_fmt<C, LMOE_NVFP4_2D, false>(g, grid, nN, s);
+        return hipGetLastError();
+    }
+    if (g.tt.bm == 192 && g.b_fmt == LMOE_BF16_TILED && g.N % 256 == 0 && (g.K / 64) % (kBregD + 1) == 0 &&
+        g.K / 64 > kBregD) {
+        // packed weights streamed into registers
+        const int grid = persistent_grid(), nN = g.N / 256;
+        if (!g.a_row_map)
+            LMOE_LAUNCH("grouped_gemm", s,
+                        grouped_gemm_breg_kernel<LMOE_BF16_TILED, GATHER_NONE, kBregD><<<grid, 512, 0, s>>>(g, nN));
+        else if (g.n_rows >= 8)
+            LMOE_LAUNCH("grouped_gemm", s,
+                        grouped_gemm_breg_kernel<LMOE_BF16_TILED, GATHER_SCALAR, kBregD><<<grid, 512, 0, s>>>(g, nN));
+        else
+            LMOE_LAUNCH("grouped_gemm", s,
+                        grouped_gemm_breg_kernel<LMOE_BF16_TILED, GATHER_LANE, kBregD><<<grid, 512, 0, s>>>(g, nN));
         return hipGetLastError();
     }
     if (g.tt.bm == 192) return run_grouped<MfmaCfg<192, 256, 2, 4, true, 64, 2>>(g, s);
