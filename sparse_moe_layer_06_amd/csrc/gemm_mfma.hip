@@ -1328,15 +1328,16 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 // fragments read from a row-major stack touch 32 rows per load; measured on
 // L2-resident data that streams 3.4 times slower per byte.)  The gathered
 // activation rows, which all 8 waves read, go through a ring of NB = D + 1
-// LDS stages by DMA (24 KB per K step).  Step q's iteration waits for its
-// own loads, passes the barrier, issues step q + D (A by DMA into the stage
-// step q - 1 used, the weights into the register set step q - 1 used), then
-// multiplies.
+// LDS stages by DMA (24 KB per K step).  The barrier comes late: the last
+// 16-wide sub-step of step q waits for step q + 1's loads and passes the
+// barrier, refills stage q with step q + NB's activation rows, reads step
+// q + 1's first fragments under its own MFMAs and then loads step q + NB's
+// weights into the register set those MFMAs have just used.
 //
 // Every thread issues the same PT loads per step, also past the block's
 // last step (the fill side then re-reads the last item, at valid
 // addresses, into stages and registers nothing uses), so waiting for
-// vmcnt((D - 1) PT) leaves exactly steps q + 1 .. q + D - 1 in flight.
+// vmcnt((D - 1) PT) leaves exactly steps q + 2 .. q + D in flight.
 // Epilogue stores issued since count among the outstanding operations too,
 // so after an epilogue that wait can only be longer than needed, never
 // short.  The work list and the items' order are the persistent grouped
@@ -1349,7 +1350,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
     constexpr int PT = SA::N + KS;  // vector-memory instructions per step and thread
     static_assert(BFMT == LMOE_BF16_TILED, "packed bf16 weights");
     static_assert(C::TN == 1 && C::WN == 32 && SA::CPW % 64 == 0, "8 waves of 192 x 32");
-    static_assert(D >= 1 && (D - 1) * PT < 64, "vmcnt range");
+    static_assert(D >= 1 && D * PT < 64, "vmcnt range");
     __shared__ u32x4_t ring[NB * ACH];
     const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, hi = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1415,9 +1416,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
     int f_item = 0, f_kt = 0;
     setup(fdesc);
     u32x4_t breg[NB][KS];
-    // issues the next K step of the fill item: the weights into registers
-    // br, the activation rows by DMA into stage As
-    auto fill = [&](u32x4_t* As, u32x4_t (&br)[KS]) __attribute__((always_inline)) {
+    // issue the next K step of the fill item: fill_a its activation rows by
+    // DMA into stage As (moving to the next item first when the current one
+    // is done), fill_b its weights into registers br; no other vector-memory
+    // operation comes between the two
+    int f_kk = 0;
+    auto fill_a = [&](u32x4_t* As) __attribute__((always_inline)) {
         if (f_kt == nk) {  // next item: its descriptor was fetched one item ahead
             ++f_item;
             f_kt = 0;
@@ -1425,12 +1429,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
             setup(fdesc);
             fnext = load_item(f_item + 1);
         }
-        const int kt = f_kt++;
-        const uint16_t* bp = b_ptr + kt * 2048;
+        f_kk = f_kt++;
+#pragma unroll
+        for (int j = 0; j < SA::N; ++j) dma16(a_ptr[j] + f_kk * C::BK, SA::dst(As, wave, j));
+    };
+    auto fill_b = [&](u32x4_t (&br)[KS]) __attribute__((always_inline)) {
+        const uint16_t* bp = b_ptr + f_kk * 2048;
 #pragma unroll
         for (int s = 0; s < KS; ++s) br[s] = *reinterpret_cast<const u32x4_t*>(bp + s * 512);
-#pragma unroll
-        for (int j = 0; j < SA::N; ++j) dma16(a_ptr[j] + kt * C::BK, SA::dst(As, wave, j));
     };
 
     // ---- multiply side
@@ -1443,23 +1449,41 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
 #pragma unroll
         for (int tm = 0; tm < C::TM; ++tm) af[b][tm] = as_bf16x8(pa[tm * 32 * C::CPR]);
     };
-    auto mma = [&](const u32x4_t* As, const u32x4_t (&br)[KS]) __attribute__((always_inline)) {
-        read(As, 0, 0);
+    // One K step, the barrier late: sub-step ks reads the fragments of
+    // ks + 1 under its MFMAs.  The last sub-step first waits for step q + 1
+    // (its own loads, then the barrier for everyone's), refills stage q with
+    // step q + NB's activation rows (every wave has read stage q's last
+    // fragments by then), reads step q + 1's first fragments under its
+    // MFMAs, and then loads step q + NB's weights into the register set
+    // those MFMAs have just taken theirs from.
+    auto mma = [&](u32x4_t* As, u32x4_t (&br)[KS], const u32x4_t* Asn) __attribute__((always_inline)) {
         static_for<KS>([&](auto kc) __attribute__((always_inline)) {
             constexpr int ks = decltype(kc)::value, b = ks & 1;
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this sub-step's fragments
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (ks + 1 < KS) read(As, ks + 1, b ^ 1);
+            if constexpr (ks + 1 < KS) {
+                read(As, ks + 1, b ^ 1);
+            } else {
+                asm volatile("" ::: "memory");
+                wait_vmcnt<(D - 1) * PT>();    // this thread's loads of step q + 1
+                __builtin_amdgcn_s_barrier();  // everyone's
+                asm volatile("" ::: "memory");
+                fill_a(As);
+                __builtin_amdgcn_sched_barrier(0);
+                read(Asn, 0, b ^ 1);
+            }
             const bf16x8_t bf = as_bf16x8(br[ks]);
 #pragma unroll
             for (int tm = 0; tm < C::TM; ++tm) acc[tm][0] = mfma32x32x16(bf, af[b][tm], acc[tm][0]);
-            if constexpr (ks + 1 < KS) {  // MFMA tm, then the next sub-step's fragment tm
-                static_for<C::TM>([&](auto) __attribute__((always_inline)) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                });
-            }
+            static_for<C::TM>([&](auto) __attribute__((always_inline)) {  // MFMA tm, then fragment tm
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            });
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ks + 1 == KS) {
+                fill_b(br);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         });
     };
     auto epilogue = [&](const int4& d) __attribute__((always_inline)) {
@@ -1490,26 +1514,28 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
         });
     };
 
-    static_for<D>([&](auto uc) __attribute__((always_inline)) {
+    // steps 0 .. D in flight, then step 0's first fragments
+    static_for<NB>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        fill(ring + u * ACH, breg[u]);
+        fill_a(ring + u * ACH);
+        fill_b(breg[u]);
     });
+    asm volatile("" ::: "memory");
+    wait_vmcnt<D * PT>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read(ring, 0, 0);
     int4 mdesc = fdesc;
     int m_kt = 0;
     for (int q0 = 0; q0 < total; q0 += NB) {  // total is a multiple of NB (nk is)
         static_for<NB>([&](auto uc) __attribute__((always_inline)) {
-            constexpr int u = decltype(uc)::value, un = (u + D) % NB;
-            asm volatile("" ::: "memory");
-            wait_vmcnt<(D - 1) * PT>();  // this thread's loads of step q
-            __builtin_amdgcn_s_barrier();  // everyone's; and step q - 1 is done
-            asm volatile("" ::: "memory");
-            fill(ring + un * ACH, breg[un]);
-            mma(ring + u * ACH, breg[u]);
+            constexpr int u = decltype(uc)::value;
+            mma(ring + u * ACH, breg[u], ring + ((u + 1) % NB) * ACH);
             if (++m_kt == nk) {
                 epilogue(mdesc);
                 zero_acc<C>(acc);
                 m_kt = 0;
-                mdesc = fdesc;  // the fill side is D < nk steps ahead, in the next item
+                mdesc = fdesc;  // the fill side is NB <= nk steps ahead, in the next item
             }
         });
     }
