@@ -1340,8 +1340,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void grouped_gemm_kernel(GroupedGem
 // vmcnt((D - 1) PT) leaves exactly steps q + 2 .. q + D in flight.
 // Epilogue stores issued since count among the outstanding operations too,
 // so after an epilogue that wait can only be longer than needed, never
-// short.  The work list and the items' order are the persistent grouped
-// GEMM's (whole items, N-tile-major within an expert).
+// short.  The output tile leaves through LDS (see the epilogue) in whole
+// 512-byte rows.  The work list and the items' order are the persistent
+// grouped GEMM's (whole items, N-tile-major within an expert).
 template <int BFMT, int GATHER, int D>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g, int nN) {
     using C = MfmaCfg<192, 256, 1, 8, true, 64, D + 1>;
@@ -1351,7 +1352,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
     static_assert(BFMT == LMOE_BF16_TILED, "packed bf16 weights");
     static_assert(C::TN == 1 && C::WN == 32 && SA::CPW % 64 == 0, "8 waves of 192 x 32");
     static_assert(D >= 1 && D * PT < 64, "vmcnt range");
-    __shared__ u32x4_t ring[NB * ACH];
+    // one LDS array for the activation ring and the output staging (with a
+    // second array the compiler waits for all DMA in flight before every
+    // LDS read, unable to tell the two apart; with one it still waits once
+    // per item, before the first staging write)
+    constexpr int CPITCH = C::BN * 2 + 16;  // bytes per output row staged in LDS
+    __shared__ u32x4_t ring[NB * ACH + C::BM / 2 * CPITCH / 16];
+    uint8_t* const cbuf = reinterpret_cast<uint8_t*>(ring + NB * ACH);
     const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, hi = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = g.N, K = g.K, nk = K / C::BK;
@@ -1486,16 +1493,31 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
             }
         });
     };
+    // Barrier for LDS traffic only: this wave's LDS accesses complete, then
+    // the workgroup barrier.  (__syncthreads would also wait for every load
+    // in flight, the steps prefetched for the next item.)
+    auto lds_barrier = []() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // The output tile goes out through LDS, half of its rows at a time: each
+    // wave writes its 32 columns of 96 rows (a lane's 4 consecutive values
+    // per 8-byte write), then every thread stores 16-byte pieces of whole
+    // 512-byte output rows, so a wave's store covers 2 rows instead of 32.
+    // Rows are padded by 16 bytes in LDS.  Two barriers per half: the
+    // writes are complete before the reads, the reads before the next
+    // half's writes.
     auto epilogue = [&](const int4& d) __attribute__((always_inline)) {
         const int row0 = d.y, rows = d.z, n0 = d.w;
-        static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
-            constexpr int tm = decltype(tmc)::value;
-            const int ml = tm * 32 + l31;
-            if (ml < rows) {
-                uint16_t* crow = (uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc;
+        static_for<2>([&](auto hc) __attribute__((always_inline)) {
+            constexpr int half = decltype(hc)::value;
+            static_for<C::TM / 2>([&](auto tc) __attribute__((always_inline)) {
+                constexpr int t = decltype(tc)::value, tm = half * (C::TM / 2) + t;
+                uint32_t* crow = reinterpret_cast<uint32_t*>(cbuf) + (t * 32 + l31) * (CPITCH / 4);
                 static_for<4>([&](auto qc) __attribute__((always_inline)) {
                     constexpr int q = decltype(qc)::value;
-                    const int n = n0 + wave * C::WN + q * 8 + hi * 4;
                     float v[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -1508,9 +1530,21 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
                     uint2 o;
                     o.x = pack_bf16x2(v[0], v[1]);
                     o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(crow + n) = o;
+                    *reinterpret_cast<uint2*>(crow + (wave * C::WN + q * 8 + hi * 4) / 2) = o;
                 });
+            });
+            lds_barrier();
+            constexpr int PIECES = C::BM / 2 * (C::BN / 8);  // 16-byte pieces of the half tile
+            static_assert(PIECES % C::NT == 0, "whole passes");
+#pragma unroll
+            for (int i = 0; i < PIECES / C::NT; ++i) {
+                const int c = tid + i * C::NT, r = c / (C::BN / 8), p = c % (C::BN / 8);
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cbuf + r * CPITCH + p * 16);
+                const int ml = half * (C::BM / 2) + r;
+                if (ml < rows)
+                    *reinterpret_cast<u32x4_t*>((uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc + n0 + p * 8) = v;
             }
+            lds_barrier();
         });
     };
 
