@@ -1610,7 +1610,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
     static_assert(C::TM == 3 && C::TN == 2 && KS == 4 && SA::CPW % 64 == 0 && C::NT == 2 * C::BN,
                   "8 waves of 96 x 64, two threads per weight row");
     static_assert(D >= 1 && (D - 1) * PT < 64, "vmcnt range");
-    __shared__ u32x4_t ring[NB * (ACH + RAWC)];
+    // one LDS array for the ring and the output staging (see the epilogue)
+    constexpr int CPITCH = C::BN * 2 + 16;  // bytes per output row staged in LDS
+    __shared__ u32x4_t ring[NB * (ACH + RAWC) + 32 * CPITCH / 16];
+    uint8_t* const cbuf = reinterpret_cast<uint8_t*>(ring + NB * (ACH + RAWC));
     const int tid = threadIdx.x, lane = tid & 63, l31 = lane & 31, hi = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -1757,16 +1760,27 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
         });
     };
     float mscale = 1.0f;
+    // Barrier for LDS traffic only (__syncthreads would also wait for the
+    // steps prefetched for the next item).
+    auto lds_barrier = []() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // The output tile leaves through LDS 32 rows at a time (the LDS left
+    // beside the ring holds 32 padded rows): the waves that own those rows
+    // write their values (a lane's 4 consecutive columns per 8-byte write),
+    // then every thread stores 16-byte pieces of whole 512-byte rows, so a
+    // wave's store covers 2 rows instead of 32.
     auto epilogue = [&](const int4& d) __attribute__((always_inline)) {
         const int row0 = d.y, rows = d.z, n0 = d.w;
-        static_for<C::TM>([&](auto tmc) __attribute__((always_inline)) {
-            constexpr int tm = decltype(tmc)::value;
-            const int ml = wm * C::WM + tm * 32 + l31;
-            if (ml < rows) {
-                uint16_t* crow = (uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc;
+        static_for<C::WAVES_M * C::TM>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value, tm = r % C::TM;
+            if (wm == r / C::TM) {
+                uint32_t* crow = reinterpret_cast<uint32_t*>(cbuf) + l31 * (CPITCH / 4);
                 static_for<C::TN * 4>([&](auto tqc) __attribute__((always_inline)) {
                     constexpr int tn = decltype(tqc)::value / 4, q = decltype(tqc)::value % 4;
-                    const int n = n0 + wn * C::WN + tn * 32 + q * 8 + hi * 4;
                     float v[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -1779,9 +1793,21 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
                     uint2 o;
                     o.x = pack_bf16x2(v[0], v[1]);
                     o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(crow + n) = o;
+                    *reinterpret_cast<uint2*>(crow + (wn * C::WN + tn * 32 + q * 8 + hi * 4) / 2) = o;
                 });
             }
+            lds_barrier();
+            constexpr int PIECES = 32 * (C::BN / 8);  // 16-byte pieces of 32 rows
+            static_assert(PIECES % C::NT == 0, "whole passes");
+#pragma unroll
+            for (int i = 0; i < PIECES / C::NT; ++i) {
+                const int c = tid + i * C::NT, rr = c / (C::BN / 8), p = c % (C::BN / 8);
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cbuf + rr * CPITCH + p * 16);
+                const int ml = r * 32 + rr;
+                if (ml < rows)
+                    *reinterpret_cast<u32x4_t*>((uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc + n0 + p * 8) = v;
+            }
+            lds_barrier();
         });
     };
 
