@@ -1578,8 +1578,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
 
 // Prefill NVFP4 expert GEMM with the weights decoded in registers.
 //
-// 192 x 256 tiles over 8 waves of 96 x 64 (2 x 4).  Each K step moves by
-// LDS-DMA into a ring of NB = D + 1 stages: the gathered activation rows
+// 192 x 256 tiles over 8 waves of 192 x 32: each wave owns one 32-row
+// block of weights and decodes it alone (with waves of 96 x 64 two waves
+// decoded every block, and the decode's VALU work set the pace; reading
+// all 192 activation rows' fragments from LDS costs less).  Each K step
+// moves by LDS-DMA into a ring of NB = D + 1 stages: the gathered activation rows
 // (24 KB) and the tile's raw weight codes and scale words (thread t stages
 // 16 code bytes of weight row t / 2, half t % 2, and that row's 4-byte
 // scale word: 10 KB).  A lane then reads from LDS the 32 codes of its own
@@ -1600,15 +1603,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
 // grouped GEMM's (whole items, N-tile-major within an expert).
 template <int BFMT, int GATHER, int D>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedGemm g, int nN) {
-    using C = MfmaCfg<192, 256, 2, 4, true, 64, D + 1>;
+    using C = MfmaCfg<192, 256, 1, 8, true, 64, D + 1>;
     using SA = Slots<C, C::BM>;
     constexpr int NB = D + 1, ACH = C::BM * C::CPR, KS = C::BK / 16;
     // raw slot: a 16-byte code chunk per thread, then a scale word per thread
     constexpr int RAWC = C::NT + C::NT / 4;
     constexpr int PT = SA::N + 2;  // DMA instructions per step and thread
     static_assert(BFMT == LMOE_NVFP4 || BFMT == LMOE_NVFP4_2D, "NVFP4 weights");
-    static_assert(C::TM == 3 && C::TN == 2 && KS == 4 && SA::CPW % 64 == 0 && C::NT == 2 * C::BN,
-                  "8 waves of 96 x 64, two threads per weight row");
+    static_assert(C::WN % 32 == 0 && KS == 4 && SA::CPW % 64 == 0 && C::NT == 2 * C::BN,
+                  "waves of whole 32-row weight blocks, two threads per weight row");
     static_assert(D >= 1 && (D - 1) * PT < 64, "vmcnt range");
     // one LDS array for the ring and the output staging (see the epilogue)
     constexpr int CPITCH = C::BN * 2 + 16;  // bytes per output row staged in LDS
