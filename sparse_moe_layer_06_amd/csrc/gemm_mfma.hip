@@ -158,6 +158,44 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+// Writes and reads of an output tile staged in LDS beside a DMA ring.  The
+// compiler cannot tell that the K steps still landing by DMA go to other
+// bytes of the same array, and before a plain LDS access it waits for every
+// one of them (the steps prefetched for the next item); before these asm
+// accesses it does not.  The reads wait for their own data in the same asm
+// statement; the caller orders the writes before the reads with
+// lgkmcnt(0) and a barrier.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void lds_write_b64(void* p, uint32_t lo, uint32_t hi) {
+    const uint64_t v = (uint64_t)lo | ((uint64_t)hi << 32);
+    asm volatile("ds_write_b64 %0, %1" : : "v"(lds_offset(p)), "v"(v) : "memory");
+}
+
+// N 16-byte reads at p + i * STRIDE bytes (N = 2 or 6)
+template <int N, int STRIDE>
+__device__ __forceinline__ void lds_read_b128xn(const void* p, u32x4_t (&v)[N]) {
+    static_assert((N == 2 || N == 6) && (N - 1) * STRIDE < 65536 && STRIDE % 16 == 0, "ds offset range");
+    const uint32_t a = lds_offset(p);
+    if constexpr (N == 2) {
+        asm volatile(
+            "ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1])
+            : "v"(a), "i"(STRIDE)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %6\n\tds_read_b128 %1, %6 offset:%7\n\tds_read_b128 %2, %6 offset:%8\n\t"
+            "ds_read_b128 %3, %6 offset:%9\n\tds_read_b128 %4, %6 offset:%10\n\t"
+            "ds_read_b128 %5, %6 offset:%11\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+            : "v"(a), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE), "i"(4 * STRIDE), "i"(5 * STRIDE)
+            : "memory");
+    }
+}
+
 // Waits until at most `ahead` K tiles of this wave's DMA are still in flight
 // (`per_tile` instructions each), then the workgroup barrier.  The empty asm
 // statements keep the compiler from moving memory accesses across.
@@ -1527,22 +1565,22 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
                             v[i] *= v[i];
                         }
                     }
-                    uint2 o;
-                    o.x = pack_bf16x2(v[0], v[1]);
-                    o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(crow + (wave * C::WN + q * 8 + hi * 4) / 2) = o;
+                    lds_write_b64(crow + (wave * C::WN + q * 8 + hi * 4) / 2, pack_bf16x2(v[0], v[1]),
+                                  pack_bf16x2(v[2], v[3]));
                 });
             });
             lds_barrier();
             constexpr int PIECES = C::BM / 2 * (C::BN / 8);  // 16-byte pieces of the half tile
+            constexpr int RPP = C::NT / (C::BN / 8);         // rows per pass
             static_assert(PIECES % C::NT == 0, "whole passes");
+            const int r0 = tid / (C::BN / 8), p = tid % (C::BN / 8);
+            u32x4_t v[PIECES / C::NT];
+            lds_read_b128xn<PIECES / C::NT, RPP * CPITCH>(cbuf + r0 * CPITCH + p * 16, v);
 #pragma unroll
             for (int i = 0; i < PIECES / C::NT; ++i) {
-                const int c = tid + i * C::NT, r = c / (C::BN / 8), p = c % (C::BN / 8);
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cbuf + r * CPITCH + p * 16);
-                const int ml = half * (C::BM / 2) + r;
+                const int ml = half * (C::BM / 2) + r0 + i * RPP;
                 if (ml < rows)
-                    *reinterpret_cast<u32x4_t*>((uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc + n0 + p * 8) = v;
+                    *reinterpret_cast<u32x4_t*>((uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc + n0 + p * 8) = v[i];
             }
             lds_barrier();
         });
@@ -1592,14 +1630,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
 // read from LDS.  The K positions inside a step are renumbered (sub-step s
 // of lane half h takes k = 32 h + 8 s .. +8, the activation fragments
 // read from LDS take the same k), which leaves the product unchanged and
-// makes a lane's codes of a step one 16-byte chunk.  Step q's iteration
-// waits for its own DMA, passes the barrier, issues step q + D into the
-// stage step q - 1 used, then multiplies.  Every thread issues the same PT
-// DMA instructions per step, also past the block's last step (the fill
-// side then re-reads the last item at valid addresses into stages nothing
-// uses), so waiting for vmcnt((D - 1) PT) leaves exactly steps q + 1 ..
-// q + D - 1 in flight (epilogue stores issued since can only make that
-// wait longer).  The work list and the items' order are the persistent
+// makes a lane's codes of a step one 16-byte chunk.  Step q's last
+// sub-step waits for step q + 1's DMA, passes the barrier, issues step
+// q + NB into stage q, and reads and decodes the start of step q + 1 under
+// its MFMAs.  Every thread issues the same PT DMA instructions per step,
+// also past the block's last step (the fill side then re-reads the last
+// item at valid addresses into stages nothing uses), so waiting for
+// vmcnt((D - 1) PT) leaves exactly steps q + 2 .. q + D in flight
+// (epilogue stores issued since can only make that wait longer).  The
+// work list and the items' order are the persistent
 // grouped GEMM's (whole items, N-tile-major within an expert).
 template <int BFMT, int GATHER, int D>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedGemm g, int nN) {
@@ -1612,7 +1651,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
     static_assert(BFMT == LMOE_NVFP4 || BFMT == LMOE_NVFP4_2D, "NVFP4 weights");
     static_assert(C::WN % 32 == 0 && KS == 4 && SA::CPW % 64 == 0 && C::NT == 2 * C::BN,
                   "waves of whole 32-row weight blocks, two threads per weight row");
-    static_assert(D >= 1 && (D - 1) * PT < 64, "vmcnt range");
+    static_assert(D >= 1 && D * PT < 64, "vmcnt range");
     // one LDS array for the ring and the output staging (see the epilogue)
     constexpr int CPITCH = C::BN * 2 + 16;  // bytes per output row staged in LDS
     __shared__ u32x4_t ring[NB * (ACH + RAWC) + 32 * CPITCH / 16];
@@ -1728,16 +1767,23 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
     // the lane's weight row of group tn: wn * 64 + tn * 32 + l31, its chunk
     // (and scale word) 2 row + half in the raw slot
     const int rraw = 2 * (wn * C::WN + l31) + hi;
-    auto mma = [&](const u32x4_t* As, const u32x4_t* Raw) __attribute__((always_inline)) {
-        u32x4_t bc[C::TN];
-        uint32_t bs[C::TN];
+    u32x4_t bc[C::TN];
+    uint32_t bs[C::TN];
+    auto read_raw = [&](const u32x4_t* Raw) __attribute__((always_inline)) {
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn) {
             bc[tn] = Raw[rraw + 64 * tn];
             bs[tn] = reinterpret_cast<const uint32_t*>(Raw + C::NT)[rraw + 64 * tn] >> (16 * hi);
         }
-        read(As, 0, 0);
-        decode(bc, bs, 0, 0);
+    };
+    // One K step, the barrier late: sub-step ks reads and decodes the
+    // fragments of ks + 1 under its MFMAs.  The last sub-step first waits
+    // for step q + 1 (its own DMA, then the barrier for everyone's), refills
+    // stage q with step q + NB (every wave has read stage q's codes and last
+    // activation fragments by then), reads step q + 1's codes and first
+    // activation fragments under its MFMAs and decodes their first sub-step.
+    auto mma = [&](u32x4_t* As, u32x4_t* Raw, const u32x4_t* Asn, const u32x4_t* Rawn)
+                   __attribute__((always_inline)) {
         static_for<KS>([&](auto kc) __attribute__((always_inline)) {
             constexpr int ks = decltype(kc)::value, b = ks & 1;
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this sub-step's activation fragments
@@ -1745,6 +1791,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
             if constexpr (ks + 1 < KS) {
                 read(As, ks + 1, b ^ 1);
                 decode(bc, bs, ks + 1, b ^ 1);
+            } else {
+                asm volatile("" ::: "memory");
+                wait_vmcnt<(D - 1) * PT>();    // this thread's loads of step q + 1
+                __builtin_amdgcn_s_barrier();  // everyone's
+                asm volatile("" ::: "memory");
+                fill(As, Raw);
+                __builtin_amdgcn_sched_barrier(0);
+                read_raw(Rawn);
+                read(Asn, 0, b ^ 1);
             }
 #pragma unroll
             for (int tm = 0; tm < C::TM; ++tm)
@@ -1758,8 +1813,19 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
                     if constexpr (m < C::TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                 });
+            } else {  // the codes first, then MFMA m and an activation fragment
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::TN, 0);
+                static_for<C::TM * C::TN>([&](auto mc) __attribute__((always_inline)) {
+                    constexpr int m = decltype(mc)::value;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (m < C::TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                });
             }
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ks + 1 == KS) {
+                decode(bc, bs, 0, b ^ 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         });
     };
     float mscale = 1.0f;
@@ -1793,49 +1859,52 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
                             v[i] *= v[i];
                         }
                     }
-                    uint2 o;
-                    o.x = pack_bf16x2(v[0], v[1]);
-                    o.y = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(crow + (wn * C::WN + tn * 32 + q * 8 + hi * 4) / 2) = o;
+                    lds_write_b64(crow + (wn * C::WN + tn * 32 + q * 8 + hi * 4) / 2, pack_bf16x2(v[0], v[1]),
+                                  pack_bf16x2(v[2], v[3]));
                 });
             }
             lds_barrier();
             constexpr int PIECES = 32 * (C::BN / 8);  // 16-byte pieces of 32 rows
+            constexpr int RPP = C::NT / (C::BN / 8);  // rows per pass
             static_assert(PIECES % C::NT == 0, "whole passes");
+            const int r0 = tid / (C::BN / 8), p = tid % (C::BN / 8);
+            u32x4_t v[PIECES / C::NT];
+            lds_read_b128xn<PIECES / C::NT, RPP * CPITCH>(cbuf + r0 * CPITCH + p * 16, v);
 #pragma unroll
             for (int i = 0; i < PIECES / C::NT; ++i) {
-                const int c = tid + i * C::NT, rr = c / (C::BN / 8), p = c % (C::BN / 8);
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cbuf + rr * CPITCH + p * 16);
-                const int ml = r * 32 + rr;
+                const int ml = r * 32 + r0 + i * RPP;
                 if (ml < rows)
-                    *reinterpret_cast<u32x4_t*>((uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc + n0 + p * 8) = v;
+                    *reinterpret_cast<u32x4_t*>((uint16_t*)g.C + (int64_t)(row0 + ml) * g.ldc + n0 + p * 8) = v[i];
             }
             lds_barrier();
         });
     };
 
+    // steps 0 .. D in flight, then step 0's codes, first fragments and first decode
     u32x4_t* const raw = ring + NB * ACH;
-    static_for<D>([&](auto uc) __attribute__((always_inline)) {
+    static_for<NB>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         fill(ring + u * ACH, raw + u * RAWC);
     });
+    asm volatile("" ::: "memory");
+    wait_vmcnt<D * PT>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_raw(raw);
+    read(ring, 0, 0);
+    decode(bc, bs, 0, 0);
     int4 mdesc = fdesc;
     mscale = sload_f32(g.B_ts + mdesc.x);
     int m_kt = 0;
     for (int q0 = 0; q0 < total; q0 += NB) {  // total is a multiple of NB (nk is)
         static_for<NB>([&](auto uc) __attribute__((always_inline)) {
-            constexpr int u = decltype(uc)::value, un = (u + D) % NB;
-            asm volatile("" ::: "memory");
-            wait_vmcnt<(D - 1) * PT>();    // this thread's loads of step q
-            __builtin_amdgcn_s_barrier();  // everyone's; and step q - 1 is done
-            asm volatile("" ::: "memory");
-            fill(ring + un * ACH, raw + un * RAWC);
-            mma(ring + u * ACH, raw + u * RAWC);
+            constexpr int u = decltype(uc)::value, un = (u + 1) % NB;
+            mma(ring + u * ACH, raw + u * RAWC, ring + un * ACH, raw + un * RAWC);
             if (++m_kt == nk) {
                 epilogue(mdesc);
                 zero_acc<C>(acc);
                 m_kt = 0;
-                mdesc = fdesc;  // the fill side is D < nk steps ahead, in the next item
+                mdesc = fdesc;  // the fill side is NB <= nk steps ahead, in the next item
                 mscale = sload_f32(g.B_ts + mdesc.x);
             }
         });
