@@ -41,9 +41,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// Two fp32 -> packed bf16x2 (low half = a).
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 (the same result as f32_to_bf16_rne for finite
+// inputs; a NaN stays a NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
