@@ -437,7 +437,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--decode-steps", type=int, default=100)
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
