@@ -29,20 +29,22 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
     for (int j0 = 0; j0 < k; j0 += kGroup) {
         int p[kGroup];
         float gj[kGroup];
-        uint4 v[kGroup];
+        u32x4_t v[kGroup];
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
             // p < 0: pair left out by the permutation (invalid expert id)
             p[i] = (j0 + i < k) ? row[j0 + i] : -1;
             gj[i] = (j0 + i < k) ? grow[j0 + i] : 0.f;
         }
+        // each row of Y is read exactly once: non-temporal loads
 #pragma unroll
         for (int i = 0; i < kGroup; ++i)
-            v[i] = (p[i] >= 0) ? *reinterpret_cast<const uint4*>(Y + (int64_t)p[i] * l + col) : make_uint4(0, 0, 0, 0);
+            v[i] = (p[i] >= 0) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Y + (int64_t)p[i] * l + col))
+                               : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) {
             if (p[i] < 0) continue;
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            const uint32_t w[4] = {v[i][0], v[i][1], v[i][2], v[i][3]};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 acc[2 * q] = fmaf(gj[i], __uint_as_float(w[q] << 16), acc[2 * q]);
