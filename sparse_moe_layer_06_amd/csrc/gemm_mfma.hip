@@ -1632,8 +1632,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_breg_kernel(GroupedGemm g
 // read from LDS take the same k), which leaves the product unchanged and
 // makes a lane's codes of a step one 16-byte chunk.  Step q's last
 // sub-step waits for step q + 1's DMA, passes the barrier, issues step
-// q + NB into stage q, and reads and decodes the start of step q + 1 under
-// its MFMAs.  Every thread issues the same PT DMA instructions per step,
+// q + NB into stage q, and reads step q + 1's codes and first activation
+// fragments under its MFMAs; the decode of that first sub-step follows
+// (the compiler places it right before the MFMAs that take it).  Every thread issues the same PT DMA instructions per step,
 // also past the block's last step (the fill side then re-reads the last
 // item at valid addresses into stages nothing uses), so waiting for
 // vmcnt((D - 1) PT) leaves exactly steps q + 2 .. q + D in flight
@@ -1781,7 +1782,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_nvfp4_reg_kernel(GroupedG
     // for step q + 1 (its own DMA, then the barrier for everyone's), refills
     // stage q with step q + NB (every wave has read stage q's codes and last
     // activation fragments by then), reads step q + 1's codes and first
-    // activation fragments under its MFMAs and decodes their first sub-step.
+    // activation fragments under its MFMAs, and then decodes their first
+    // sub-step.
     auto mma = [&](u32x4_t* As, u32x4_t* Raw, const u32x4_t* Asn, const u32x4_t* Rawn)
                    __attribute__((always_inline)) {
         static_for<KS>([&](auto kc) __attribute__((always_inline)) {
